@@ -1,0 +1,387 @@
+#!/usr/bin/env python3
+"""Benchmark of the multi-LoRA add-on (SGMV/BGMV shrink + expand) on one MI355X.
+
+Default workload: Llama-2-7B decode, batch 32, every row its own rank-16 adapter
+(32 slots, scale 2.0), all 7 adapted projections of all 32 layers
+(q/k/v/o 4096->4096, gate/up 4096->11008, down 11008->4096).  One step = one decode
+step's LoRA work for the whole model: 32 x 7 x (shrink + expand) launches in the
+per-row-slot (BGMV) form, captured once in a HIP graph and replayed.  Each layer has
+its own adapter weights (2.6 GB in total), so every step reads them from HBM rather
+than from the 256 MB Infinity Cache.  Inputs are seeded synthetic fp16 N(0, 0.02),
+generated on the GPU before the timed region.
+
+Prints one JSON line: metric, value (algorithmic GB/s of the whole step), us_per_layer,
+TFLOP/s, the roofline of the dominant kernel (durations from HIP events attached to
+every launch of that kernel, on its stream), and the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SGMV shrink+expand µs/layer, GB/s & TFLOP/s vs roofline at bs=32 decode"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ workloads
+def workload_spec(name):
+    from segmented_gather_matmul_amd import workloads as wl
+    if name == "decode_distinct_7b":
+        b = wl.batch_decode_distinct(32)
+        return dict(cfg_id=2, shapes=wl.LLAMA2_7B, layers=32, num_slots=32, rank=np.full(32, 16, np.int32),
+                    scale=np.full(32, 2.0, np.float32), batch=b, form="bgmv", layout="dense",
+                    model="Llama-2-7B", popularity="distinct")
+    if name.startswith("decode_") and name.endswith("_13b"):
+        pop = name.split("_")[1]
+        b = wl.batch_decode_mix(pop)
+        return dict(cfg_id=3, shapes=wl.LLAMA2_13B, layers=40, num_slots=16, rank=np.full(16, 64, np.int32),
+                    scale=np.full(16, 0.5, np.float32), batch=b, form="sgmv", layout="dense",
+                    model="Llama-2-13B", popularity=pop)
+    if name == "prefill_7b":
+        b = wl.batch_prefill()
+        return dict(cfg_id=4, shapes=wl.LLAMA2_7B, layers=4, num_slots=16, rank=np.full(16, 16, np.int32),
+                    scale=np.full(16, 2.0, np.float32), batch=b, form="sgmv_contiguous", layout="dense",
+                    model="Llama-2-7B", popularity="distinct")
+    if name == "paged_70b":
+        rank = wl.paged_ranks(2000)
+        b = wl.batch_paged_zipf(256, 2000)
+        return dict(cfg_id=5, shapes=wl.LLAMA2_70B, layers=2, num_slots=2000, rank=rank,
+                    scale=wl.scale_for_rank(rank), batch=b, form="bgmv", layout="paged", page_elems=1024,
+                    model="Llama-2-70B", popularity="zipf1.2")
+    raise SystemExit(f"unknown workload {name}")
+
+
+class Op:
+    """One adapted projection of one layer: its weights, activations and launch metadata."""
+
+
+def make_ops(spec, layers, device):
+    import torch
+    from segmented_gather_matmul_amd import binding as B
+    b = spec["batch"]
+    n, S, rank = b.n, spec["num_slots"], spec["rank"]
+    r_max = int(rank.max())
+    idx_d = torch.from_numpy(b.idx.astype(np.int32)).to(device)
+    segs = None
+    if spec["form"].startswith("sgmv"):
+        if spec["form"] == "sgmv":
+            row_map, seg_ptr, seg_slot, n_act = B.lora_build_segments(b.idx, S)
+            tiles = B.lora_build_tiles(seg_ptr, seg_slot)
+            segs = B.segments_to_device(tiles, row_map, n_act, device)
+        else:
+            tiles = B.lora_build_tiles(b.seg_ptr, b.seg_slot)
+            segs = B.segments_to_device(tiles, None, n, device)
+    rank_d = torch.from_numpy(rank.astype(np.int32)).to(device)
+    scale_d = torch.from_numpy(spec["scale"].astype(np.float32)).to(device)
+    gen = torch.Generator(device=device)
+    ops = []
+    for layer in range(layers):
+        for pname, (d_in, d_out) in spec["shapes"].items():
+            pid = list(spec["shapes"]).index(pname)
+            gen.manual_seed(spec["cfg_id"] * 1_000_003 + layer * 101 + pid)
+
+            def rnd(*shape):
+                return (torch.randn(*shape, generator=gen, device=device, dtype=torch.float32) * 0.02).half()
+
+            op = Op()
+            op.layer, op.proj, op.d_in, op.d_out = layer, pname, d_in, d_out
+            op.x = rnd(n, d_in)
+            op.y = rnd(n, d_out)
+            if spec["layout"] == "dense":
+                a_t = rnd(S, r_max, d_in)
+                bb = rnd(S, r_max, d_out)
+                op.w = B.Weights(num_slots=S, d_in=d_in, d_out=d_out, r_max=r_max, rank=rank_d, scale=scale_d,
+                                 a_t=a_t, b=bb)
+            else:
+                from segmented_gather_matmul_amd import workloads as wl
+                P = spec["page_elems"]
+                pt, a_off, b_off, num_pages = wl.page_placement(spec["cfg_id"], layer * 7 + pid, rank, d_in,
+                                                                d_out, P)
+                pool = torch.empty((num_pages, P), dtype=torch.float16, device=device)
+                for c0 in range(0, num_pages, 1 << 20):
+                    c1 = min(num_pages, c0 + (1 << 20))
+                    pool[c0:c1] = rnd(c1 - c0, P)
+                op.w = B.Weights(num_slots=S, d_in=d_in, d_out=d_out, r_max=r_max, rank=rank_d, scale=scale_d,
+                                 pool=pool, page_elems=P, page_table=torch.from_numpy(pt).to(device),
+                                 a_pt_off=torch.from_numpy(a_off).to(device),
+                                 b_pt_off=torch.from_numpy(b_off).to(device))
+            op.v = torch.zeros((n, max(4, -(-r_max // 4) * 4)), dtype=torch.float32, device=device)
+            op.idx, op.segs = idx_d, segs
+            ops.append(op)
+    # one v buffer serves every op of the step (same stream, in order)
+    v = torch.zeros_like(ops[0].v)
+    for o in ops:
+        o.v = v
+    return ops
+
+
+def launch_op(op, kernel):
+    from segmented_gather_matmul_amd import binding as B
+    if op.segs is None:
+        if kernel == "shrink":
+            B.lora_bgmv_shrink(op.v, op.x, op.idx, op.w)
+        else:
+            B.lora_bgmv_expand(op.y, op.v, op.idx, op.w)
+    else:
+        if kernel == "shrink":
+            B.lora_sgmv_shrink(op.v, op.x, op.w, op.segs)
+        else:
+            B.lora_sgmv_expand(op.y, op.v, op.w, op.segs)
+
+
+def step(ops):
+    for op in ops:
+        launch_op(op, "shrink")
+        launch_op(op, "expand")
+
+
+# ------------------------------------------------------------------ HIP events (raw handles)
+class HipEvents:
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.hip.hipEventSynchronize(b) == 0
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return out.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def kernel_durations(ops, steps):
+    """Average duration of every launch of each kernel, from event pairs attached to
+    the launches themselves (hipExtLaunchKernel records start/stop on the stream)."""
+    from segmented_gather_matmul_amd import binding as B
+    import torch
+    ev = HipEvents()
+    pairs = {"shrink": [], "expand": []}
+    for _ in range(steps):
+        for op in ops:
+            for k in ("shrink", "expand"):
+                e0, e1 = ev.create(), ev.create()
+                B.lora_set_launch_events(e0, e1)
+                launch_op(op, k)
+                pairs[k].append((op, e0, e1))
+    torch.cuda.synchronize()
+    out = {}
+    for k, lst in pairs.items():
+        ms = [ev.elapsed_ms(e0, e1) for _, e0, e1 in lst]
+        out[k] = dict(n=len(ms), avg_us=1e3 * float(np.mean(ms)), p10_us=1e3 * float(np.percentile(ms, 10)),
+                      p90_us=1e3 * float(np.percentile(ms, 90)), total_us=1e3 * float(np.sum(ms)),
+                      ops=[o for o, _, _ in lst])
+        for _, e0, e1 in lst:
+            ev.destroy(e0)
+            ev.destroy(e1)
+    return out
+
+
+# ------------------------------------------------------------------ accounting
+def op_counts(spec, op):
+    from segmented_gather_matmul_amd import costmodel as cm
+    idx, rank, r_max = spec["batch"].idx, spec["rank"], int(spec["rank"].max())
+    return dict(shrink_bytes=cm.shrink_bytes(idx, rank, op.d_in, r_max),
+                expand_bytes=cm.expand_bytes(idx, rank, op.d_out, r_max),
+                shrink_flops=cm.shrink_flops(idx, rank, op.d_in),
+                expand_flops=cm.expand_flops(idx, rank, op.d_out))
+
+
+def kernel_source_sha():
+    p = os.path.join(ROOT, "segmented_gather_matmul_amd", "csrc", "lora_kernels.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(workload, kernel):
+    """HBM bytes per launch from the committed counter summary, if it matches the current kernels."""
+    p = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(spec, ops, budget_s=10.0):
+    """The CPU oracle, as it is, on the same step: whole layers in order, repeated until
+    about budget_s seconds of oracle time have run (inputs copied to host beforehand)."""
+    import oracle
+    from segmented_gather_matmul_amd import workloads as wl
+    if spec["layout"] != "dense":
+        return None
+    cores = min(16, len(os.sched_getaffinity(0)))
+    b = spec["batch"]
+    S, rank, scale = spec["num_slots"], spec["rank"], spec["scale"]
+    r_max = int(rank.max())
+    host = []
+    for op in ops:
+        store = wl.DenseStore(S, op.d_in, op.d_out, r_max, rank, scale, op.w.tensors[2].cpu().numpy(),
+                              op.w.tensors[3].cpu().numpy())
+        c = op_counts(spec, op)
+        host.append((op.layer, store, op.x.cpu().numpy(), op.y.cpu().numpy(), c["shrink_bytes"] + c["expand_bytes"]))
+    if spec["form"] != "bgmv":
+        rm, sp, ss, _ = oracle.build_segments(b.idx, S)
+    n_layers = len(set(h[0] for h in host))
+    t_total, bytes_total, layers_done = 0.0, 0, 0
+    while t_total < budget_s:
+        layer_t = 0.0
+        for lay in range(n_layers):
+            for _, store, x, y0, nbytes in (h for h in host if h[0] == lay):
+                t0 = time.perf_counter()
+                if spec["form"] == "bgmv":
+                    oracle.bgmv(store, x, y0, b.idx, nthreads=cores)
+                else:
+                    oracle.sgmv(store, x, y0, sp, ss, rm, nthreads=cores)
+                dt = time.perf_counter() - t0
+                t_total += dt
+                layer_t += dt
+                bytes_total += nbytes
+            layers_done += 1
+            if t_total >= budget_s:
+                break
+    return dict(value=round(bytes_total / t_total / 1e9, 4), unit="GB/s", cores=cores, kind="oracle",
+                us_per_layer=round(1e6 * t_total / layers_done, 1),
+                sample=f"{layers_done} layer passes over the {n_layers} layers x {len(spec['shapes'])} projections "
+                       f"of the step ({b.n} rows each), fp64 C loops with OpenMP over rows, {t_total:.1f} s")
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_distinct_7b")
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--kernel-steps", type=int, default=5, help="steps of the per-launch event pass")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(a batch shards across GPUs by rows without any exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from segmented_gather_matmul_amd import binding as B
+    from segmented_gather_matmul_amd import costmodel as cm
+    B.lib()
+    if not torch.cuda.is_available():
+        raise SystemExit("no GPU visible")
+    device = "cuda"
+    spec = workload_spec(args.workload)
+    layers = args.layers or spec["layers"]
+    log(f"[bench] workload={args.workload} layers={layers} building inputs")
+    ops = make_ops(spec, layers, device)
+    torch.cuda.synchronize()
+    counts = [op_counts(spec, o) for o in ops]
+    step_bytes = sum(c["shrink_bytes"] + c["expand_bytes"] for c in counts)
+    step_flops = sum(c["shrink_flops"] + c["expand_flops"] for c in counts)
+
+    log(f"[bench] {len(ops)} ops/step, {step_bytes / 1e6:.1f} MB algorithmic per step; warmup {args.warmup}")
+    stream = torch.cuda.current_stream()
+    if args.no_graph:
+        run = lambda: step(ops)
+    else:
+        step(ops)  # first eager pass (loads kernels)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(ops)
+        run = g.replay
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step (wall {wall_ms:.4f})")
+
+    log(f"[bench] per-launch event pass: {args.kernel_steps} steps")
+    kd = kernel_durations(ops, args.kernel_steps)
+    per_kernel = {}
+    for k in ("shrink", "expand"):
+        d = kd[k]
+        kb = sum(op_counts(spec, o)[f"{k}_bytes"] for o in d["ops"])
+        kf = sum(op_counts(spec, o)[f"{k}_flops"] for o in d["ops"])
+        per_kernel[k] = dict(launches_per_step=len(ops), avg_us=round(d["avg_us"], 3), p10_us=round(d["p10_us"], 3),
+                             p90_us=round(d["p90_us"], 3), bytes_per_launch=kb / d["n"],
+                             gbs=round(kb / (d["total_us"] * 1e-6) / 1e9, 1),
+                             tflops=round(kf / (d["total_us"] * 1e-6) / 1e12, 3))
+    dom = max(per_kernel, key=lambda k: kd[k]["total_us"])
+    pk = per_kernel[dom]
+    kernel_name = {"shrink": "lora_shrink_kernel", "expand": "lora_expand_kernel"}[dom]
+    traffic = traffic_from_profile(args.workload, dom)
+    roofline = dict(bound="hbm", achieved=pk["gbs"], peak=cm.HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(pk["gbs"] / cm.HBM_PEAK_GBS, 4), traffic=traffic, kernel=kernel_name,
+                    avg_launch_us=pk["avg_us"], algorithmic_bytes_per_launch=round(pk["bytes_per_launch"]))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_baseline(spec, ops, args.cpu_budget)
+
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 (fp32 accumulate)",
+        "data": "synthetic (seeded N(0,0.02) fp16, generated on the GPU)",
+        "config": {"workload": args.workload, "model_shapes": spec["model"], "layers": layers,
+                   "projections": list(spec["shapes"]), "batch_rows": spec["batch"].n,
+                   "num_slots": spec["num_slots"], "rank": sorted(set(int(r) for r in spec["rank"])),
+                   "popularity": spec["popularity"], "form": spec["form"], "layout": spec["layout"],
+                   "launches_per_step": 2 * len(ops), "graph": not args.no_graph, "parallelism": "none"},
+        "us_per_layer": round(1e3 * ms / layers, 3),
+        "tflops": round(step_flops / (ms * 1e-3) / 1e12, 4),
+        "step_bytes": step_bytes,
+        "step_flops": step_flops,
+        "hbm_frac_step": round(gbs / cm.HBM_PEAK_GBS, 4),
+        "wall_ms_per_step": round(wall_ms, 5),
+        "kernels": per_kernel,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,235 @@
+/*
+ * lora_sgmv.h -- C ABI of the MI355X (gfx950) multi-LoRA add-on library.
+ *
+ * The operation (Punica summary, section 3.4 "The SGMV Operator: What It Computes";
+ * Multi-LoRA Serving blog, "Why a mixed batch needs special kernels"):
+ * every row i of a batch that carries an adapter slot s computes
+ *
+ *     shrink   v[i][j] = sum_k x[i][k] * A[s][k][j]                 (j < r_s, d_in -> r)
+ *     expand   y[i][c] = y[i][c] + scale[s] * sum_j v[i][j] * B[s][j][c]   (r -> d_out)
+ *
+ * in place on the base output y.  Rows are given either as contiguous segments that
+ * share one adapter (SGMV; Punica summary, "The SGMV Operator", segment offsets
+ * s_0 = 0 < s_1 < ... < s_n) or with one slot per row (BGMV; Punica digest, section
+ * 5.5, and the blog's reference loop, where slot -1 means "no adapter").  Each of
+ * shrink and expand is one kernel launch whatever the adapter mix, including mixed
+ * ranks and adapters held as scattered pages (S-LoRA summary, "Unified Paging" and
+ * "Heterogeneous Batching").
+ *
+ * Conventions for every entry point:
+ *  - Pointers documented "device" must point to GPU memory; "host" to CPU memory.
+ *    All device pointers to fp16/fp32 data must be 16-byte aligned.
+ *  - fp16 = IEEE binary16 (x, y, A, B); v and scale are fp32; slots, ranks and page
+ *    ids are int32; page-table offsets are int64.  Matrices are row-major with the
+ *    given leading dimension (in elements).
+ *  - The caller owns every buffer.  The library never allocates or frees device memory,
+ *    never synchronises, and keeps no state except a thread-local error message
+ *    (and the one-shot timing events of lora_set_launch_events).
+ *    Launching calls are asynchronous on `stream` (a hipStream_t; NULL = default).
+ *    Inputs, outputs and metadata must stay alive until the work on `stream` ends.
+ *  - Return value: LORA_OK (0) or a negative LORA_E_* code; lora_last_error() then
+ *    describes the problem.  Argument checks run on the host before any launch, so
+ *    a rejected call launches nothing.  Device-resident metadata (slots, ranks,
+ *    row maps, page tables) is read by the kernels without a host check; an entry
+ *    outside its documented range makes that tile or page a no-op instead of an
+ *    out-of-bounds access.  lora_validate_*_host() check host copies fully.
+ *  - An "active" row has slot s in [0, num_slots) with rank[s] > 0.  Rows that are
+ *    not active keep y and v bit-identical.
+ *
+ * Numerics: fp16 products accumulate in fp32; v is stored in fp32; the expand adds
+ * (scale[s] * v) . B to y in fp32 and rounds once to fp16 (round to nearest even).
+ * Results are bit-identical from run to run for the same inputs (no float atomics);
+ * different launch shapes may round differently within fp32 accumulation error.
+ */
+#ifndef LORA_SGMV_H
+#define LORA_SGMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status codes */
+#define LORA_OK 0
+#define LORA_E_NULL (-1)        /* a required pointer is NULL */
+#define LORA_E_SHAPE (-2)       /* a size or leading dimension is invalid */
+#define LORA_E_ALIGN (-3)       /* a pointer or leading dimension is misaligned */
+#define LORA_E_INDEX (-4)       /* a slot, row, tile or page index is out of range */
+#define LORA_E_UNSUPPORTED (-5) /* valid request this library does not support (r_max > 64) */
+#define LORA_E_HIP (-6)         /* the HIP runtime reported an error at launch */
+#define LORA_E_CAPACITY (-7)    /* a host output array is too small */
+
+#define LORA_LAYOUT_DENSE 0
+#define LORA_LAYOUT_PAGED 1
+
+#define LORA_MAX_RANK 64        /* largest r_max (the pages' ranks run from 8 to 64) */
+#define LORA_MAX_TILE_ROWS 64   /* largest number of rows in one work tile */
+
+/* ---------------------------------------------------------------- descriptors */
+/*
+ * One adapted projection (d_in -> d_out) of one layer, for all adapter slots.
+ *
+ * Dense layout (LORA_LAYOUT_DENSE): A is stored transposed, as rank-rows
+ * (Punica digest, section 5.4, LoraWeight: A as [r][in], B as [r][out]):
+ *     a_t[(s*r_max + j)*d_in  + k] = A[s][k][j]
+ *     b  [(s*r_max + j)*d_out + c] = B[s][j][c]
+ * Rank-rows j >= rank[s] are never read.
+ *
+ * Paged layout (LORA_LAYOUT_PAGED; S-LoRA summary, "Unified Paging": A is held as r
+ * pages, one per column of A, and B as r pages, one per row of B, anywhere in one
+ * pool).  Each rank-row is cut into d/P pages of P = page_elems elements:
+ *     A[s][k][j] = pool[page_table[a_pt_off[s] + j*(d_in/P)  + k/P]*P + k%P]
+ *     B[s][j][c] = pool[page_table[b_pt_off[s] + j*(d_out/P) + c/P]*P + c%P]
+ * P must be a multiple of 8 that divides d_in and d_out.
+ */
+typedef struct lora_weights {
+    int32_t layout;          /* LORA_LAYOUT_DENSE or LORA_LAYOUT_PAGED */
+    int32_t num_slots;       /* number of adapter slots (>= 1) */
+    int32_t d_in, d_out;     /* multiples of 8 */
+    int32_t r_max;           /* 1..LORA_MAX_RANK; row stride of v must be >= r_max */
+    const int32_t *rank;     /* device [num_slots], each in 0..r_max */
+    const float *scale;      /* device [num_slots] (e.g. alpha / r) */
+    const void *a_t;         /* dense: device fp16 [num_slots][r_max][d_in] */
+    const void *b;           /* dense: device fp16 [num_slots][r_max][d_out] */
+    const void *pool;        /* paged: device fp16 [num_pages][page_elems] */
+    int64_t num_pages;       /* paged: pages in the pool */
+    int32_t page_elems;      /* paged: P */
+    const int32_t *page_table; /* paged: device [pt_entries], each in 0..num_pages-1 */
+    int64_t pt_entries;      /* paged: length of page_table */
+    const int64_t *a_pt_off; /* paged: device [num_slots] */
+    const int64_t *b_pt_off; /* paged: device [num_slots] */
+} lora_weights;
+
+/* One work tile: `nrows` consecutive positions pos0.. of one segment, slot `slot`. */
+typedef struct lora_tile {
+    int32_t slot;   /* adapter slot of the segment (-1 = none) */
+    int32_t pos0;   /* first position (index into row_map, or a row when row_map is NULL) */
+    int32_t nrows;  /* 1..LORA_MAX_TILE_ROWS */
+    int32_t seg;    /* segment the tile belongs to (informational) */
+} lora_tile;
+
+/*
+ * Segment form of a batch, as consumed by the SGMV kernels: a flat work-list of
+ * tiles (built once per batch by lora_build_tiles) and the position -> row map.
+ */
+typedef struct lora_segments {
+    int32_t n_tiles;
+    const lora_tile *tiles;  /* device [n_tiles] */
+    const int32_t *row_map;  /* device [n_pos] or NULL (position p is row p) */
+    int32_t n_pos;           /* number of positions (length of row_map) */
+    int32_t max_rows;        /* largest nrows of any tile, 0 = unknown (taken as 64); a launch-shape
+                              * hint only: results do not depend on it */
+} lora_segments;
+
+/* ---------------------------------------------------------------- host metadata */
+/*
+ * Group rows by adapter (Punica summary, "Batch Layout Construction": rows that share
+ * an adapter are placed consecutively and the segment offsets are built once per
+ * batch, then reused by every adapted projection of every layer).
+ *
+ * idx      host [n]: slot of each row, -1 = no adapter.
+ * row_map  host out [n]: positions -> original rows; segments in ascending slot order,
+ *          rows of one segment in ascending original index; rows with -1 left out.
+ * seg_ptr  host out [min(n, num_slots) + 1]: seg_ptr[0] = 0, strictly increasing.
+ * seg_slot host out [min(n, num_slots)].
+ * n_seg, n_act  host out: number of segments; active positions (= seg_ptr[n_seg]).
+ * Returns LORA_E_INDEX if some idx is outside [-1, num_slots), LORA_E_SHAPE for
+ * n < 0 or num_slots < 1, LORA_E_NULL for a missing pointer (arrays may be NULL
+ * only when n == 0).  Deterministic; allocates no device memory.
+ */
+int lora_build_segments(const int32_t *idx, int32_t n, int32_t num_slots, int32_t *row_map,
+                        int32_t *seg_ptr, int32_t *seg_slot, int32_t *n_seg, int32_t *n_act);
+
+/* Capacity that lora_build_tiles needs for n_pos positions in n_seg segments. */
+int32_t lora_tiles_bound(int32_t n_pos, int32_t n_seg, int32_t max_tile_rows);
+
+/*
+ * Cut segments into the flat tile work-list the SGMV kernels run on.  Segment g
+ * (positions seg_ptr[g] .. seg_ptr[g+1]-1, slot seg_slot[g]) becomes
+ * ceil(len / max_tile_rows) tiles of near-equal size; empty segments and segments
+ * with slot -1 produce no tile.  seg_ptr/seg_slot are host arrays (seg_ptr[0] may
+ * be > 0; it must be non-decreasing).  tiles: host out [tiles_cap].
+ * max_tile_rows in 1..LORA_MAX_TILE_ROWS.  Returns LORA_E_CAPACITY if tiles_cap is
+ * too small (see lora_tiles_bound), LORA_E_SHAPE for decreasing offsets.
+ */
+int lora_build_tiles(const int32_t *seg_ptr, const int32_t *seg_slot, int32_t n_seg,
+                     int32_t max_tile_rows, lora_tile *tiles, int32_t tiles_cap, int32_t *n_tiles);
+
+/*
+ * Host checks of host copies of a descriptor's device arrays.  `w` must hold host
+ * pointers for rank (and, for paged layout, page_table, a_pt_off, b_pt_off); the
+ * fp16 data pointers are not read.  Checks ranks against r_max, every page-table
+ * range and page id, and the shape rules above.
+ */
+int lora_validate_weights_host(const lora_weights *w);
+
+/* Host check of a host copy of a segment descriptor against n_rows and num_slots:
+ * tiles inside [0, n_pos), 1..LORA_MAX_TILE_ROWS rows, slots in [-1, num_slots),
+ * row_map entries in [0, n_rows) and no row used twice. */
+int lora_validate_segments_host(const lora_segments *seg, int32_t n_rows, int32_t num_slots);
+
+/* ---------------------------------------------------------------- SGMV (segments) */
+/*
+ * Shrink for a segment batch (Punica summary, "The SGMV Operator"; Punica digest,
+ * section 5.4, add_lora SGMV semantics).  For every active position p of every tile
+ * with row = row_map ? row_map[p] : p:
+ *     v[row*ldv + j] = sum_k x[row*ldx + k] * A[slot][k][j]   for j <  rank[slot]
+ *     v[row*ldv + j] = 0                                      for rank[slot] <= j < r_max
+ * v (device fp32 [n_rows][ldv], ldv >= r_max, ldv % 4 == 0) is overwritten there
+ * and untouched elsewhere.  x: device fp16 [n_rows][ldx], ldx % 8 == 0, ldx >= d_in.
+ * One launch; needs no workspace (partial sums are combined inside a workgroup).
+ */
+int lora_sgmv_shrink(void *stream, float *v, int64_t ldv, const void *x, int64_t ldx,
+                     int32_t n_rows, const lora_weights *w, const lora_segments *seg);
+
+/*
+ * Expand for a segment batch: for every active position's row,
+ *     y[row*ldy + c] = fp16( y[row*ldy + c] + scale[slot] * sum_{j<rank} v[row*ldv + j] * B[slot][j][c] )
+ * y: device fp16 [n_rows][ldy] updated in place, ldy % 8 == 0, ldy >= d_out.
+ * Reads only v[row][0:rank].  One launch; needs no workspace.
+ */
+int lora_sgmv_expand(void *stream, void *y, int64_t ldy, const float *v, int64_t ldv,
+                     int32_t n_rows, const lora_weights *w, const lora_segments *seg);
+
+/* ---------------------------------------------------------------- BGMV (per-row slots) */
+/*
+ * Shrink with one slot per row (Punica digest, section 5.5, BGMV; blog reference
+ * loop: slot -1 = no adapter).  idx: device int32 [n_rows].  Same v contract as
+ * lora_sgmv_shrink with row = position.
+ */
+int lora_bgmv_shrink(void *stream, float *v, int64_t ldv, const void *x, int64_t ldx,
+                     const int32_t *idx, int32_t n_rows, const lora_weights *w);
+
+/* Expand with one slot per row; same y contract as lora_sgmv_expand. */
+int lora_bgmv_expand(void *stream, void *y, int64_t ldy, const float *v, int64_t ldv,
+                     const int32_t *idx, int32_t n_rows, const lora_weights *w);
+
+/*
+ * The whole add-on in decode form: lora_bgmv_shrink then lora_bgmv_expand on the
+ * same stream (two launches).  v (device fp32 [n_rows][ldv]) receives the shrink
+ * result as documented above.
+ */
+int lora_bgmv(void *stream, void *y, int64_t ldy, const void *x, int64_t ldx, const int32_t *idx,
+              int32_t n_rows, const lora_weights *w, float *v, int64_t ldv);
+
+/* ---------------------------------------------------------------- diagnostics */
+/*
+ * Timing hook: attach two hipEvent_t (created by the caller; either may be NULL) to
+ * the next kernel launch made by the calling thread (launched with
+ * hipExtLaunchKernelGGL, which records `start_event` when the kernel starts and
+ * `stop_event` when it ends, on the launch stream).  The pair is consumed by that
+ * one launch; for lora_bgmv it is the shrink launch.  This is the library's only
+ * other per-thread state.  Returns LORA_OK.
+ */
+int lora_set_launch_events(void *start_event, void *stop_event);
+
+const char *lora_last_error(void);   /* message of this thread's last failed call */
+const char *lora_status_str(int status);
+int lora_abi_version(void);          /* 1 */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LORA_SGMV_H */

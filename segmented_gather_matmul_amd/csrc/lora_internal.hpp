@@ -1,0 +1,28 @@
+// Internal helpers shared by the host-side code and the launchers of the library.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "lora_sgmv.h"
+
+namespace lora {
+
+// Records a formatted message for lora_last_error() and returns `code`.
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Host-side checks of a descriptor that read no device memory: layout, sizes,
+// non-null and 16-byte-aligned device pointers, page geometry.
+int check_weights_desc(const lora_weights *w);
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Rank-rows per shrink workgroup for a launch over n_tiles tiles (16 when a tile
+// may take the MFMA path, else 1, 2 or 4 to keep the grid near kTargetGroups).
+int32_t plan_shrink_jw(int32_t n_tiles, int32_t r_max, int32_t max_rows);
+
+constexpr int32_t kMfmaMinRows = 8;      // tiles with at least this many rows use MFMA
+constexpr int32_t kTargetGroups = 1024;  // shrink workgroups to aim for
+
+}  // namespace lora

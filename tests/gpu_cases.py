@@ -1,0 +1,174 @@
+"""Shared machinery of the GPU parity tests: device inputs, the two call forms, checks.
+
+Tolerance (fp16 inputs, fp32 accumulation, against the fp64 oracle), over the whole
+y tensor of the call:  max |y_gpu - y_ref| <= 1e-2 and
+||y_gpu - y_ref||_F / ||y_ref||_F <= 1e-3.  Rows without an adapter must be
+bit-identical to the base output; index metadata must be bit-exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from segmented_gather_matmul_amd import binding as B
+from segmented_gather_matmul_amd import workloads as wl
+
+TOL_MAX_ABS = 1e-2
+TOL_REL_FRO = 1e-3
+TOL_V_REL_FRO = 1e-5   # internal check of the shrink output v on active rows
+GUARD_ROWS = 3
+CANARY16 = 0x5A5A     # fp16 bit pattern written around y; must survive every call
+NAN32 = np.float32(np.nan)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def torch():
+    import torch as t
+    return t
+
+
+class DeviceCase:
+    """Inputs of one call on the GPU, with guard rows and padded leading dimensions."""
+
+    def __init__(self, x, y0, r_max, pad_y=8, pad_v=4):
+        t = torch()
+        n, d_in = x.shape
+        d_out = y0.shape[1]
+        self.n, self.d_in, self.d_out, self.r_max = n, d_in, d_out, r_max
+        G = GUARD_ROWS
+        xf = np.zeros((n + 2 * G, d_in + 8), dtype=np.float16)
+        xf[G:G + n, :d_in] = x
+        self.x_full = t.from_numpy(xf).cuda()
+        self.x = self.x_full[G:G + n]
+        yf = np.full((n + 2 * G, d_out + pad_y), CANARY16, dtype=np.uint16).view(np.float16)
+        yf[G:G + n, :d_out] = y0
+        self.y_init = yf.copy()
+        self.y_full = t.from_numpy(yf).cuda()
+        self.y = self.y_full[G:G + n]
+        ldv = -(-r_max // 4) * 4 + pad_v
+        vf = np.full((n + 2 * G, ldv), NAN32, dtype=np.float32)
+        self.v_init = vf.copy()
+        self.v_full = t.from_numpy(vf).cuda()
+        self.v = self.v_full[G:G + n]
+
+    def reset(self):
+        self.y_full.copy_(torch().from_numpy(self.y_init))
+        self.v_full.copy_(torch().from_numpy(self.v_init))
+
+    def results(self):
+        torch().cuda.synchronize()
+        return self.y_full.cpu().numpy(), self.v_full.cpu().numpy()
+
+
+def run_bgmv(w: B.Weights, dc: DeviceCase, idx, split_calls=False):
+    t = torch()
+    idx_d = t.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda()
+    if split_calls:
+        B.lora_bgmv_shrink(dc.v, dc.x, idx_d, w)
+        B.lora_bgmv_expand(dc.y, dc.v, idx_d, w)
+    else:
+        B.lora_bgmv(dc.y, dc.x, idx_d, w, dc.v)
+    return dc.results()
+
+
+def run_sgmv(w: B.Weights, dc: DeviceCase, idx=None, seg_ptr=None, seg_slot=None, max_tile_rows=64):
+    """Segment form.  With idx: rows are grouped by the library's builder (row_map);
+    with seg_ptr/seg_slot: contiguous segments, no row map."""
+    if idx is not None:
+        row_map, seg_ptr, seg_slot, n_act = B.lora_build_segments(idx, w.num_slots)
+        want = oracle.build_segments(idx, w.num_slots)
+        for g, e in zip((row_map, seg_ptr, seg_slot), want[:3]):
+            assert np.array_equal(g, e), "metadata differs from the reference builder"
+        n_pos = n_act
+    else:
+        row_map, n_pos = None, dc.n
+    tiles = B.lora_build_tiles(seg_ptr, seg_slot, max_tile_rows)
+    nprob, msgs = oracle.check_tiles(tiles, seg_ptr, seg_slot, max_tile_rows)
+    assert nprob == 0, msgs[:3]
+    segs = B.segments_to_device(tiles, row_map, n_pos)
+    host = B.CSegments()
+    host.n_tiles, host.tiles = len(tiles), tiles.ctypes.data if len(tiles) else None
+    host.row_map = row_map.ctypes.data if row_map is not None else None
+    host.n_pos = n_pos
+    host.max_rows = segs.c.max_rows
+    B.lora_validate_segments_host(host, dc.n, w.num_slots)
+    B.lora_sgmv_shrink(dc.v, dc.x, w, segs)
+    B.lora_sgmv_expand(dc.y, dc.v, w, segs)
+    return dc.results()
+
+
+def check(dc: DeviceCase, y_full, v_full, y_ref, v_ref, active, label=""):
+    """Tolerance on the whole y, bit-exact untouched rows and guard bands, v on active rows."""
+    G, n, d_out, r_max = GUARD_ROWS, dc.n, dc.d_out, dc.r_max
+    yi = dc.y_init
+    # guard rows and padding columns untouched (bitwise)
+    assert np.array_equal(y_full[:G].view(np.uint16), yi[:G].view(np.uint16)), f"{label}: y guard rows written"
+    assert np.array_equal(y_full[G + n:].view(np.uint16), yi[G + n:].view(np.uint16)), f"{label}: y guard rows written"
+    assert np.array_equal(y_full[G:G + n, d_out:].view(np.uint16), yi[G:G + n, d_out:].view(np.uint16)), \
+        f"{label}: y padding columns written"
+    assert np.isnan(v_full[:G]).all() and np.isnan(v_full[G + n:]).all(), f"{label}: v guard rows written"
+    assert np.isnan(v_full[G:G + n, r_max:]).all(), f"{label}: v padding columns written"
+    y = y_full[G:G + n, :d_out]
+    v = v_full[G:G + n, :r_max]
+    y0 = yi[G:G + n, :d_out]
+    # rows without adapter: y bit-identical, v untouched
+    inact = ~active
+    assert np.array_equal(y[inact].view(np.uint16), y0[inact].view(np.uint16)), f"{label}: inactive row changed"
+    assert np.isnan(v[inact]).all(), f"{label}: v of an inactive row written"
+    # whole-y tolerance against the fp64 oracle
+    yg = y.astype(np.float64)
+    assert np.isfinite(yg).all(), f"{label}: non-finite output"
+    max_abs = float(np.abs(yg - y_ref).max()) if yg.size else 0.0
+    rel = float(np.linalg.norm(yg - y_ref) / max(np.linalg.norm(y_ref), 1e-300)) if yg.size else 0.0
+    say(f"  {label}: max|dy| = {max_abs:.3e}  rel_F = {rel:.3e}")
+    assert max_abs <= TOL_MAX_ABS, f"{label}: max abs error {max_abs}"
+    assert rel <= TOL_REL_FRO, f"{label}: relative Frobenius error {rel}"
+    if active.any():
+        va, vr = v[active].astype(np.float64), v_ref[active]
+        assert np.isfinite(va).all(), f"{label}: v not written on an active row"
+        vrel = float(np.linalg.norm(va - vr) / max(np.linalg.norm(vr), 1e-300))
+        assert vrel <= TOL_V_REL_FRO, f"{label}: v rel error {vrel}"
+    return max_abs, rel
+
+
+def active_rows(idx, rank):
+    idx = np.asarray(idx)
+    rank = np.asarray(rank)
+    act = idx >= 0
+    act[act] = rank[idx[act]] > 0
+    return act
+
+
+def dense_case(cfg_id, proj, n, d_in, d_out, num_slots, rank, scale, idx, r_max=None):
+    x, y0 = wl.activations(cfg_id, proj, n, d_in, d_out)
+    store = wl.dense_store(cfg_id, proj, num_slots, d_in, d_out, rank, scale, r_max=r_max, fill=np.unique(idx))
+    return x, y0, store
+
+
+def paged_device_pool(cfg_id, proj, rank, d_in, d_out, page_elems, touched):
+    """Full scattered pool on the GPU (NaN outside the touched slots' pages) and a
+    compact host pool holding only the touched pages, for the oracle."""
+    t = torch()
+    pt, a_off, b_off, num_pages = wl.page_placement(cfg_id, proj, rank, d_in, d_out, page_elems)
+    pool = t.full((num_pages, page_elems), float("nan"), dtype=t.float16, device="cuda")
+    pa, pb = d_in // page_elems, d_out // page_elems
+    pages, rows = [], []
+    for s in sorted(set(int(s) for s in touched if s >= 0)):
+        r = int(rank[s])
+        if not r:
+            continue
+        a_t, b = wl.slot_matrices(cfg_id, proj, s, r, d_in, d_out)
+        ia = pt[a_off[s]:a_off[s] + r * pa]
+        ib = pt[b_off[s]:b_off[s] + r * pb]
+        pages += [ia, ib]
+        rows += [a_t.reshape(-1, page_elems), b.reshape(-1, page_elems)]
+    pages = np.concatenate(pages).astype(np.int64)
+    rows = np.concatenate(rows)
+    pool[t.from_numpy(pages).cuda()] = t.from_numpy(rows).cuda()
+    inverse = np.full(num_pages, -1, dtype=np.int32)
+    inverse[pages] = np.arange(len(pages), dtype=np.int32)
+    compact_pt = inverse[pt]
+    return pool, pt, a_off, b_off, rows, compact_pt
