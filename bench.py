@@ -68,7 +68,12 @@ class Op:
     """One adapted projection of one layer: its weights, activations and launch metadata."""
 
 
+# Projections of a layer that read the same input (one x tensor, one launch when grouped).
+INPUT_GROUPS = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+
+
 def make_ops(spec, layers, device):
+    """Per layer: one x per input group, one y, v and weight descriptor per projection."""
     import torch
     from segmented_gather_matmul_amd import binding as B
     b = spec["batch"]
@@ -79,73 +84,110 @@ def make_ops(spec, layers, device):
     if spec["form"].startswith("sgmv"):
         if spec["form"] == "sgmv":
             row_map, seg_ptr, seg_slot, n_act = B.lora_build_segments(b.idx, S)
-            tiles = B.lora_build_tiles(seg_ptr, seg_slot)
+            tiles = B.lora_build_tiles(seg_ptr, seg_slot, 16)
             segs = B.segments_to_device(tiles, row_map, n_act, device)
         else:
-            tiles = B.lora_build_tiles(b.seg_ptr, b.seg_slot)
+            tiles = B.lora_build_tiles(b.seg_ptr, b.seg_slot, 16)
             segs = B.segments_to_device(tiles, None, n, device)
     rank_d = torch.from_numpy(rank.astype(np.int32)).to(device)
     scale_d = torch.from_numpy(spec["scale"].astype(np.float32)).to(device)
     gen = torch.Generator(device=device)
-    ops = []
+    names = list(spec["shapes"])
+    ldv = max(4, -(-r_max // 4) * 4)
+    groups = []
     for layer in range(layers):
-        for pname, (d_in, d_out) in spec["shapes"].items():
-            pid = list(spec["shapes"]).index(pname)
-            gen.manual_seed(spec["cfg_id"] * 1_000_003 + layer * 101 + pid)
+        for grp in INPUT_GROUPS:
+            gen.manual_seed(spec["cfg_id"] * 1_000_003 + layer * 101 + 50 + names.index(grp[0]))
+            d_in = spec["shapes"][grp[0]][0]
+            x = (torch.randn(n, d_in, generator=gen, device=device, dtype=torch.float32) * 0.02).half()
+            ops = []
+            for pname in grp:
+                d_in_p, d_out = spec["shapes"][pname]
+                assert d_in_p == d_in
+                pid = names.index(pname)
+                gen.manual_seed(spec["cfg_id"] * 1_000_003 + layer * 101 + pid)
 
-            def rnd(*shape):
-                return (torch.randn(*shape, generator=gen, device=device, dtype=torch.float32) * 0.02).half()
+                def rnd(*shape):
+                    return (torch.randn(*shape, generator=gen, device=device, dtype=torch.float32) * 0.02).half()
 
-            op = Op()
-            op.layer, op.proj, op.d_in, op.d_out = layer, pname, d_in, d_out
-            op.x = rnd(n, d_in)
-            op.y = rnd(n, d_out)
-            if spec["layout"] == "dense":
-                a_t = rnd(S, r_max, d_in)
-                bb = rnd(S, r_max, d_out)
-                op.w = B.Weights(num_slots=S, d_in=d_in, d_out=d_out, r_max=r_max, rank=rank_d, scale=scale_d,
-                                 a_t=a_t, b=bb)
-            else:
-                from segmented_gather_matmul_amd import workloads as wl
-                P = spec["page_elems"]
-                pt, a_off, b_off, num_pages = wl.page_placement(spec["cfg_id"], layer * 7 + pid, rank, d_in,
-                                                                d_out, P)
-                pool = torch.empty((num_pages, P), dtype=torch.float16, device=device)
-                for c0 in range(0, num_pages, 1 << 20):
-                    c1 = min(num_pages, c0 + (1 << 20))
-                    pool[c0:c1] = rnd(c1 - c0, P)
-                op.w = B.Weights(num_slots=S, d_in=d_in, d_out=d_out, r_max=r_max, rank=rank_d, scale=scale_d,
-                                 pool=pool, page_elems=P, page_table=torch.from_numpy(pt).to(device),
-                                 a_pt_off=torch.from_numpy(a_off).to(device),
-                                 b_pt_off=torch.from_numpy(b_off).to(device))
-            op.v = torch.zeros((n, max(4, -(-r_max // 4) * 4)), dtype=torch.float32, device=device)
-            op.idx, op.segs = idx_d, segs
-            ops.append(op)
-    # one v buffer serves every op of the step (same stream, in order)
-    v = torch.zeros_like(ops[0].v)
-    for o in ops:
-        o.v = v
-    return ops
+                op = Op()
+                op.layer, op.proj, op.d_in, op.d_out = layer, pname, d_in, d_out
+                op.x = x
+                op.y = rnd(n, d_out)
+                if spec["layout"] == "dense":
+                    op.w = B.Weights(num_slots=S, d_in=d_in, d_out=d_out, r_max=r_max, rank=rank_d, scale=scale_d,
+                                     a_t=rnd(S, r_max, d_in), b=rnd(S, r_max, d_out))
+                else:
+                    from segmented_gather_matmul_amd import workloads as wl
+                    P = spec["page_elems"]
+                    pt, a_off, b_off, num_pages = wl.page_placement(spec["cfg_id"], layer * 7 + pid, rank, d_in,
+                                                                    d_out, P)
+                    pool = torch.empty((num_pages, P), dtype=torch.float16, device=device)
+                    for c0 in range(0, num_pages, 1 << 20):
+                        c1 = min(num_pages, c0 + (1 << 20))
+                        pool[c0:c1] = rnd(c1 - c0, P)
+                    op.w = B.Weights(num_slots=S, d_in=d_in, d_out=d_out, r_max=r_max, rank=rank_d,
+                                     scale=scale_d, pool=pool, page_elems=P,
+                                     page_table=torch.from_numpy(pt).to(device),
+                                     a_pt_off=torch.from_numpy(a_off).to(device),
+                                     b_pt_off=torch.from_numpy(b_off).to(device))
+                op.v = torch.zeros((n, ldv), dtype=torch.float32, device=device)
+                op.idx, op.segs = idx_d, segs
+                ops.append(op)
+            groups.append(ops)
+    return groups
 
 
-def launch_op(op, kernel):
+def launch_group(ops, kernel, grouped):
+    """One launch for the whole group (grouped) or one launch per projection."""
     from segmented_gather_matmul_amd import binding as B
-    if op.segs is None:
+    op0 = ops[0]
+    if not grouped or len(ops) == 1:
+        for op in ops:
+            if op.segs is None:
+                if kernel == "shrink":
+                    B.lora_bgmv_shrink(op.v, op.x, op.idx, op.w)
+                else:
+                    B.lora_bgmv_expand(op.y, op.v, op.idx, op.w)
+            else:
+                if kernel == "shrink":
+                    B.lora_sgmv_shrink(op.v, op.x, op.w, op.segs)
+                else:
+                    B.lora_sgmv_expand(op.y, op.v, op.w, op.segs)
+        return
+    items = [(op.w, op.v, op.y) for op in ops]
+    n = op0.x.shape[0]
+    if op0.segs is None:
         if kernel == "shrink":
-            B.lora_bgmv_shrink(op.v, op.x, op.idx, op.w)
+            B.lora_bgmv_shrink_multi(op0.x, op0.idx, items)
         else:
-            B.lora_bgmv_expand(op.y, op.v, op.idx, op.w)
+            B.lora_bgmv_expand_multi(op0.idx, items, n)
     else:
         if kernel == "shrink":
-            B.lora_sgmv_shrink(op.v, op.x, op.w, op.segs)
+            B.lora_sgmv_shrink_multi(op0.x, op0.segs, items)
         else:
-            B.lora_sgmv_expand(op.y, op.v, op.w, op.segs)
+            B.lora_sgmv_expand_multi(op0.segs, items, n)
 
 
-def step(ops):
-    for op in ops:
-        launch_op(op, "shrink")
-        launch_op(op, "expand")
+def launches(groups, grouped):
+    """(kernel, ops) of every launch of one step, in order."""
+    out = []
+    for ops in groups:
+        units = [ops] if grouped else [[op] for op in ops]
+        for k in ("shrink", "expand"):
+            out += [(k, u) for u in units]
+    return out
+
+
+def step(groups, grouped):
+    for ops in groups:
+        if grouped:
+            launch_group(ops, "shrink", True)
+            launch_group(ops, "expand", True)
+        else:
+            for op in ops:
+                launch_group([op], "shrink", False)
+                launch_group([op], "expand", False)
 
 
 # ------------------------------------------------------------------ HIP events (raw handles)
@@ -172,41 +214,44 @@ class HipEvents:
         self.hip.hipEventDestroy(e)
 
 
-def kernel_durations(ops, steps):
-    """Average duration of every launch of each kernel, from event pairs attached to
-    the launches themselves (hipExtLaunchKernel records start/stop on the stream)."""
+def kernel_durations(groups, grouped, steps):
+    """Duration of every launch, from event pairs attached to the launches themselves
+    (hipExtLaunchKernel records start and stop on the launch stream)."""
     from segmented_gather_matmul_amd import binding as B
     import torch
     ev = HipEvents()
-    pairs = {"shrink": [], "expand": []}
+    recs = []
     for _ in range(steps):
-        for op in ops:
-            for k in ("shrink", "expand"):
-                e0, e1 = ev.create(), ev.create()
-                B.lora_set_launch_events(e0, e1)
-                launch_op(op, k)
-                pairs[k].append((op, e0, e1))
+        for ops in groups:
+            units = [ops] if grouped else [[op] for op in ops]
+            for u in units:
+                for k in ("shrink", "expand"):
+                    e0, e1 = ev.create(), ev.create()
+                    B.lora_set_launch_events(e0, e1)
+                    launch_group(u, k, grouped)
+                    recs.append((k, u, e0, e1))
     torch.cuda.synchronize()
-    out = {}
-    for k, lst in pairs.items():
-        ms = [ev.elapsed_ms(e0, e1) for _, e0, e1 in lst]
-        out[k] = dict(n=len(ms), avg_us=1e3 * float(np.mean(ms)), p10_us=1e3 * float(np.percentile(ms, 10)),
-                      p90_us=1e3 * float(np.percentile(ms, 90)), total_us=1e3 * float(np.sum(ms)),
-                      ops=[o for o, _, _ in lst])
-        for _, e0, e1 in lst:
-            ev.destroy(e0)
-            ev.destroy(e1)
+    out = {"shrink": [], "expand": []}
+    for k, u, e0, e1 in recs:
+        out[k].append((u, ev.elapsed_ms(e0, e1)))
+        ev.destroy(e0)
+        ev.destroy(e1)
     return out
 
 
 # ------------------------------------------------------------------ accounting
-def op_counts(spec, op):
+def unit_counts(spec, ops):
+    """Algorithmic bytes/flops of one launch over `ops` (projections sharing one x):
+    the shared x is read once; each projection adds its adapters, v and y traffic."""
     from segmented_gather_matmul_amd import costmodel as cm
     idx, rank, r_max = spec["batch"].idx, spec["rank"], int(spec["rank"].max())
-    return dict(shrink_bytes=cm.shrink_bytes(idx, rank, op.d_in, r_max),
-                expand_bytes=cm.expand_bytes(idx, rank, op.d_out, r_max),
-                shrink_flops=cm.shrink_flops(idx, rank, op.d_in),
-                expand_flops=cm.expand_flops(idx, rank, op.d_out))
+    n_act = int(cm.active_rows(idx, rank))
+    x_bytes = 2 * n_act * ops[0].d_in
+    sb = x_bytes + sum(cm.shrink_bytes(idx, rank, o.d_in, r_max) - x_bytes for o in ops)
+    eb = sum(cm.expand_bytes(idx, rank, o.d_out, r_max) for o in ops)
+    sf = sum(cm.shrink_flops(idx, rank, o.d_in) for o in ops)
+    ef = sum(cm.expand_flops(idx, rank, o.d_out) for o in ops)
+    return dict(shrink_bytes=sb, expand_bytes=eb, shrink_flops=sf, expand_flops=ef)
 
 
 def kernel_source_sha():
@@ -225,7 +270,7 @@ def traffic_from_profile(workload, kernel):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(spec, ops, budget_s=10.0):
+def cpu_baseline(spec, groups, budget_s=10.0):
     """The CPU oracle, as it is, on the same step: whole layers in order, repeated until
     about budget_s seconds of oracle time have run (inputs copied to host beforehand)."""
     import oracle
@@ -237,27 +282,26 @@ def cpu_baseline(spec, ops, budget_s=10.0):
     S, rank, scale = spec["num_slots"], spec["rank"], spec["scale"]
     r_max = int(rank.max())
     host = []
-    for op in ops:
-        store = wl.DenseStore(S, op.d_in, op.d_out, r_max, rank, scale, op.w.tensors[2].cpu().numpy(),
-                              op.w.tensors[3].cpu().numpy())
-        c = op_counts(spec, op)
-        host.append((op.layer, store, op.x.cpu().numpy(), op.y.cpu().numpy(), c["shrink_bytes"] + c["expand_bytes"]))
+    for ops in groups:
+        x = ops[0].x.cpu().numpy()
+        c = unit_counts(spec, ops)
+        stores = [(wl.DenseStore(S, op.d_in, op.d_out, r_max, rank, scale, op.w.tensors[2].cpu().numpy(),
+                                 op.w.tensors[3].cpu().numpy()), op.y.cpu().numpy()) for op in ops]
+        host.append((ops[0].layer, x, stores, c["shrink_bytes"] + c["expand_bytes"]))
     if spec["form"] != "bgmv":
         rm, sp, ss, _ = oracle.build_segments(b.idx, S)
     n_layers = len(set(h[0] for h in host))
     t_total, bytes_total, layers_done = 0.0, 0, 0
     while t_total < budget_s:
-        layer_t = 0.0
         for lay in range(n_layers):
-            for _, store, x, y0, nbytes in (h for h in host if h[0] == lay):
+            for _, x, stores, nbytes in (h for h in host if h[0] == lay):
                 t0 = time.perf_counter()
-                if spec["form"] == "bgmv":
-                    oracle.bgmv(store, x, y0, b.idx, nthreads=cores)
-                else:
-                    oracle.sgmv(store, x, y0, sp, ss, rm, nthreads=cores)
-                dt = time.perf_counter() - t0
-                t_total += dt
-                layer_t += dt
+                for store, y0 in stores:
+                    if spec["form"] == "bgmv":
+                        oracle.bgmv(store, x, y0, b.idx, nthreads=cores)
+                    else:
+                        oracle.sgmv(store, x, y0, sp, ss, rm, nthreads=cores)
+                t_total += time.perf_counter() - t0
                 bytes_total += nbytes
             layers_done += 1
             if t_total >= budget_s:
@@ -278,6 +322,7 @@ def main():
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--kernel-steps", type=int, default=5, help="steps of the per-launch event pass")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-group", action="store_true", help="one launch per projection (14 per layer)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -293,25 +338,27 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible")
     device = "cuda"
+    grouped = not args.no_group
     spec = workload_spec(args.workload)
     layers = args.layers or spec["layers"]
-    log(f"[bench] workload={args.workload} layers={layers} building inputs")
-    ops = make_ops(spec, layers, device)
+    log(f"[bench] workload={args.workload} layers={layers} grouped={grouped} building inputs")
+    groups = make_ops(spec, layers, device)
     torch.cuda.synchronize()
-    counts = [op_counts(spec, o) for o in ops]
+    counts = [unit_counts(spec, ops) for ops in groups]
     step_bytes = sum(c["shrink_bytes"] + c["expand_bytes"] for c in counts)
     step_flops = sum(c["shrink_flops"] + c["expand_flops"] for c in counts)
+    n_launch = len(launches(groups, grouped))
 
-    log(f"[bench] {len(ops)} ops/step, {step_bytes / 1e6:.1f} MB algorithmic per step; warmup {args.warmup}")
+    log(f"[bench] {n_launch} launches/step, {step_bytes / 1e6:.1f} MB algorithmic per step; warmup {args.warmup}")
     stream = torch.cuda.current_stream()
     if args.no_graph:
-        run = lambda: step(ops)
+        run = lambda: step(groups, grouped)
     else:
-        step(ops)  # first eager pass (loads kernels)
+        step(groups, grouped)  # first eager pass (loads kernels)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(ops)
+            step(groups, grouped)
         run = g.replay
     for _ in range(args.warmup):
         run()
@@ -328,28 +375,40 @@ def main():
     log(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step (wall {wall_ms:.4f})")
 
     log(f"[bench] per-launch event pass: {args.kernel_steps} steps")
-    kd = kernel_durations(ops, args.kernel_steps)
-    per_kernel = {}
+    kd = kernel_durations(groups, grouped, args.kernel_steps)
+    per_kernel, totals = {}, {}
     for k in ("shrink", "expand"):
-        d = kd[k]
-        kb = sum(op_counts(spec, o)[f"{k}_bytes"] for o in d["ops"])
-        kf = sum(op_counts(spec, o)[f"{k}_flops"] for o in d["ops"])
-        per_kernel[k] = dict(launches_per_step=len(ops), avg_us=round(d["avg_us"], 3), p10_us=round(d["p10_us"], 3),
-                             p90_us=round(d["p90_us"], 3), bytes_per_launch=kb / d["n"],
-                             gbs=round(kb / (d["total_us"] * 1e-6) / 1e9, 1),
-                             tflops=round(kf / (d["total_us"] * 1e-6) / 1e12, 3))
-    dom = max(per_kernel, key=lambda k: kd[k]["total_us"])
+        recs = kd[k]
+        us = np.array([1e3 * t for _, t in recs])
+        kb = sum(unit_counts(spec, u)[f"{k}_bytes"] for u, _ in recs)
+        kf = sum(unit_counts(spec, u)[f"{k}_flops"] for u, _ in recs)
+        totals[k] = float(us.sum())
+        per_kernel[k] = dict(launches_per_step=len(recs) // args.kernel_steps, avg_us=round(float(us.mean()), 3),
+                             p10_us=round(float(np.percentile(us, 10)), 3),
+                             p90_us=round(float(np.percentile(us, 90)), 3), bytes_per_launch=round(kb / len(recs)),
+                             gbs=round(kb / (totals[k] * 1e-6) / 1e9, 1),
+                             tflops=round(kf / (totals[k] * 1e-6) / 1e12, 3))
+    by_shape = {}
+    for k in ("shrink", "expand"):
+        for u, t in kd[k]:
+            key = f"{k} {'+'.join(o.proj for o in u)} {u[0].d_in}->{'/'.join(str(o.d_out) for o in u)}"
+            rec = by_shape.setdefault(key, [0, 0.0, unit_counts(spec, u)[f"{k}_bytes"]])
+            rec[0] += 1
+            rec[1] += 1e3 * t
+    by_shape = {key: dict(avg_us=round(t / n, 3), gbs=round(nb / (t / n * 1e-6) / 1e9, 1))
+                for key, (n, t, nb) in by_shape.items()}
+    dom = max(per_kernel, key=lambda k: totals[k])
     pk = per_kernel[dom]
     kernel_name = {"shrink": "lora_shrink_kernel", "expand": "lora_expand_kernel"}[dom]
     traffic = traffic_from_profile(args.workload, dom)
     roofline = dict(bound="hbm", achieved=pk["gbs"], peak=cm.HBM_PEAK_GBS, unit="GB/s",
                     frac=round(pk["gbs"] / cm.HBM_PEAK_GBS, 4), traffic=traffic, kernel=kernel_name,
-                    avg_launch_us=pk["avg_us"], algorithmic_bytes_per_launch=round(pk["bytes_per_launch"]))
+                    avg_launch_us=pk["avg_us"], algorithmic_bytes_per_launch=pk["bytes_per_launch"])
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
-        cpu = cpu_baseline(spec, ops, args.cpu_budget)
+        cpu = cpu_baseline(spec, groups, args.cpu_budget)
 
     gbs = step_bytes / (ms * 1e-3) / 1e9
     out = {
@@ -369,7 +428,8 @@ def main():
                    "projections": list(spec["shapes"]), "batch_rows": spec["batch"].n,
                    "num_slots": spec["num_slots"], "rank": sorted(set(int(r) for r in spec["rank"])),
                    "popularity": spec["popularity"], "form": spec["form"], "layout": spec["layout"],
-                   "launches_per_step": 2 * len(ops), "graph": not args.no_graph, "parallelism": "none"},
+                   "grouped": grouped, "launches_per_step": n_launch, "graph": not args.no_graph,
+                   "parallelism": "none"},
         "us_per_layer": round(1e3 * ms / layers, 3),
         "tflops": round(step_flops / (ms * 1e-3) / 1e12, 4),
         "step_bytes": step_bytes,
@@ -377,6 +437,7 @@ def main():
         "hbm_frac_step": round(gbs / cm.HBM_PEAK_GBS, 4),
         "wall_ms_per_step": round(wall_ms, 5),
         "kernels": per_kernel,
+        "launch_shapes": by_shape,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -123,6 +123,20 @@ typedef struct lora_segments {
                               * hint only: results do not depend on it */
 } lora_segments;
 
+/*
+ * One adapted projection of a launch that serves several projections of the same
+ * batch (e.g. q, k and v, which share their input x; or gate and up).
+ */
+typedef struct lora_proj {
+    const lora_weights *w;   /* adapters of this projection */
+    float *v;                /* device fp32 [n_rows][ldv], ldv >= w->r_max, ldv % 4 == 0 */
+    int64_t ldv;
+    void *y;                 /* expand: device fp16 [n_rows][ldy], ldy >= w->d_out, ldy % 8 == 0 */
+    int64_t ldy;             /* (shrink ignores y and ldy) */
+} lora_proj;
+
+#define LORA_MAX_PROJ 4      /* projections one launch can serve */
+
 /* ---------------------------------------------------------------- host metadata */
 /*
  * Group rows by adapter (Punica summary, "Batch Layout Construction": rows that share
@@ -213,6 +227,26 @@ int lora_bgmv_expand(void *stream, void *y, int64_t ldy, const float *v, int64_t
  */
 int lora_bgmv(void *stream, void *y, int64_t ldy, const void *x, int64_t ldx, const int32_t *idx,
               int32_t n_rows, const lora_weights *w, float *v, int64_t ldv);
+
+/* ---------------------------------------------------------------- several projections per launch */
+/*
+ * The same operations for up to LORA_MAX_PROJ projections of one batch in one launch
+ * each: every projection p gets exactly the result of the single-projection call
+ * with (proj[p].w, proj[p].v, proj[p].y).  This cuts the launches of a transformer
+ * layer from 14 to 8 (q/k/v and gate/up grouped) without changing the work.
+ * All projections of one launch must use the same weight layout
+ * (LORA_E_UNSUPPORTED otherwise); the shrink's projections share x, so they must
+ * share d_in (LORA_E_SHAPE otherwise).  Output regions of different projections
+ * must not overlap.  n_proj in 1..LORA_MAX_PROJ.
+ */
+int lora_sgmv_shrink_multi(void *stream, const void *x, int64_t ldx, int32_t n_rows,
+                           const lora_segments *seg, int32_t n_proj, const lora_proj *proj);
+int lora_sgmv_expand_multi(void *stream, int32_t n_rows, const lora_segments *seg, int32_t n_proj,
+                           const lora_proj *proj);
+int lora_bgmv_shrink_multi(void *stream, const void *x, int64_t ldx, const int32_t *idx,
+                           int32_t n_rows, int32_t n_proj, const lora_proj *proj);
+int lora_bgmv_expand_multi(void *stream, const int32_t *idx, int32_t n_rows, int32_t n_proj,
+                           const lora_proj *proj);
 
 /* ---------------------------------------------------------------- diagnostics */
 /*

@@ -30,7 +30,9 @@ MAX_TILE_ROWS = 64
 EXPORTS = ["lora_build_segments", "lora_tiles_bound", "lora_build_tiles", "lora_validate_weights_host",
            "lora_validate_segments_host", "lora_sgmv_shrink", "lora_sgmv_expand",
            "lora_bgmv_shrink", "lora_bgmv_expand", "lora_bgmv", "lora_last_error", "lora_status_str",
-           "lora_abi_version", "lora_set_launch_events"]
+           "lora_abi_version", "lora_set_launch_events", "lora_sgmv_shrink_multi", "lora_sgmv_expand_multi",
+           "lora_bgmv_shrink_multi", "lora_bgmv_expand_multi"]
+MAX_PROJ = 4
 
 
 class LoraError(RuntimeError):
@@ -46,6 +48,11 @@ class CWeights(ctypes.Structure):
                 ("pool", ctypes.c_void_p), ("num_pages", ctypes.c_int64), ("page_elems", ctypes.c_int32),
                 ("page_table", ctypes.c_void_p), ("pt_entries", ctypes.c_int64),
                 ("a_pt_off", ctypes.c_void_p), ("b_pt_off", ctypes.c_void_p)]
+
+
+class CProj(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("v", ctypes.c_void_p), ("ldv", ctypes.c_int64), ("y", ctypes.c_void_p),
+                ("ldy", ctypes.c_int64)]
 
 
 class CSegments(ctypes.Structure):
@@ -80,6 +87,10 @@ def lib() -> ctypes.CDLL:
             "lora_last_error": [],
             "lora_abi_version": [],
             "lora_set_launch_events": [P, P],
+            "lora_sgmv_shrink_multi": [P, P, I64, I32, P, I32, P],
+            "lora_sgmv_expand_multi": [P, I32, P, I32, P],
+            "lora_bgmv_shrink_multi": [P, P, I64, P, I32, I32, P],
+            "lora_bgmv_expand_multi": [P, P, I32, I32, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -267,3 +278,35 @@ def lora_bgmv(y, x, idx, weights: Weights, v, stream=None):
 def lora_set_launch_events(start_event, stop_event):
     """Attach raw hipEvent_t handles (ints) to this thread's next kernel launch."""
     _check(lib().lora_set_launch_events(start_event, stop_event))
+
+
+# ------------------------------------------------------------------ several projections per launch
+def proj_list(items):
+    """items: sequence of (Weights, v, y_or_None).  Returns a ctypes lora_proj array."""
+    arr = (CProj * len(items))()
+    for i, (w, v, y) in enumerate(items):
+        arr[i].w = ctypes.addressof(w.c)
+        arr[i].v, arr[i].ldv = _ptr(v), _ld(v)
+        arr[i].y, arr[i].ldy = (_ptr(y), _ld(y)) if y is not None else (None, 0)
+    return arr
+
+
+def lora_sgmv_shrink_multi(x, segments: Segments, items, n_rows=None, stream=None):
+    n_rows = x.shape[0] if n_rows is None else n_rows
+    arr = proj_list(items)
+    _check(lib().lora_sgmv_shrink_multi(_stream(stream), _ptr(x), _ld(x), int(n_rows), segments.ref, len(items), arr))
+
+
+def lora_sgmv_expand_multi(segments: Segments, items, n_rows, stream=None):
+    arr = proj_list(items)
+    _check(lib().lora_sgmv_expand_multi(_stream(stream), int(n_rows), segments.ref, len(items), arr))
+
+
+def lora_bgmv_shrink_multi(x, idx, items, stream=None):
+    arr = proj_list(items)
+    _check(lib().lora_bgmv_shrink_multi(_stream(stream), _ptr(x), _ld(x), _ptr(idx), int(x.shape[0]), len(items), arr))
+
+
+def lora_bgmv_expand_multi(idx, items, n_rows, stream=None):
+    arr = proj_list(items)
+    _check(lib().lora_bgmv_expand_multi(_stream(stream), _ptr(idx), int(n_rows), len(items), arr))

@@ -37,6 +37,11 @@ def _active_ranks(idx, rank):
     return r[r > 0]
 
 
+def active_rows(idx, rank):
+    """Rows with an adapter slot of rank > 0."""
+    return len(_active_ranks(idx, rank))
+
+
 def shrink_bytes(idx, rank, d_in, r_max):
     _, rd = _distinct_ranks(idx, rank)
     n_act = len(_active_ranks(idx, rank))

@@ -18,11 +18,11 @@ int check_weights_desc(const lora_weights *w);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Rank-rows per shrink workgroup for a launch over n_tiles tiles (16 when a tile
-// may take the MFMA path, else 1, 2 or 4 to keep the grid near kTargetGroups).
-int32_t plan_shrink_jw(int32_t n_tiles, int32_t r_max, int32_t max_rows);
+// Rank-rows per workgroup of a VALU shrink launch over `work_tiles` (tile,
+// projection) pairs: 1, 2 or 4, to keep the grid near kTargetGroups workgroups.
+int32_t plan_shrink_jw(int32_t work_tiles, int32_t r_max);
 
-constexpr int32_t kMfmaMinRows = 8;      // tiles with at least this many rows use MFMA
+constexpr int32_t kMfmaMinRows = 8;      // launches with a tile this tall run the MFMA kernels
 constexpr int32_t kTargetGroups = 1024;  // shrink workgroups to aim for
 
 }  // namespace lora

@@ -3,32 +3,32 @@
 // shrink  v[row][j] = sum_k x[row][k] A^T[s][j][k]      (Punica summary, "The SGMV Operator")
 // expand  y[row][c] += scale[s] sum_j v[row][j] B[s][j][c]
 //
-// Both kernels run over a flat work-list of tiles (a tile = up to 64 consecutive rows
-// of one segment, or one row in the per-row-slot form) instead of binding the adapter
-// to a grid dimension, so segments of 1 to thousands of rows share one launch.  A
-// workgroup is 4 wavefronts (256 lanes); workgroup ids are remapped so that the 8
-// XCDs (which take workgroups round-robin) each own a contiguous range of work
-// items, keeping the x rows and weights that neighbouring items share in one L2.
+// Work decomposition.  Both kernels run over a flat work-list of tiles (a tile = up to
+// 64 consecutive rows of one segment, or one row in the per-row-slot form) instead of
+// binding the adapter to a grid dimension, so segments of 1 to thousands of rows share
+// one launch.  One launch may also serve up to LORA_MAX_PROJ projections that share
+// the batch (q/k/v, gate/up): each work item is (tile, projection, slice) and the items
+// of one tile are consecutive.  A workgroup is 4 wavefronts (256 lanes); workgroup ids
+// are remapped so that each of the 8 XCDs (which take workgroups round-robin) owns a
+// contiguous range of items, so the x row and v row of a tile stay in one L2.
 //
-// Shrink.  Its output is only r wide, so parallelism comes from splitting the
-// rank-rows of a tile over workgroups (jw rank-rows each) and d_in over the 4
-// wavefronts of a workgroup.  The 4 partial sums are added in LDS in wavefront order:
-// no cross-workgroup reduction, no atomics, no workspace, and the result does not
-// depend on scheduling.
-//   - few rows (< 8, the decode case): fp16 dot2 (v_dot2_f32_f16) on 16-byte
-//     coalesced loads of x rows and A^T rank-rows, both contiguous in d_in.
-//   - 8..64 rows: v_mfma_f32_16x16x32_f16, one 16-rank slice per workgroup; both
-//     operands load straight from global memory (x rows and A^T rank-rows give each
-//     lane 8 consecutive k values).
+// Shrink.  The output is only r wide, so parallelism comes from splitting rank-rows
+// over workgroups (jw per workgroup) and d_in over the 4 wavefronts of a workgroup;
+// the 4 partial sums are added in LDS in wavefront order.  No cross-workgroup
+// reduction, no atomics, no workspace, and results do not depend on scheduling.
+//   - tiles of < 8 rows (decode): fp16 dot2 (v_dot2_f32_f16) on 16-byte coalesced
+//     loads of x rows and A^T rank-rows, both contiguous in d_in;
+//   - tiles of 8..64 rows: v_mfma_f32_16x16x32_f16 on a 16-rank slice; each lane
+//     loads 8 consecutive k of an x row and of an A^T rank-row straight from memory,
+//     four k-steps in flight.
 // Expand.  A workgroup owns 512 output columns of one tile.
-//   - few rows: each wavefront reads a quarter of the rank-rows of B (16-byte loads,
-//     contiguous in d_out), the quarters are added in LDS, and one fp32 -> fp16
-//     rounding updates y.
-//   - 8..64 rows: B[0:r][512 columns] is staged in LDS once and reused by every
-//     16-row slice; the product D^T = B^T (s v)^T runs on v_mfma_f32_16x16x16_f16
-//     with s*v split into fp16 hi + lo/2048 parts (two MFMAs) so that v keeps ~22
-//     bits; the accumulator starts from y, and each lane updates 4 consecutive y
-//     elements of one row.
+//   - tiles of < 8 rows: each wavefront loads its quarter of the rank-rows of B once
+//     (16-byte loads, contiguous in d_out, all in flight together), the quarters are
+//     added in LDS, and one fp32 -> fp16 rounding updates y;
+//   - tiles of 8..64 rows: B[0:r][512 columns] is staged in LDS and reused by every
+//     16-row slice; D^T = B^T (s v)^T runs on v_mfma_f32_16x16x16_f16 with s*v split
+//     into fp16 hi + lo/2048 parts (two MFMAs, ~22 bits kept); the accumulator starts
+//     from y and each lane updates 4 consecutive y elements of one row.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -58,6 +58,15 @@ struct WeightsDev {
     const int64_t *a_pt_off, *b_pt_off;
 };
 
+struct ProjDev {
+    WeightsDev w;
+    float *v;        // shrink output / expand input
+    int64_t ldv;
+    uint16_t *y;     // expand output
+    int64_t ldy;
+    int32_t slices;  // shrink: rank groups; expand: 512-column chunks
+};
+
 struct TileSrc {
     const lora_tile *tiles;   // segment form
     const int32_t *row_map;   // segment form, may be NULL
@@ -65,60 +74,34 @@ struct TileSrc {
     const int32_t *idx;       // per-row form
 };
 
-struct ShrinkArgs {
-    float *v;
-    int64_t ldv;
-    const uint16_t *x;
+struct Args {
+    const uint16_t *x;  // shrink input
     int64_t ldx;
-    int32_t n_rows, n_tiles;
+    int32_t n_rows, n_tiles, n_proj, per_tile, grid;
+    int32_t jw;         // shrink: rank-rows per workgroup
+    int32_t off[LORA_MAX_PROJ];  // first slice of projection p within a tile's items
     TileSrc ts;
-    WeightsDev w;
-    int32_t jw, n_jg, grid;
-};
-
-struct ExpandArgs {
-    uint16_t *y;
-    int64_t ldy;
-    const float *v;
-    int64_t ldv;
-    int32_t n_rows, n_tiles, n_cchunks, grid;
-    int32_t mfma;  // the launch may contain MFMA tiles (LDS holds a B chunk)
-    TileSrc ts;
-    WeightsDev w;
+    ProjDev p[LORA_MAX_PROJ];
 };
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kRowsPerPass = 4;
+constexpr int kRowsPerPass = 4;     // rows per pass of the VALU kernels (segment form)
 constexpr int kCols = 512;           // expand columns per workgroup
 constexpr int kBStride = kCols;      // LDS row stride of the staged B chunk (halves)
-
-struct TileInfo {
-    int32_t slot, pos0, nrows, rank;
-};
+constexpr int kMaxRankPerWave = LORA_MAX_RANK / kWaves;
+constexpr int kMfmaShrinkThreads = 1024;  // 16 wavefronts split d_in in the MFMA shrink
 
 // Contiguous work ranges per XCD: workgroup b runs on XCD b % 8; grid % 8 == 0.
 __device__ inline int work_item(int b, int grid) { return (b & 7) * (grid >> 3) + (b >> 3); }
 
-// Resolves work tile `t`; rank 0 means "nothing to do" (no adapter, rank 0, or a
-// slot outside the descriptor).
-template <bool PERROW>
-__device__ inline TileInfo load_tile(const TileSrc &ts, const WeightsDev &w, int t)
+// Projection of slice `r` of a tile's items (uniform over the workgroup).
+__device__ inline int proj_of(const Args &a, int r)
 {
-    TileInfo ti;
-    if (PERROW) {
-        ti.slot = ts.idx[t];
-        ti.pos0 = t;
-        ti.nrows = 1;
-    } else {
-        const lora_tile tl = ts.tiles[t];
-        ti.slot = tl.slot;
-        ti.pos0 = tl.pos0;
-        ti.nrows = min(tl.nrows, LORA_MAX_TILE_ROWS);
-    }
-    ti.rank = 0;
-    if (ti.slot >= 0 && ti.slot < w.num_slots && ti.nrows > 0) ti.rank = min(w.rank[ti.slot], w.r_max);
-    return ti;
+    int p = 0;
+#pragma unroll
+    for (int q = 1; q < LORA_MAX_PROJ; ++q) p += (q < a.n_proj && r >= a.off[q]) ? 1 : 0;
+    return p;
 }
 
 // Row of position `pos`, or -1 when it falls outside the row map or the row range.
@@ -172,33 +155,91 @@ __device__ inline float wave_sum(float s)
     return s;
 }
 
-// ------------------------------------------------------------------------ shrink
-// Rows without an MFMA tile: workgroup = one tile x rank-rows [j0, j1);
-// RJ rank-rows per pass, d_in striped over all 256 lanes (16 bytes each).
-template <bool PAGED, bool PERROW, int RJ>
-__device__ void shrink_valu(const ShrinkArgs &a, const TileInfo &ti, int j0, int j1, float *red)
+// ------------------------------------------------------------------------ common head
+// Slot and rows of work tile `t`.  The slot's rank is read separately: the dense
+// layout holds r_max rank-rows per slot, so loads of rank-rows below r_max are in
+// bounds and can be issued before the rank arrives (rows at or past the rank are
+// masked out of every result); the paged layout reads only rank-rows below the rank.
+struct TileHead {
+    int32_t slot, pos0, nrows;
+    bool valid;
+};
+
+template <bool PERROW>
+__device__ inline TileHead tile_head(const TileSrc &ts, const WeightsDev &w, int t)
 {
+    TileHead th;
+    if (PERROW) {
+        th.slot = ts.idx[t];
+        th.pos0 = t;
+        th.nrows = 1;
+    } else {
+        const lora_tile tl = ts.tiles[t];
+        th.slot = tl.slot;
+        th.pos0 = tl.pos0;
+        th.nrows = min(tl.nrows, LORA_MAX_TILE_ROWS);
+    }
+    th.valid = th.slot >= 0 && th.slot < w.num_slots && th.nrows > 0;
+    return th;
+}
+
+__device__ inline int slot_rank(const WeightsDev &w, int slot) { return max(0, min(w.rank[slot], w.r_max)); }
+
+// Work item of this workgroup: tile, projection and slice within the projection.
+struct Item {
+    int tile, p, slice;
+    bool ok;
+};
+
+__device__ inline Item work(const Args &a)
+{
+    Item it;
+    const int wi = work_item(blockIdx.x, a.grid);
+    it.tile = wi / a.per_tile;
+    const int sl = wi - it.tile * a.per_tile;
+    it.p = proj_of(a, sl);
+    it.slice = sl - a.off[it.p];
+    it.ok = it.tile < a.n_tiles && it.slice < a.p[it.p].slices;
+    return it;
+}
+
+// ------------------------------------------------------------------------ shrink
+// VALU shrink.  Workgroup = one tile x rank-rows [j0, j0 + jw); NR rows and RJ
+// rank-rows per pass; d_in striped over the 256 lanes, 16 bytes per lane per load.
+template <bool PAGED, bool PERROW, int RJ, int NR>
+__global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
+{
+    __shared__ float red[kWaves * NR * RJ];
+    const Item it = work(a);
+    if (!it.ok) return;
+    const ProjDev &pd = a.p[it.p];
+    const int j0 = it.slice * a.jw;
+    const int jend = min(j0 + a.jw, pd.w.r_max);
+    const TileHead th = tile_head<PERROW>(a.ts, pd.w, it.tile);
+    if (!th.valid || j0 >= jend) return;
+    const int rank = slot_rank(pd.w, th.slot);
+    const int jload = PAGED ? min(jend, rank) : jend;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n_oct = a.w.d_in >> 3;
+    const int n_oct = pd.w.d_in >> 3;
     const uint4 z4 = make_uint4(0, 0, 0, 0);
-    for (int rg = 0; rg < ti.nrows; rg += kRowsPerPass) {
-        int rows[kRowsPerPass];
+    for (int rg = 0; rg < th.nrows; rg += NR) {
+        int rows[NR];
 #pragma unroll
-        for (int q = 0; q < kRowsPerPass; ++q)
-            rows[q] = (rg + q < ti.nrows) ? row_of<PERROW>(a.ts, ti.pos0 + rg + q, a.n_rows) : -1;
-        for (int jb = j0; jb < j1; jb += RJ) {
-            float acc[kRowsPerPass][RJ];
+        for (int q = 0; q < NR; ++q)
+            rows[q] = (rg + q < th.nrows) ? row_of<PERROW>(a.ts, th.pos0 + rg + q, a.n_rows) : -1;
+        for (int jb = j0; jb < jend; jb += RJ) {
+            float acc[NR][RJ];
 #pragma unroll
-            for (int q = 0; q < kRowsPerPass; ++q)
+            for (int q = 0; q < NR; ++q)
 #pragma unroll
                 for (int jj = 0; jj < RJ; ++jj) acc[q][jj] = 0.f;
             // two octets per lane per iteration keep more loads in flight
             for (int o = tid; o < n_oct; o += 2 * kThreads) {
                 const int o2 = o + kThreads;
                 const bool in2 = o2 < n_oct;
-                uint4 xv[kRowsPerPass], xw[kRowsPerPass], av[RJ], aw[RJ];
+                uint4 xv[NR], xw[NR], av[RJ], aw[RJ];
 #pragma unroll
-                for (int q = 0; q < kRowsPerPass; ++q) {
+                for (int q = 0; q < NR; ++q) {
                     const uint16_t *xr = a.x + (int64_t)(rows[q] < 0 ? 0 : rows[q]) * a.ldx;
                     xv[q] = rows[q] >= 0 ? load16(xr + 8 * o) : z4;
                     xw[q] = (rows[q] >= 0 && in2) ? load16(xr + 8 * o2) : z4;
@@ -206,264 +247,288 @@ __device__ void shrink_valu(const ShrinkArgs &a, const TileInfo &ti, int j0, int
 #pragma unroll
                 for (int jj = 0; jj < RJ; ++jj) {
                     av[jj] = aw[jj] = z4;
-                    if (jb + jj < j1) {
-                        const uint16_t *p = rank_row_ptr<PAGED, false>(a.w, ti.slot, jb + jj, 8 * o);
+                    if (jb + jj < jload) {
+                        const uint16_t *p = rank_row_ptr<PAGED, false>(pd.w, th.slot, jb + jj, 8 * o);
                         if (p) av[jj] = load16(p);
                         if (in2) {
-                            const uint16_t *p2 = rank_row_ptr<PAGED, false>(a.w, ti.slot, jb + jj, 8 * o2);
+                            const uint16_t *p2 = rank_row_ptr<PAGED, false>(pd.w, th.slot, jb + jj, 8 * o2);
                             if (p2) aw[jj] = load16(p2);
                         }
                     }
                 }
 #pragma unroll
-                for (int q = 0; q < kRowsPerPass; ++q)
+                for (int q = 0; q < NR; ++q)
 #pragma unroll
                     for (int jj = 0; jj < RJ; ++jj) acc[q][jj] = dot8(xw[q], aw[jj], dot8(xv[q], av[jj], acc[q][jj]));
             }
 #pragma unroll
-            for (int q = 0; q < kRowsPerPass; ++q)
+            for (int q = 0; q < NR; ++q)
 #pragma unroll
                 for (int jj = 0; jj < RJ; ++jj) {
                     const float s = wave_sum(acc[q][jj]);
-                    if (lane == 0) red[wave * kRowsPerPass * RJ + q * RJ + jj] = s;
+                    if (lane == 0) red[wave * NR * RJ + q * RJ + jj] = s;
                 }
             __syncthreads();
-            if (tid < kRowsPerPass * RJ) {
-                const int q = tid / RJ, jj = tid - q * RJ;
+            if (tid < NR * RJ && rank > 0) {
+                const int q = tid / RJ, jj = tid - q * RJ, j = jb + jj;
                 // wavefront order: the same sum for every launch of this shape
-                const float s = red[tid] + red[kRowsPerPass * RJ + tid] + red[2 * kRowsPerPass * RJ + tid] +
-                                red[3 * kRowsPerPass * RJ + tid];
-                if (rows[q] >= 0 && jb + jj < j1) a.v[(int64_t)rows[q] * a.ldv + jb + jj] = s;
+                const float s = red[tid] + red[NR * RJ + tid] + red[2 * NR * RJ + tid] + red[3 * NR * RJ + tid];
+                if (rows[q] >= 0 && j < jend) pd.v[(int64_t)rows[q] * pd.ldv + j] = j < rank ? s : 0.f;
             }
             __syncthreads();
         }
     }
 }
 
-// 8..64 rows: MFMA 16x16x32 over (16-row slices) x (16 rank slice j0..j0+15); the 4
-// wavefronts take interleaved 32-wide k-steps and their sums are added in LDS.
-template <bool PAGED, bool PERROW>
-__device__ void shrink_mfma(const ShrinkArgs &a, const TileInfo &ti, int j0, float *red)
+// MFMA shrink for tiles of up to 64 rows: v_mfma_f32_16x16x32_f16 over (16-row
+// slices) x (ranks j0 .. j0+15).  16 wavefronts take interleaved 32-wide k-steps,
+// 8 / MTX of them in flight each, and their sums are added in LDS in wavefront order.
+template <bool PAGED, int MTX>
+__global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Args a)
 {
+    constexpr int W = kMfmaShrinkThreads / 64;
+    constexpr int U = 8 / MTX;  // k-steps in flight per wavefront
+    __shared__ float red[W * 1024];
+    const Item it = work(a);
+    if (!it.ok) return;
+    const ProjDev &pd = a.p[it.p];
+    const int j0 = it.slice * 16;
+    if (j0 >= pd.w.r_max) return;
+    const TileHead th = tile_head<false>(a.ts, pd.w, it.tile);
+    if (!th.valid) return;
+    const int rank = slot_rank(pd.w, th.slot);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;       // operand row/col, k-group of the lane
-    const int MT = (ti.nrows + 15) >> 4;
-    const int r = ti.rank;
+    const int MT = min((th.nrows + 15) >> 4, MTX);
     const int jcol = j0 + li;                        // this lane's rank column (B operand)
-    int xrow[4];
+    const bool jload = jcol < (PAGED ? rank : pd.w.r_max);
+    int xrow[MTX];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < MTX; ++mt) {
         const int rr = 16 * mt + li;
-        xrow[mt] = (mt < MT && rr < ti.nrows) ? row_of<PERROW>(a.ts, ti.pos0 + rr, a.n_rows) : -1;
+        xrow[mt] = (mt < MT && rr < th.nrows) ? row_of<false>(a.ts, th.pos0 + rr, a.n_rows) : -1;
     }
-    f4_t acc[4];
+    f4_t acc[MTX];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = f4_t{0.f, 0.f, 0.f, 0.f};
-    const int d_in = a.w.d_in;
+    for (int mt = 0; mt < MTX; ++mt) acc[mt] = f4_t{0.f, 0.f, 0.f, 0.f};
+    const int d_in = pd.w.d_in;
     const int steps = (d_in + 31) >> 5;
     const uint4 z4 = make_uint4(0, 0, 0, 0);
-    for (int s = wave; s < steps; s += kWaves) {
-        const int k = 32 * s + 8 * lg;
-        const bool kin = k < d_in;
-        uint4 bq = z4;
-        if (kin && jcol < r) {
-            const uint16_t *p = rank_row_ptr<PAGED, false>(a.w, ti.slot, jcol, k);
-            if (p) bq = load16(p);
-        }
-        const h8_t bop = __builtin_bit_cast(h8_t, bq);
+    for (int s0 = wave; s0 < steps; s0 += W * U) {
+        uint4 bq[U], xq[U][MTX];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            if (mt >= MT) break;
-            const uint4 xq = (kin && xrow[mt] >= 0) ? load16(a.x + (int64_t)xrow[mt] * a.ldx + k) : z4;
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xq), bop, acc[mt], 0, 0, 0);
+        for (int u = 0; u < U; ++u) {
+            const int k = 32 * (s0 + W * u) + 8 * lg;
+            const bool kin = k < d_in;
+            bq[u] = z4;
+            if (kin && jload) {
+                const uint16_t *p = rank_row_ptr<PAGED, false>(pd.w, th.slot, jcol, k);
+                if (p) bq[u] = load16(p);
+            }
+#pragma unroll
+            for (int mt = 0; mt < MTX; ++mt)
+                xq[u][mt] = (kin && xrow[mt] >= 0) ? load16(a.x + (int64_t)xrow[mt] * a.ldx + k) : z4;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const h8_t bop = __builtin_bit_cast(h8_t, bq[u]);
+#pragma unroll
+            for (int mt = 0; mt < MTX; ++mt)
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xq[u][mt]), bop, acc[mt], 0,
+                                                                 0, 0);
         }
     }
     // D layout: lane holds rows 4*lg + e of the slice, rank column li.
-    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int mt = 0; mt < MTX; ++mt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) red[wave * 1024 + mt * 256 + (4 * lg + e) * 16 + li] = acc[mt][e];
     __syncthreads();
-    for (int o = tid; o < MT * 256; o += kThreads) {
+    if (rank <= 0) return;
+    for (int o = tid; o < MT * 256; o += kMfmaShrinkThreads) {
         const int mt = o >> 8, i = (o >> 4) & 15, j = o & 15;
         const int rr = 16 * mt + i, col = j0 + j;
-        if (rr >= ti.nrows || col >= a.w.r_max) continue;
-        const int row = row_of<PERROW>(a.ts, ti.pos0 + rr, a.n_rows);
+        if (rr >= th.nrows || col >= pd.w.r_max) continue;
+        const int row = row_of<false>(a.ts, th.pos0 + rr, a.n_rows);
         if (row < 0) continue;
-        const float s = red[o] + red[1024 + o] + red[2048 + o] + red[3072 + o];
-        a.v[(int64_t)row * a.ldv + col] = col < r ? s : 0.f;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) s += red[w * 1024 + o];
+        pd.v[(int64_t)row * pd.ldv + col] = col < rank ? s : 0.f;
     }
-}
-
-template <bool PAGED, bool PERROW, int RJ>
-__global__ __launch_bounds__(kThreads) void lora_shrink_kernel(ShrinkArgs a)
-{
-    __shared__ float red[kWaves * 1024];
-    const int wi = work_item(blockIdx.x, a.grid);
-    const int tile = wi / a.n_jg;
-    if (tile >= a.n_tiles) return;
-    const int jg = wi - tile * a.n_jg;
-    const TileInfo ti = load_tile<PERROW>(a.ts, a.w, tile);
-    if (ti.rank <= 0) return;
-    const int j0 = jg * a.jw;
-    const int jend = min(j0 + a.jw, a.w.r_max);
-    if (j0 >= jend) return;
-    if (!PERROW && ti.nrows >= kMfmaMinRows && a.jw == 16 && j0 < ti.rank) {
-        shrink_mfma<PAGED, PERROW>(a, ti, j0, red);
-        return;
-    }
-    // columns rank .. r_max-1 of the tile's rows are zero
-    const int z0 = max(j0, ti.rank);
-    if (z0 < jend) {
-        const int zc = jend - z0;
-        for (int e = threadIdx.x; e < ti.nrows * zc; e += kThreads) {
-            const int row = row_of<PERROW>(a.ts, ti.pos0 + e / zc, a.n_rows);
-            if (row >= 0) a.v[(int64_t)row * a.ldv + z0 + e % zc] = 0.f;
-        }
-    }
-    const int j1 = min(jend, ti.rank);
-    if (j0 < j1) shrink_valu<PAGED, PERROW, RJ>(a, ti, j0, j1, red);
 }
 
 // ------------------------------------------------------------------------ expand
-template <bool PAGED, bool PERROW>
-__device__ void expand_valu(const ExpandArgs &a, const TileInfo &ti, int c0, float *red)
+// VALU expand.  Workgroup = one tile x 512 columns; wavefront w holds rank-rows
+// w, w+4, ... of B (loaded once, all in flight); NR rows per pass; the four partial
+// sums are added in LDS and wavefront q updates row q of the pass.
+template <bool PAGED, bool PERROW, int NR>
+__global__ __launch_bounds__(kThreads) void lora_expand_valu_kernel(Args a)
 {
+    __shared__ float red[kWaves * NR * 8 * 64];
+    const Item it = work(a);
+    if (!it.ok) return;
+    const ProjDev &pd = a.p[it.p];
+    const TileHead th = tile_head<PERROW>(a.ts, pd.w, it.tile);
+    if (!th.valid) return;
+    const int rank = slot_rank(pd.w, th.slot);
+    const int jlim = PAGED ? rank : pd.w.r_max;
+    const float sc = pd.w.scale[th.slot];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = c0 + 8 * lane;
-    const bool cin = c < a.w.d_out;
-    const int r = ti.rank;
-    const float sc = a.w.scale[ti.slot];
-    for (int rg = 0; rg < ti.nrows; rg += kRowsPerPass) {
-        int rows[kRowsPerPass];
-        float sv[kRowsPerPass];  // lane j holds scale * v[row][j]
+    const int c = it.slice * kCols + 8 * lane;
+    const bool cin = c < pd.w.d_out;
+    uint4 bv[kMaxRankPerWave];
 #pragma unroll
-        for (int q = 0; q < kRowsPerPass; ++q) {
-            rows[q] = (rg + q < ti.nrows) ? row_of<PERROW>(a.ts, ti.pos0 + rg + q, a.n_rows) : -1;
-            sv[q] = (rows[q] >= 0 && lane < r) ? sc * a.v[(int64_t)rows[q] * a.ldv + lane] : 0.f;
+    for (int u = 0; u < kMaxRankPerWave; ++u) {
+        const int j = wave + kWaves * u;
+        bv[u] = make_uint4(0, 0, 0, 0);
+        if (cin && j < jlim) {
+            const uint16_t *p = rank_row_ptr<PAGED, true>(pd.w, th.slot, j, c);
+            if (p) bv[u] = load16(p);
         }
-        float acc[kRowsPerPass][8];
+    }
+    for (int rg = 0; rg < th.nrows; rg += NR) {
+        int rows[NR];
+        float sv[NR];  // lane j holds v[row][j]
 #pragma unroll
-        for (int q = 0; q < kRowsPerPass; ++q)
+        for (int q = 0; q < NR; ++q) {
+            rows[q] = (rg + q < th.nrows) ? row_of<PERROW>(a.ts, th.pos0 + rg + q, a.n_rows) : -1;
+            sv[q] = (rows[q] >= 0 && lane < pd.w.r_max) ? pd.v[(int64_t)rows[q] * pd.ldv + lane] : 0.f;
+        }
+        // the wavefront that updates row `wave` of the pass fetches that y octet now
+        const int my_row = (wave < NR && rg + wave < th.nrows) ? row_of<PERROW>(a.ts, th.pos0 + rg + wave, a.n_rows) : -1;
+        uint4 yv = make_uint4(0, 0, 0, 0);
+        if (my_row >= 0 && cin) yv = load16(pd.y + (int64_t)my_row * pd.ldy + c);
+#pragma unroll
+        for (int q = 0; q < NR; ++q) sv[q] = lane < rank ? sc * sv[q] : 0.f;
+        float acc[NR][8];
+#pragma unroll
+        for (int q = 0; q < NR; ++q)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
-        // wavefront w takes rank-rows w, w+4, ...; four of them per pass in flight
-        for (int jb = wave; jb < r; jb += 4 * kWaves) {
-            uint4 bv[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int j = jb + u * kWaves;
-                bv[u] = make_uint4(0, 0, 0, 0);
-                if (cin && j < r) {
-                    const uint16_t *p = rank_row_ptr<PAGED, true>(a.w, ti.slot, j, c);
-                    if (p) bv[u] = load16(p);
-                }
+        for (int u = 0; u < kMaxRankPerWave; ++u) {
+            const int j = wave + kWaves * u;
+            if (j >= rank) break;
+            const uint32_t bw[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
+            float bf[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bf[2 * e] = h2f((uint16_t)(bw[e] & 0xffff));
+                bf[2 * e + 1] = h2f((uint16_t)(bw[e] >> 16));
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int j = jb + u * kWaves;
-                if (j >= r) break;
-                const uint32_t bw[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
-                float bf[8];
+            for (int q = 0; q < NR; ++q) {
+                const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv[q]), j));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    bf[2 * e] = h2f((uint16_t)(bw[e] & 0xffff));
-                    bf[2 * e + 1] = h2f((uint16_t)(bw[e] >> 16));
-                }
-#pragma unroll
-                for (int q = 0; q < kRowsPerPass; ++q) {
-                    const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv[q]), j));
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[q][e] = __builtin_fmaf(s, bf[e], acc[q][e]);
-                }
+                for (int e = 0; e < 8; ++e) acc[q][e] = __builtin_fmaf(s, bf[e], acc[q][e]);
             }
         }
-        // red[wave][q][e][lane]
 #pragma unroll
-        for (int q = 0; q < kRowsPerPass; ++q)
+        for (int q = 0; q < NR; ++q)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) red[((wave * kRowsPerPass + q) * 8 + e) * 64 + lane] = acc[q][e];
+            for (int e = 0; e < 8; ++e) red[((wave * NR + q) * 8 + e) * 64 + lane] = acc[q][e];
         __syncthreads();
-        {
-            const int q = wave;  // wavefront q updates row q of the pass
-            if (rows[q] >= 0 && cin) {
-                uint16_t *yp = a.y + (int64_t)rows[q] * a.ldy + c;
-                const uint4 yv = load16(yp);
-                const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w};
-                uint32_t out[4];
+        if (my_row >= 0 && cin && rank > 0) {
+            const int q = wave;
+            const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w};
+            uint32_t out[4];
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    float d[2];
+            for (int e2 = 0; e2 < 4; ++e2) {
+                float d[2];
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int e = 2 * e2 + h;
-                        d[h] = red[((0 * kRowsPerPass + q) * 8 + e) * 64 + lane] +
-                               red[((1 * kRowsPerPass + q) * 8 + e) * 64 + lane] +
-                               red[((2 * kRowsPerPass + q) * 8 + e) * 64 + lane] +
-                               red[((3 * kRowsPerPass + q) * 8 + e) * 64 + lane];
-                    }
-                    const float lo = h2f((uint16_t)(yw[e2] & 0xffff)) + d[0];
-                    const float hi = h2f((uint16_t)(yw[e2] >> 16)) + d[1];
-                    out[e2] = (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
+                for (int h = 0; h < 2; ++h) {
+                    const int e = 2 * e2 + h;
+                    d[h] = red[((0 * NR + q) * 8 + e) * 64 + lane] + red[((1 * NR + q) * 8 + e) * 64 + lane] +
+                           red[((2 * NR + q) * 8 + e) * 64 + lane] + red[((3 * NR + q) * 8 + e) * 64 + lane];
                 }
-                *reinterpret_cast<uint4 *>(yp) = make_uint4(out[0], out[1], out[2], out[3]);
+                const float lo = h2f((uint16_t)(yw[e2] & 0xffff)) + d[0];
+                const float hi = h2f((uint16_t)(yw[e2] >> 16)) + d[1];
+                out[e2] = (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
             }
+            *reinterpret_cast<uint4 *>(pd.y + (int64_t)my_row * pd.ldy + c) = make_uint4(out[0], out[1], out[2], out[3]);
         }
         __syncthreads();
     }
 }
 
-// 8..64 rows: B chunk in LDS (row k at a column rotation of 8 * ((k >> 2) & 3)
-// halves, so the 4 k-groups of a wavefront read different banks), then per 16-row
-// slice D^T[cols][rows] = B^T (s v)^T with hi/lo fp16 operands.
-template <bool PAGED, bool PERROW>
-__device__ void expand_mfma(const ExpandArgs &a, const TileInfo &ti, int c0, uint16_t *lds_b)
+// MFMA expand for tiles of up to 64 rows.  B[0:r][512 columns] is staged in LDS
+// (rank-row k at a column rotation of 8 * ((k >> 2) & 3) halves, so the 4 k-groups of
+// a wavefront read different banks); per 16-row slice D^T[cols][rows] = B^T (s v)^T
+// runs with s*v split into fp16 hi + lo/2048 operands; the accumulator starts from y.
+template <bool PAGED, int RQ>
+__global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args a)
 {
+    constexpr int kStage = RQ * 16 * (kCols / 8) / kThreads;  // 16-byte loads per lane to stage B
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t *lds_b = reinterpret_cast<uint16_t *>(smem);
+    const Item it = work(a);
+    if (!it.ok) return;
+    const ProjDev &pd = a.p[it.p];
+    const TileHead th = tile_head<false>(a.ts, pd.w, it.tile);
+    if (!th.valid) return;
+    const int rank = slot_rank(pd.w, th.slot);
+    const float sc = pd.w.scale[th.slot];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int r = ti.rank;
-    const int rk = (r + 15) & ~15;  // ranks padded to the 16-wide k-step
-    // stage B[0:rk][c0:c0+512] (zeros past the rank or past d_out)
-    for (int o = tid; o < rk * (kCols / 8); o += kThreads) {
-        const int k = o >> 6, oc = (o & 63) * 8;
-        uint4 q = make_uint4(0, 0, 0, 0);
-        if (k < r && c0 + oc < a.w.d_out) {
-            const uint16_t *p = rank_row_ptr<PAGED, true>(a.w, ti.slot, k, c0 + oc);
-            if (p) q = load16(p);
-        }
-        const int pc = (oc + 8 * ((k >> 2) & 3)) & (kCols - 1);
-        *reinterpret_cast<uint4 *>(lds_b + k * kBStride + pc) = q;
-    }
-    __syncthreads();
-    const float sc = a.w.scale[ti.slot];
-    const int MT = (ti.nrows + 15) >> 4;
+    const int c0 = it.slice * kCols;
     const int cw = c0 + 128 * wave;  // this wavefront's 128 columns = 8 slices of 16
+    const int MT = (th.nrows + 15) >> 4;
+    const int rstage = PAGED ? ((rank + 15) & ~15) : ((pd.w.r_max + 15) & ~15);
     for (int mt = 0; mt < MT; ++mt) {
         const int rr = 16 * mt + li;
-        const int row = rr < ti.nrows ? row_of<PERROW>(a.ts, ti.pos0 + rr, a.n_rows) : -1;
-        f4_t acc_hi[8], acc_lo[8];
-        // accumulator starts from y: lane holds y[row][cw + 16 nt + 4 lg + e]
+        const int row = rr < th.nrows ? row_of<false>(a.ts, th.pos0 + rr, a.n_rows) : -1;
+        // y (accumulator start) and v for this slice: lane holds y[row][cw + 16 nt + 4 lg .. +3]
+        f4_t acc[8];
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
             const int col = cw + 16 * nt + 4 * lg;
-            acc_lo[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
-            if (row >= 0 && col < a.w.d_out) {
-                const uint2 yq = *reinterpret_cast<const uint2 *>(a.y + (int64_t)row * a.ldy + col);
-                acc_hi[nt] = f4_t{h2f((uint16_t)(yq.x & 0xffff)), h2f((uint16_t)(yq.x >> 16)),
-                                  h2f((uint16_t)(yq.y & 0xffff)), h2f((uint16_t)(yq.y >> 16))};
-            } else {
-                acc_hi[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
+            acc[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
+            if (row >= 0 && col < pd.w.d_out) {
+                const uint2 yq = *reinterpret_cast<const uint2 *>(pd.y + (int64_t)row * pd.ldy + col);
+                acc[nt] = f4_t{h2f((uint16_t)(yq.x & 0xffff)), h2f((uint16_t)(yq.x >> 16)),
+                               h2f((uint16_t)(yq.y & 0xffff)), h2f((uint16_t)(yq.y >> 16))};
             }
         }
-        for (int kb = 0; kb < rk; kb += 16) {
-            // B operand of the MFMA: (s v)^T, lane holds ranks kb + 4 lg .. +3 of its row
-            const int j = kb + 4 * lg;
-            float4 vq = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (row >= 0 && j < r) vq = *reinterpret_cast<const float4 *>(a.v + (int64_t)row * a.ldv + j);
-            const float sv[4] = {sc * vq.x, sc * vq.y, sc * vq.z, sc * vq.w};
+        float4 vq[RQ];
+#pragma unroll
+        for (int kq = 0; kq < RQ; ++kq) {
+            const int j = 16 * kq + 4 * lg;
+            vq[kq] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (row >= 0 && j < pd.w.r_max) vq[kq] = *reinterpret_cast<const float4 *>(pd.v + (int64_t)row * pd.ldv + j);
+        }
+        if (mt == 0) {
+            // stage B while the y and v loads are in flight: all loads first, then LDS;
+            // rows past the rank become 0, rows past r_max (dense) are not read
+            uint4 q[kStage];
+#pragma unroll
+            for (int i = 0; i < kStage; ++i) {
+                const int o = tid + i * kThreads, k = o >> 6, oc = (o & 63) * 8;
+                q[i] = make_uint4(0, 0, 0, 0);
+                if (k < rstage && c0 + oc < pd.w.d_out && k < (PAGED ? rank : pd.w.r_max)) {
+                    const uint16_t *p = rank_row_ptr<PAGED, true>(pd.w, th.slot, k, c0 + oc);
+                    if (p) q[i] = load16(p);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kStage; ++i) {
+                const int o = tid + i * kThreads, k = o >> 6, oc = (o & 63) * 8;
+                if (k >= rstage) continue;
+                const int pc = (oc + 8 * ((k >> 2) & 3)) & (kCols - 1);
+                *reinterpret_cast<uint4 *>(lds_b + k * kBStride + pc) = k < rank ? q[i] : make_uint4(0, 0, 0, 0);
+            }
+            __syncthreads();
+            if (rank <= 0) return;
+        }
+#pragma unroll
+        for (int kq = 0; kq < RQ; ++kq) {
+            if (16 * kq >= rank) break;
+            const int j = 16 * kq + 4 * lg;
+            const float sv[4] = {vq[kq].x, vq[kq].y, vq[kq].z, vq[kq].w};
             h4_t vhi, vlo;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float m = (j + e < r) ? sv[e] : 0.f;
+                const float m = (j + e < rank) ? sc * sv[e] : 0.f;
                 const _Float16 h = (_Float16)m;
                 vhi[e] = h;
                 vlo[e] = (_Float16)((m - (float)h) * 2048.f);
@@ -479,47 +544,34 @@ __device__ void expand_mfma(const ExpandArgs &a, const TileInfo &ti, int c0, uin
                     const int pc = (lc + 8 * ((k >> 2) & 3)) & (kCols - 1);
                     bop[e] = __builtin_bit_cast(_Float16, lds_b[k * kBStride + pc]);
                 }
-                acc_hi[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(bop, vhi, acc_hi[nt], 0, 0, 0);
-                acc_lo[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(bop, vlo, acc_lo[nt], 0, 0, 0);
+                f4_t lo = f4_t{0.f, 0.f, 0.f, 0.f};
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(bop, vhi, acc[nt], 0, 0, 0);
+                lo = __builtin_amdgcn_mfma_f32_16x16x16f16(bop, vlo, lo, 0, 0, 0);
+                acc[nt] += lo * (1.f / 2048.f);
             }
         }
         if (row < 0) continue;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
             const int col = cw + 16 * nt + 4 * lg;
-            if (col >= a.w.d_out) continue;
+            if (col >= pd.w.d_out) continue;
             uint16_t o[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = f2h(acc_hi[nt][e] + acc_lo[nt][e] * (1.f / 2048.f));
-            *reinterpret_cast<uint2 *>(a.y + (int64_t)row * a.ldy + col) =
+            for (int e = 0; e < 4; ++e) o[e] = f2h(acc[nt][e]);
+            *reinterpret_cast<uint2 *>(pd.y + (int64_t)row * pd.ldy + col) =
                 make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
         }
     }
-}
-
-template <bool PAGED, bool PERROW>
-__global__ __launch_bounds__(kThreads) void lora_expand_kernel(ExpandArgs a)
-{
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int wi = work_item(blockIdx.x, a.grid);
-    const int tile = wi / a.n_cchunks;
-    if (tile >= a.n_tiles) return;
-    const int cch = wi - tile * a.n_cchunks;
-    const TileInfo ti = load_tile<PERROW>(a.ts, a.w, tile);
-    if (ti.rank <= 0) return;
-    if (!PERROW && a.mfma && ti.nrows >= kMfmaMinRows)
-        expand_mfma<PAGED, PERROW>(a, ti, cch * kCols, reinterpret_cast<uint16_t *>(smem));
-    else
-        expand_valu<PAGED, PERROW>(a, ti, cch * kCols, reinterpret_cast<float *>(smem));
 }
 
 // ------------------------------------------------------------------------ launchers
 // Event pair attached to this thread's next kernel launch (lora_set_launch_events).
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 
-template <typename Kernel, typename Args>
-void launch(Kernel kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, const Args &a)
+template <typename Kernel>
+void launch(Kernel kernel, dim3 grid, int threads, size_t lds, hipStream_t s, const Args &a)
 {
+    const dim3 block(threads);
     if (t_ev_start || t_ev_stop) {
         hipEvent_t e0 = t_ev_start, e1 = t_ev_stop;
         t_ev_start = t_ev_stop = nullptr;
@@ -578,78 +630,140 @@ int check_segments(const lora_segments *seg)
     return LORA_OK;
 }
 
+// Checks the projection list shared by shrink and expand; fills the per-projection
+// parts of `a` that do not depend on the kernel.
+int check_projs(int32_t n_proj, const lora_proj *proj, bool expand, Args &a, bool &paged)
+{
+    if (n_proj < 1 || n_proj > LORA_MAX_PROJ)
+        return fail(LORA_E_SHAPE, "n_proj = %d outside 1..%d", n_proj, LORA_MAX_PROJ);
+    if (!proj) return fail(LORA_E_NULL, "projection list is NULL");
+    for (int32_t p = 0; p < n_proj; ++p) {
+        const lora_weights *w = proj[p].w;
+        int st = check_weights_desc(w);
+        if (st) return st;
+        if (p > 0 && w->layout != proj[0].w->layout)
+            return fail(LORA_E_UNSUPPORTED, "projections of one launch must share the weight layout");
+        if ((st = check_rows_arg(proj[p].v, proj[p].ldv, w->r_max, 4, "v"))) return st;
+        if (expand && (st = check_rows_arg(proj[p].y, proj[p].ldy, w->d_out, 8, "y"))) return st;
+        a.p[p].w = to_dev(w);
+        a.p[p].v = proj[p].v;
+        a.p[p].ldv = proj[p].ldv;
+        a.p[p].y = static_cast<uint16_t *>(proj[p].y);
+        a.p[p].ldy = proj[p].ldy;
+    }
+    paged = proj[0].w->layout == LORA_LAYOUT_PAGED;
+    a.n_proj = n_proj;
+    return LORA_OK;
+}
+
 inline int32_t pad8(int64_t g) { return (int32_t)((g + 7) & ~int64_t(7)); }
 
-template <bool PERROW>
-int shrink_impl(void *stream, float *v, int64_t ldv, const void *x, int64_t ldx, int32_t n_rows,
-                const lora_weights *w, TileSrc ts, int32_t n_tiles, int32_t max_rows)
+int finish_layout(Args &a, int32_t n_tiles)
 {
-    int st = check_weights_desc(w);
+    int32_t off = 0;
+    for (int32_t p = 0; p < LORA_MAX_PROJ; ++p) {
+        a.off[p] = off;
+        if (p < a.n_proj) off += a.p[p].slices;
+    }
+    a.per_tile = off;
+    const int64_t items = (int64_t)n_tiles * off;
+    if (items > (int64_t)1 << 30) return fail(LORA_E_SHAPE, "launch of %lld work items is too large", (long long)items);
+    a.grid = pad8(items);
+    return LORA_OK;
+}
+
+template <bool PERROW>
+int shrink_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSrc ts, int32_t n_tiles,
+                int32_t max_rows, int32_t n_proj, const lora_proj *proj)
+{
+    Args a{};
+    bool paged = false;
+    int st = check_projs(n_proj, proj, false, a, paged);
     if (st) return st;
+    for (int32_t p = 1; p < n_proj; ++p)
+        if (proj[p].w->d_in != proj[0].w->d_in)
+            return fail(LORA_E_SHAPE, "projections of one shrink launch share x: d_in %d != %d", proj[p].w->d_in,
+                        proj[0].w->d_in);
     if (n_rows < 0) return fail(LORA_E_SHAPE, "n_rows = %d", n_rows);
     if (n_rows == 0 || n_tiles == 0) return LORA_OK;
-    if ((st = check_rows_arg(v, ldv, w->r_max, 4, "v"))) return st;
-    if ((st = check_rows_arg(x, ldx, w->d_in, 8, "x"))) return st;
-    const int32_t jw = plan_shrink_jw(n_tiles, w->r_max, max_rows);
-    ShrinkArgs a;
-    a.v = v;
-    a.ldv = ldv;
+    if ((st = check_rows_arg(x, ldx, proj[0].w->d_in, 8, "x"))) return st;
+    int32_t r_max = 0;
+    for (int32_t p = 0; p < n_proj; ++p) r_max = std::max(r_max, proj[p].w->r_max);
+    const bool mfma = !PERROW && max_rows >= kMfmaMinRows;
+    a.jw = mfma ? 16 : plan_shrink_jw(n_tiles * n_proj, r_max);
+    for (int32_t p = 0; p < n_proj; ++p) a.p[p].slices = (proj[p].w->r_max + a.jw - 1) / a.jw;
+    if ((st = finish_layout(a, n_tiles))) return st;
     a.x = static_cast<const uint16_t *>(x);
     a.ldx = ldx;
     a.n_rows = n_rows;
     a.n_tiles = n_tiles;
     a.ts = ts;
-    a.w = to_dev(w);
-    a.jw = jw;
-    a.n_jg = (w->r_max + jw - 1) / jw;
-    a.grid = pad8((int64_t)n_tiles * a.n_jg);
-    const dim3 grid((unsigned)a.grid), block(kThreads);
+    const dim3 grid((unsigned)a.grid);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool paged = w->layout == LORA_LAYOUT_PAGED;
-    if (jw == 1) {
-        if (paged) launch(lora_shrink_kernel<true, PERROW, 1>, grid, block, 0, s, a);
-        else launch(lora_shrink_kernel<false, PERROW, 1>, grid, block, 0, s, a);
-    } else if (jw == 2) {
-        if (paged) launch(lora_shrink_kernel<true, PERROW, 2>, grid, block, 0, s, a);
-        else launch(lora_shrink_kernel<false, PERROW, 2>, grid, block, 0, s, a);
+    constexpr int NR = PERROW ? 1 : kRowsPerPass;
+    if (mfma) {
+        const int slices = (max_rows + 15) / 16;
+        if (slices <= 1) {
+            if (paged) launch(lora_shrink_mfma_kernel<true, 1>, grid, kMfmaShrinkThreads, 0, s, a);
+            else launch(lora_shrink_mfma_kernel<false, 1>, grid, kMfmaShrinkThreads, 0, s, a);
+        } else if (slices == 2) {
+            if (paged) launch(lora_shrink_mfma_kernel<true, 2>, grid, kMfmaShrinkThreads, 0, s, a);
+            else launch(lora_shrink_mfma_kernel<false, 2>, grid, kMfmaShrinkThreads, 0, s, a);
+        } else {
+            if (paged) launch(lora_shrink_mfma_kernel<true, 4>, grid, kMfmaShrinkThreads, 0, s, a);
+            else launch(lora_shrink_mfma_kernel<false, 4>, grid, kMfmaShrinkThreads, 0, s, a);
+        }
+    } else if (a.jw == 1) {
+        if (paged) launch(lora_shrink_valu_kernel<true, PERROW, 1, NR>, grid, kThreads, 0, s, a);
+        else launch(lora_shrink_valu_kernel<false, PERROW, 1, NR>, grid, kThreads, 0, s, a);
+    } else if (a.jw == 2) {
+        if (paged) launch(lora_shrink_valu_kernel<true, PERROW, 2, NR>, grid, kThreads, 0, s, a);
+        else launch(lora_shrink_valu_kernel<false, PERROW, 2, NR>, grid, kThreads, 0, s, a);
     } else {
-        if (paged) launch(lora_shrink_kernel<true, PERROW, 4>, grid, block, 0, s, a);
-        else launch(lora_shrink_kernel<false, PERROW, 4>, grid, block, 0, s, a);
+        if (paged) launch(lora_shrink_valu_kernel<true, PERROW, 4, NR>, grid, kThreads, 0, s, a);
+        else launch(lora_shrink_valu_kernel<false, PERROW, 4, NR>, grid, kThreads, 0, s, a);
     }
     return launch_status("shrink");
 }
 
 template <bool PERROW>
-int expand_impl(void *stream, void *y, int64_t ldy, const float *v, int64_t ldv, int32_t n_rows,
-                const lora_weights *w, TileSrc ts, int32_t n_tiles, int32_t max_rows)
+int expand_impl(void *stream, int32_t n_rows, TileSrc ts, int32_t n_tiles, int32_t max_rows, int32_t n_proj,
+                const lora_proj *proj)
 {
-    int st = check_weights_desc(w);
+    Args a{};
+    bool paged = false;
+    int st = check_projs(n_proj, proj, true, a, paged);
     if (st) return st;
     if (n_rows < 0) return fail(LORA_E_SHAPE, "n_rows = %d", n_rows);
     if (n_rows == 0 || n_tiles == 0) return LORA_OK;
-    if ((st = check_rows_arg(y, ldy, w->d_out, 8, "y"))) return st;
-    if ((st = check_rows_arg(v, ldv, w->r_max, 4, "v"))) return st;
-    ExpandArgs a;
-    a.y = static_cast<uint16_t *>(y);
-    a.ldy = ldy;
-    a.v = v;
-    a.ldv = ldv;
+    int32_t r_max = 0;
+    for (int32_t p = 0; p < n_proj; ++p) {
+        a.p[p].slices = (proj[p].w->d_out + kCols - 1) / kCols;
+        r_max = std::max(r_max, proj[p].w->r_max);
+    }
+    if ((st = finish_layout(a, n_tiles))) return st;
     a.n_rows = n_rows;
     a.n_tiles = n_tiles;
-    a.n_cchunks = (w->d_out + kCols - 1) / kCols;
-    a.grid = pad8((int64_t)n_tiles * a.n_cchunks);
-    a.mfma = (!PERROW && max_rows >= kMfmaMinRows) ? 1 : 0;
+    const bool mfma = !PERROW && max_rows >= kMfmaMinRows;
     a.ts = ts;
-    a.w = to_dev(w);
-    const size_t lds_valu = (size_t)kWaves * kRowsPerPass * 8 * 64 * sizeof(float);
-    const size_t lds_mfma = a.mfma ? (size_t)((w->r_max + 15) & ~15) * kBStride * sizeof(uint16_t) : 0;
-    const size_t lds = std::max(lds_valu, lds_mfma);
-    const dim3 grid((unsigned)a.grid), block(kThreads);
+    const dim3 grid((unsigned)a.grid);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (w->layout == LORA_LAYOUT_PAGED)
-        launch(lora_expand_kernel<true, PERROW>, grid, block, lds, s, a);
-    else
-        launch(lora_expand_kernel<false, PERROW>, grid, block, lds, s, a);
+    if (mfma) {
+        const int rq = (r_max + 15) / 16;
+        const size_t lds = (size_t)rq * 16 * kBStride * sizeof(uint16_t);
+#define LORA_EXPAND_MFMA(RQ)                                                        \
+    (paged ? launch(lora_expand_mfma_kernel<true, RQ>, grid, kThreads, lds, s, a)   \
+           : launch(lora_expand_mfma_kernel<false, RQ>, grid, kThreads, lds, s, a))
+        if (rq == 1) LORA_EXPAND_MFMA(1);
+        else if (rq == 2) LORA_EXPAND_MFMA(2);
+        else if (rq == 3) LORA_EXPAND_MFMA(3);
+        else LORA_EXPAND_MFMA(4);
+#undef LORA_EXPAND_MFMA
+    } else {
+        constexpr int NR = PERROW ? 1 : kRowsPerPass;
+        if (paged) launch(lora_expand_valu_kernel<true, PERROW, NR>, grid, kThreads, 0, s, a);
+        else launch(lora_expand_valu_kernel<false, PERROW, NR>, grid, kThreads, 0, s, a);
+    }
     return launch_status("expand");
 }
 
@@ -671,14 +785,24 @@ TileSrc row_src(const int32_t *idx)
 
 inline int32_t seg_max_rows(const lora_segments *seg) { return seg->max_rows > 0 ? seg->max_rows : LORA_MAX_TILE_ROWS; }
 
+lora_proj one_proj(const lora_weights *w, float *v, int64_t ldv, void *y, int64_t ldy)
+{
+    lora_proj p;
+    p.w = w;
+    p.v = v;
+    p.ldv = ldv;
+    p.y = y;
+    p.ldy = ldy;
+    return p;
+}
+
 }  // namespace
 
-int32_t plan_shrink_jw(int32_t n_tiles, int32_t r_max, int32_t max_rows)
+int32_t plan_shrink_jw(int32_t work_tiles, int32_t r_max)
 {
-    if (max_rows >= kMfmaMinRows) return 16;
-    // Smallest rank-row group that keeps the grid near kTargetGroups workgroups.
+    // The smallest rank-row group that keeps the grid near kTargetGroups workgroups.
     int32_t jw = 1;
-    while (jw < 4 && (int64_t)n_tiles * ((r_max + jw - 1) / jw) > kTargetGroups) jw *= 2;
+    while (jw < 4 && (int64_t)work_tiles * ((r_max + jw - 1) / jw) > kTargetGroups) jw *= 2;
     return jw;
 }
 
@@ -696,38 +820,65 @@ int lora_set_launch_events(void *start_event, void *stop_event)
     return LORA_OK;
 }
 
-int lora_sgmv_shrink(void *stream, float *v, int64_t ldv, const void *x, int64_t ldx, int32_t n_rows,
-                     const lora_weights *w, const lora_segments *seg)
+int lora_sgmv_shrink_multi(void *stream, const void *x, int64_t ldx, int32_t n_rows, const lora_segments *seg,
+                           int32_t n_proj, const lora_proj *proj)
 {
     clear_error();
     int st = check_segments(seg);
     if (st) return st;
-    return shrink_impl<false>(stream, v, ldv, x, ldx, n_rows, w, seg_src(seg), seg->n_tiles, seg_max_rows(seg));
+    return shrink_impl<false>(stream, x, ldx, n_rows, seg_src(seg), seg->n_tiles, seg_max_rows(seg), n_proj, proj);
+}
+
+int lora_sgmv_expand_multi(void *stream, int32_t n_rows, const lora_segments *seg, int32_t n_proj,
+                           const lora_proj *proj)
+{
+    clear_error();
+    int st = check_segments(seg);
+    if (st) return st;
+    return expand_impl<false>(stream, n_rows, seg_src(seg), seg->n_tiles, seg_max_rows(seg), n_proj, proj);
+}
+
+int lora_bgmv_shrink_multi(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows,
+                           int32_t n_proj, const lora_proj *proj)
+{
+    clear_error();
+    if (n_rows > 0 && !idx) return fail(LORA_E_NULL, "idx is NULL");
+    return shrink_impl<true>(stream, x, ldx, n_rows, row_src(idx), n_rows, 1, n_proj, proj);
+}
+
+int lora_bgmv_expand_multi(void *stream, const int32_t *idx, int32_t n_rows, int32_t n_proj, const lora_proj *proj)
+{
+    clear_error();
+    if (n_rows > 0 && !idx) return fail(LORA_E_NULL, "idx is NULL");
+    return expand_impl<true>(stream, n_rows, row_src(idx), n_rows, 1, n_proj, proj);
+}
+
+int lora_sgmv_shrink(void *stream, float *v, int64_t ldv, const void *x, int64_t ldx, int32_t n_rows,
+                     const lora_weights *w, const lora_segments *seg)
+{
+    const lora_proj p = one_proj(w, v, ldv, nullptr, 0);
+    return lora_sgmv_shrink_multi(stream, x, ldx, n_rows, seg, 1, &p);
 }
 
 int lora_sgmv_expand(void *stream, void *y, int64_t ldy, const float *v, int64_t ldv, int32_t n_rows,
                      const lora_weights *w, const lora_segments *seg)
 {
-    clear_error();
-    int st = check_segments(seg);
-    if (st) return st;
-    return expand_impl<false>(stream, y, ldy, v, ldv, n_rows, w, seg_src(seg), seg->n_tiles, seg_max_rows(seg));
+    const lora_proj p = one_proj(w, const_cast<float *>(v), ldv, y, ldy);
+    return lora_sgmv_expand_multi(stream, n_rows, seg, 1, &p);
 }
 
 int lora_bgmv_shrink(void *stream, float *v, int64_t ldv, const void *x, int64_t ldx, const int32_t *idx,
                      int32_t n_rows, const lora_weights *w)
 {
-    clear_error();
-    if (n_rows > 0 && !idx) return fail(LORA_E_NULL, "idx is NULL");
-    return shrink_impl<true>(stream, v, ldv, x, ldx, n_rows, w, row_src(idx), n_rows, 1);
+    const lora_proj p = one_proj(w, v, ldv, nullptr, 0);
+    return lora_bgmv_shrink_multi(stream, x, ldx, idx, n_rows, 1, &p);
 }
 
 int lora_bgmv_expand(void *stream, void *y, int64_t ldy, const float *v, int64_t ldv, const int32_t *idx,
                      int32_t n_rows, const lora_weights *w)
 {
-    clear_error();
-    if (n_rows > 0 && !idx) return fail(LORA_E_NULL, "idx is NULL");
-    return expand_impl<true>(stream, y, ldy, v, ldv, n_rows, w, row_src(idx), n_rows, 1);
+    const lora_proj p = one_proj(w, const_cast<float *>(v), ldv, y, ldy);
+    return lora_bgmv_expand_multi(stream, idx, n_rows, 1, &p);
 }
 
 int lora_bgmv(void *stream, void *y, int64_t ldy, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows,
@@ -742,9 +893,10 @@ int lora_bgmv(void *stream, void *y, int64_t ldy, const void *x, int64_t ldx, co
     if (n_rows == 0) return LORA_OK;
     if ((st = check_rows_arg(y, ldy, w->d_out, 8, "y"))) return st;
     if ((st = check_rows_arg(v, ldv, w->r_max, 4, "v"))) return st;
-    st = shrink_impl<true>(stream, v, ldv, x, ldx, n_rows, w, row_src(idx), n_rows, 1);
+    const lora_proj p = one_proj(w, v, ldv, y, ldy);
+    st = shrink_impl<true>(stream, x, ldx, n_rows, row_src(idx), n_rows, 1, 1, &p);
     if (st) return st;
-    return expand_impl<true>(stream, y, ldy, v, ldv, n_rows, w, row_src(idx), n_rows, 1);
+    return expand_impl<true>(stream, n_rows, row_src(idx), n_rows, 1, 1, &p);
 }
 
 }  // extern "C"

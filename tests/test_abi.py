@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 14 and set(names) == set(B.EXPORTS)
+    assert len(names) == 18 and set(names) == set(B.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", build_mod.LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (lora_\w+)", out))
@@ -254,3 +254,26 @@ def test_validate_segments_host():
     over[0, 2] = 65
     s.tiles = over.ctypes.data
     assert B.lib().lora_validate_segments_host(ctypes.byref(s), 6, 3) == B.LORA_E_SHAPE
+
+
+def test_multi_projection_errors():
+    L = B.lib()
+    c1, c2 = _desc(), _desc(d_in=2048)
+    arr = (B.CProj * 5)()
+    for i in range(5):
+        arr[i].w, arr[i].v, arr[i].ldv, arr[i].y, arr[i].ldy = ctypes.addressof(c1), FAKE, 16, FAKE, 1024
+    assert L.lora_bgmv_shrink_multi(None, FAKE, 1024, FAKE, 8, 0, arr) == B.LORA_E_SHAPE
+    assert L.lora_bgmv_shrink_multi(None, FAKE, 1024, FAKE, 8, 5, arr) == B.LORA_E_SHAPE
+    assert L.lora_bgmv_shrink_multi(None, FAKE, 1024, FAKE, 8, 2, None) == B.LORA_E_NULL
+    arr[1].w = ctypes.addressof(c2)
+    assert L.lora_bgmv_shrink_multi(None, FAKE, 1024, FAKE, 8, 2, arr) == B.LORA_E_SHAPE     # d_in differs
+    assert "share x" in B.last_error()
+    c3 = _desc(layout=1, a_t=None, b=None, pool=FAKE, page_table=FAKE, a_pt_off=FAKE, b_pt_off=FAKE,
+               num_pages=10, pt_entries=10, page_elems=256)
+    arr[1].w = ctypes.addressof(c3)
+    assert L.lora_bgmv_expand_multi(None, FAKE, 8, 2, arr) == B.LORA_E_UNSUPPORTED         # mixed layouts
+    arr[1].w = ctypes.addressof(c1)
+    arr[1].ldy = 1000
+    assert L.lora_bgmv_expand_multi(None, FAKE, 8, 2, arr) == B.LORA_E_SHAPE
+    arr[1].ldy = 1024
+    assert L.lora_bgmv_expand_multi(None, FAKE, 0, 2, arr) == B.LORA_OK                     # no rows: no launch

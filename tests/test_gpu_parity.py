@@ -245,3 +245,94 @@ def test_tile_size_does_not_change_results_beyond_tolerance(max_tile_rows):
     dc = G.DeviceCase(x, y0, 64)
     y, v = G.run_sgmv(w, dc, seg_ptr=seg_ptr, seg_slot=seg_slot, max_tile_rows=max_tile_rows)
     G.check(dc, y, v, y_ref, v_ref, G.active_rows(idx, rank), f"tiles-{max_tile_rows}")
+
+
+@pytest.mark.parametrize("form", ["bgmv", "sgmv_rowmap", "sgmv_prefill"])
+def test_multi_projection_launch_matches_single_calls(form):
+    """q/k/v-like grouping (one x, three outputs): each projection bit-identical to its
+    single-projection call and within tolerance of the oracle."""
+    import torch
+    if form == "sgmv_prefill":
+        lens = [40, 3, 100, 17]
+        seg_ptr = wl.segments_from_lengths(lens)
+        seg_slot = np.array([1, 0, 3, 2], dtype=np.int32)
+        idx = np.repeat(seg_slot, lens).astype(np.int32)
+        n = len(idx)
+    else:
+        b = wl.batch_decode_mix("skewed")
+        idx, n = b.idx, b.n
+    d_in, outs, S = 2048, (2048, 512, 512), 16
+    rank = np.array([16, 8, 64, 32] * 4, dtype=np.int32)
+    scale = wl.scale_for_rank(rank)
+    x, _ = wl.activations(18, 0, n, d_in, 8)
+    stores, y0s, refs = [], [], []
+    for p, d_out in enumerate(outs):
+        store = wl.dense_store(18, 10 + p, S, d_in, d_out, rank, scale, r_max=64)
+        _, y0 = wl.activations(18, 10 + p, n, d_in, d_out)
+        stores.append(store)
+        y0s.append(y0)
+        refs.append(_oracle(store, x, y0, idx))
+    ws = [B.weights_from_store(st) for st in stores]
+    xd = torch.from_numpy(x).cuda()
+    idx_d = torch.from_numpy(idx).cuda()
+    if form == "bgmv":
+        segs = None
+    elif form == "sgmv_rowmap":
+        row_map, sp, ss, n_act = B.lora_build_segments(idx, S)
+        segs = B.segments_to_device(B.lora_build_tiles(sp, ss, 16), row_map, n_act)
+    else:
+        segs = B.segments_to_device(B.lora_build_tiles(seg_ptr, seg_slot, 16), None, n)
+    single, multi = [], []
+    for mode in ("single", "multi"):
+        vs = [torch.full((n, 64), float("nan"), dtype=torch.float32, device="cuda") for _ in outs]
+        ys = [torch.from_numpy(y0.copy()).cuda() for y0 in y0s]
+        items = list(zip(ws, vs, ys))
+        if mode == "single":
+            for w, v, y in items:
+                if segs is None:
+                    B.lora_bgmv_shrink(v, xd, idx_d, w)
+                    B.lora_bgmv_expand(y, v, idx_d, w)
+                else:
+                    B.lora_sgmv_shrink(v, xd, w, segs)
+                    B.lora_sgmv_expand(y, v, w, segs)
+        else:
+            if segs is None:
+                B.lora_bgmv_shrink_multi(xd, idx_d, items)
+                B.lora_bgmv_expand_multi(idx_d, items, n)
+            else:
+                B.lora_sgmv_shrink_multi(xd, segs, items)
+                B.lora_sgmv_expand_multi(segs, items, n)
+        torch.cuda.synchronize()
+        (single if mode == "single" else multi).extend((y.cpu().numpy(), v.cpu().numpy()) for _, v, y in items)
+    act = G.active_rows(idx, rank)
+    for p in range(len(outs)):
+        (ys_, vs_), (ym, vm) = single[p], multi[p]
+        assert np.array_equal(ys_.view(np.uint16), ym.view(np.uint16)), f"projection {p}: y differs"
+        assert np.array_equal(np.nan_to_num(vs_, nan=-1).view(np.uint32), np.nan_to_num(vm, nan=-1).view(np.uint32))
+        y_ref = refs[p][0]
+        err = np.abs(ym.astype(np.float64) - y_ref)
+        assert err.max() <= G.TOL_MAX_ABS
+        assert np.linalg.norm(ym.astype(np.float64) - y_ref) / np.linalg.norm(y_ref) <= G.TOL_REL_FRO
+        assert np.array_equal(ym[~act].view(np.uint16), y0s[p][~act].view(np.uint16))
+
+
+@pytest.mark.parametrize("layout", ["dense", "paged"])
+def test_mfma_paths_with_rank_not_multiple_of_16(layout):
+    """r_max = 20 with MFMA-sized tiles that use the last slot: the expand's LDS staging
+    pads ranks to 16 and must not read past the slot storage."""
+    lens = [30, 9, 50, 7]
+    seg_ptr = wl.segments_from_lengths(lens)
+    seg_slot = np.array([3, 0, 2, 1], dtype=np.int32)
+    idx = np.repeat(seg_slot, lens).astype(np.int32)
+    rank = np.array([5, 20, 17, 20], dtype=np.int32)
+    d_in, d_out = 1536, 2048
+    if layout == "dense":
+        store = wl.dense_store(19, 0, 4, d_in, d_out, rank, wl.scale_for_rank(rank), r_max=20)
+    else:
+        store = wl.paged_store(19, 0, 4, d_in, d_out, rank, wl.scale_for_rank(rank), 512, spare_pages=4)
+    x, y0 = wl.activations(19, 0, len(idx), d_in, d_out)
+    y_ref, v_ref = _oracle(store, x, y0, idx)
+    w = B.weights_from_store(store)
+    dc = G.DeviceCase(x, y0, 20)
+    y, v = G.run_sgmv(w, dc, seg_ptr=seg_ptr, seg_slot=seg_slot, max_tile_rows=16)
+    G.check(dc, y, v, y_ref, v_ref, G.active_rows(idx, rank), f"rmax20-{layout}")
