@@ -72,7 +72,7 @@ class Op:
 INPUT_GROUPS = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
 
 
-def make_ops(spec, layers, device):
+def make_ops(spec, layers, device, tile_rows=None):
     """Per layer: one x per input group, one y, v and weight descriptor per projection."""
     import torch
     from segmented_gather_matmul_amd import binding as B
@@ -84,10 +84,10 @@ def make_ops(spec, layers, device):
     if spec["form"].startswith("sgmv"):
         if spec["form"] == "sgmv":
             row_map, seg_ptr, seg_slot, n_act = B.lora_build_segments(b.idx, S)
-            tiles = B.lora_build_tiles(seg_ptr, seg_slot, 16)
+            tiles = B.lora_build_tiles(seg_ptr, seg_slot, tile_rows)
             segs = B.segments_to_device(tiles, row_map, n_act, device)
         else:
-            tiles = B.lora_build_tiles(b.seg_ptr, b.seg_slot, 16)
+            tiles = B.lora_build_tiles(b.seg_ptr, b.seg_slot, tile_rows)
             segs = B.segments_to_device(tiles, None, n, device)
     rank_d = torch.from_numpy(rank.astype(np.int32)).to(device)
     scale_d = torch.from_numpy(spec["scale"].astype(np.float32)).to(device)
@@ -325,7 +325,23 @@ def main():
     ap.add_argument("--no-group", action="store_true", help="one launch per projection (14 per layer)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tile-rows", type=int, default=None,
+                    help="tile height for the segment form (default: lora_pick_tile_rows)")
+    ap.add_argument("--form", choices=["bgmv", "sgmv"], default=None,
+                    help="per-row slots (bgmv) or rows grouped by adapter (sgmv); default: the workload's own")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (byte-counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 2, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(a batch shards across GPUs by rows without any exchange).", file=sys.stderr)
@@ -340,9 +356,13 @@ def main():
     device = "cuda"
     grouped = not args.no_group
     spec = workload_spec(args.workload)
+    if args.form and args.form != spec["form"].split("_")[0]:
+        if spec["form"] == "sgmv_contiguous":
+            raise SystemExit("the prefill workload is given as contiguous segments")
+        spec["form"] = args.form
     layers = args.layers or spec["layers"]
     log(f"[bench] workload={args.workload} layers={layers} grouped={grouped} building inputs")
-    groups = make_ops(spec, layers, device)
+    groups = make_ops(spec, layers, device, args.tile_rows)
     torch.cuda.synchronize()
     counts = [unit_counts(spec, ops) for ops in groups]
     step_bytes = sum(c["shrink_bytes"] + c["expand_bytes"] for c in counts)
@@ -428,7 +448,7 @@ def main():
                    "projections": list(spec["shapes"]), "batch_rows": spec["batch"].n,
                    "num_slots": spec["num_slots"], "rank": sorted(set(int(r) for r in spec["rank"])),
                    "popularity": spec["popularity"], "form": spec["form"], "layout": spec["layout"],
-                   "grouped": grouped, "launches_per_step": n_launch, "graph": not args.no_graph,
+                   "grouped": grouped, "launches_per_step": n_launch, "tile_rows": args.tile_rows, "graph": not args.no_graph,
                    "parallelism": "none"},
         "us_per_layer": round(1e3 * ms / layers, 3),
         "tflops": round(step_flops / (ms * 1e-3) / 1e12, 4),

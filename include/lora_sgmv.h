@@ -160,6 +160,14 @@ int lora_build_segments(const int32_t *idx, int32_t n, int32_t num_slots, int32_
 int32_t lora_tiles_bound(int32_t n_pos, int32_t n_seg, int32_t max_tile_rows);
 
 /*
+ * Tile height suited to a batch: 16 (the MFMA kernels' slice) when some segment
+ * has at least 128 rows, else 4 (the VALU kernels spread short segments widest).
+ * seg_ptr: host [n_seg + 1].  Any value in 1..LORA_MAX_TILE_ROWS gives the same
+ * results within the stated tolerance; this only picks the faster launch shape.
+ */
+int32_t lora_pick_tile_rows(const int32_t *seg_ptr, int32_t n_seg);
+
+/*
  * Cut segments into the flat tile work-list the SGMV kernels run on.  Segment g
  * (positions seg_ptr[g] .. seg_ptr[g+1]-1, slot seg_slot[g]) becomes
  * ceil(len / max_tile_rows) tiles of near-equal size; empty segments and segments

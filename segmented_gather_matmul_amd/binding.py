@@ -31,7 +31,7 @@ EXPORTS = ["lora_build_segments", "lora_tiles_bound", "lora_build_tiles", "lora_
            "lora_validate_segments_host", "lora_sgmv_shrink", "lora_sgmv_expand",
            "lora_bgmv_shrink", "lora_bgmv_expand", "lora_bgmv", "lora_last_error", "lora_status_str",
            "lora_abi_version", "lora_set_launch_events", "lora_sgmv_shrink_multi", "lora_sgmv_expand_multi",
-           "lora_bgmv_shrink_multi", "lora_bgmv_expand_multi"]
+           "lora_bgmv_shrink_multi", "lora_bgmv_expand_multi", "lora_pick_tile_rows"]
 MAX_PROJ = 4
 
 
@@ -91,12 +91,14 @@ def lib() -> ctypes.CDLL:
             "lora_sgmv_expand_multi": [P, I32, P, I32, P],
             "lora_bgmv_shrink_multi": [P, P, I64, P, I32, I32, P],
             "lora_bgmv_expand_multi": [P, P, I32, I32, P],
+            "lora_pick_tile_rows": [P, I32],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
         L.lora_tiles_bound.restype = ctypes.c_int32
+        L.lora_pick_tile_rows.restype = ctypes.c_int32
         L.lora_last_error.restype = ctypes.c_char_p
         L.lora_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -212,11 +214,19 @@ def lora_tiles_bound(n_pos, n_seg, max_tile_rows=MAX_TILE_ROWS):
     return int(lib().lora_tiles_bound(int(n_pos), int(n_seg), int(max_tile_rows)))
 
 
-def lora_build_tiles(seg_ptr, seg_slot, max_tile_rows=MAX_TILE_ROWS):
-    """Host: tile work-list as int32 [n_tiles, 4] = (slot, pos0, nrows, seg)."""
+def lora_pick_tile_rows(seg_ptr):
+    seg_ptr = np.ascontiguousarray(seg_ptr, dtype=np.int32)
+    return int(lib().lora_pick_tile_rows(_ptr(seg_ptr), len(seg_ptr) - 1))
+
+
+def lora_build_tiles(seg_ptr, seg_slot, max_tile_rows=None):
+    """Host: tile work-list as int32 [n_tiles, 4] = (slot, pos0, nrows, seg).
+    max_tile_rows None: the height lora_pick_tile_rows suggests for this batch."""
     seg_ptr = np.ascontiguousarray(seg_ptr, dtype=np.int32)
     seg_slot = np.ascontiguousarray(seg_slot, dtype=np.int32)
     n_seg = len(seg_slot)
+    if max_tile_rows is None:
+        max_tile_rows = lora_pick_tile_rows(seg_ptr)
     n_pos = int(seg_ptr[-1] - seg_ptr[0]) if n_seg else 0
     cap = max(lora_tiles_bound(n_pos, n_seg, max_tile_rows), 1)
     tiles = np.zeros((cap, 4), dtype=np.int32)

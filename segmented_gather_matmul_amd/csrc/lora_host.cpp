@@ -119,6 +119,15 @@ int32_t lora_tiles_bound(int32_t n_pos, int32_t n_seg, int32_t max_tile_rows)
     return (n_pos + max_tile_rows - 1) / max_tile_rows + n_seg;
 }
 
+int32_t lora_pick_tile_rows(const int32_t *seg_ptr, int32_t n_seg)
+{
+    int32_t longest = 0;
+    for (int32_t g = 0; seg_ptr && g < n_seg; ++g) longest = std::max(longest, seg_ptr[g + 1] - seg_ptr[g]);
+    // Long segments (prefill) feed the MFMA kernels 16-row tiles; short ones (decode
+    // groups) run on the VALU kernels, where 4-row tiles spread the work widest.
+    return longest >= kLongSegment ? 16 : 4;
+}
+
 int lora_build_tiles(const int32_t *seg_ptr, const int32_t *seg_slot, int32_t n_seg,
                      int32_t max_tile_rows, lora_tile *tiles, int32_t tiles_cap, int32_t *n_tiles)
 {

@@ -24,5 +24,6 @@ int32_t plan_shrink_jw(int32_t work_tiles, int32_t r_max);
 
 constexpr int32_t kMfmaMinRows = 8;      // launches with a tile this tall run the MFMA kernels
 constexpr int32_t kTargetGroups = 1024;  // shrink workgroups to aim for
+constexpr int32_t kLongSegment = 128;    // segments this long get 16-row (MFMA) tiles
 
 }  // namespace lora

@@ -113,23 +113,69 @@ __device__ inline int row_of(const TileSrc &ts, int pos, int n_rows)
     return (row >= 0 && row < n_rows) ? row : -1;
 }
 
-// Address of elements e .. e+7 of rank-row j of A^T[s] (IS_B false) or B[s];
-// NULL when a page-table entry or page id is out of range.
-template <bool PAGED, bool IS_B>
-__device__ inline const uint16_t *rank_row_ptr(const WeightsDev &w, int s, int j, int e)
+// Rank-row j of A^T[s] (IS_B false) or B[s] in the dense layout.
+template <bool IS_B>
+__device__ inline const uint16_t *dense_row(const WeightsDev &w, int s, int j)
 {
     const int d = IS_B ? w.d_out : w.d_in;
-    if (!PAGED) {
-        const uint16_t *base = IS_B ? w.b : w.a_t;
-        return base + ((int64_t)s * w.r_max + j) * d + e;
-    } else {
-        const int P = w.page_elems;
-        const int64_t off = (IS_B ? w.b_pt_off[s] : w.a_pt_off[s]) + (int64_t)j * (d / P) + e / P;
-        if (off < 0 || off >= w.pt_entries) return nullptr;
-        const int64_t page = w.page_table[off];
-        if (page < 0 || page >= w.num_pages) return nullptr;
-        return w.pool + page * P + (e % P);
-    }
+    return (IS_B ? w.b : w.a_t) + ((int64_t)s * w.r_max + j) * d;
+}
+
+// Paged layout: first entry of slot s's A^T (IS_B false) or B rank-rows in the page table.
+template <bool IS_B>
+__device__ inline int64_t pt_base(const WeightsDev &w, int s)
+{
+    return IS_B ? w.b_pt_off[s] : w.a_pt_off[s];
+}
+
+// Page-table entry for page-index q (element q*P) of rank-row j, unchecked (-1 when
+// the entry lies outside the table).  page_ok() checks the id once it has arrived, so
+// a wavefront can have all its page-table loads in flight before it uses any.
+template <bool IS_B>
+__device__ inline int page_entry(const WeightsDev &w, int64_t ptb, int j, int q)
+{
+    const int d = IS_B ? w.d_out : w.d_in;
+    const int64_t off = ptb + (int64_t)j * (d / w.page_elems) + q;
+    return (off >= 0 && off < w.pt_entries) ? w.page_table[off] : -1;
+}
+
+__device__ inline int page_ok(const WeightsDev &w, int pg) { return (pg >= 0 && pg < w.num_pages) ? pg : -1; }
+
+template <bool IS_B>
+__device__ inline int page_id(const WeightsDev &w, int64_t ptb, int j, int q)
+{
+    return page_ok(w, page_entry<IS_B>(w, ptb, j, q));
+}
+
+__device__ inline const uint16_t *page_ptr(const WeightsDev &w, int pg, int within)
+{
+    return w.pool + (int64_t)pg * w.page_elems + within;
+}
+
+constexpr int kPageCache = 4096;  // page ids a shrink workgroup keeps in LDS
+
+// Page ids of A^T rank-rows [j0, j1) of slot s, all pages, into LDS (one round trip
+// for the whole workgroup).  Returns false, and caches nothing, when they do not fit.
+template <int NTHREADS>
+__device__ inline bool cache_a_pages(const WeightsDev &w, int s, int j0, int j1, int *cache)
+{
+    const int npg = w.d_in / w.page_elems;
+    const int n = (j1 - j0) * npg;
+    if (n > kPageCache) return false;
+    const int64_t ptb = pt_base<false>(w, s);
+    for (int t = threadIdx.x; t < n; t += NTHREADS) cache[t] = page_id<false>(w, ptb, j0 + t / npg, t % npg);
+    __syncthreads();
+    return true;
+}
+
+// Element k..k+7 of A^T rank-row j through the LDS page cache (or the page table when
+// the cache was not filled); NULL for an out-of-range page.
+__device__ inline const uint16_t *a_paged(const WeightsDev &w, const int *cache, bool cached, int64_t ptb, int j0,
+                                          int j, int k)
+{
+    const int P = w.page_elems, q = k / P;
+    const int pg = cached ? cache[(j - j0) * (w.d_in / P) + q] : page_id<false>(w, ptb, j, q);
+    return pg >= 0 ? page_ptr(w, pg, k - q * P) : nullptr;
 }
 
 __device__ inline uint4 load16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
@@ -210,15 +256,22 @@ template <bool PAGED, bool PERROW, int RJ, int NR>
 __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
 {
     __shared__ float red[kWaves * NR * RJ];
+    __shared__ int pcache[PAGED ? kPageCache : 1];
     const Item it = work(a);
     if (!it.ok) return;
-    const ProjDev &pd = a.p[it.p];
+    const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
     const int j0 = it.slice * a.jw;
     const int jend = min(j0 + a.jw, pd.w.r_max);
     const TileHead th = tile_head<PERROW>(a.ts, pd.w, it.tile);
     if (!th.valid || j0 >= jend) return;
     const int rank = slot_rank(pd.w, th.slot);
     const int jload = PAGED ? min(jend, rank) : jend;
+    bool cached = false;
+    int64_t ptb = 0;
+    if (PAGED) {
+        ptb = pt_base<false>(pd.w, th.slot);
+        if (j0 < jload) cached = cache_a_pages<kThreads>(pd.w, th.slot, j0, jload, pcache);
+    }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_oct = pd.w.d_in >> 3;
     const uint4 z4 = make_uint4(0, 0, 0, 0);
@@ -247,11 +300,17 @@ __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
 #pragma unroll
                 for (int jj = 0; jj < RJ; ++jj) {
                     av[jj] = aw[jj] = z4;
-                    if (jb + jj < jload) {
-                        const uint16_t *p = rank_row_ptr<PAGED, false>(pd.w, th.slot, jb + jj, 8 * o);
+                    const int j = jb + jj;
+                    if (j >= jload) continue;
+                    if (!PAGED) {
+                        const uint16_t *r = dense_row<false>(pd.w, th.slot, j);
+                        av[jj] = load16(r + 8 * o);
+                        if (in2) aw[jj] = load16(r + 8 * o2);
+                    } else {
+                        const uint16_t *p = a_paged(pd.w, pcache, cached, ptb, j0, j, 8 * o);
                         if (p) av[jj] = load16(p);
                         if (in2) {
-                            const uint16_t *p2 = rank_row_ptr<PAGED, false>(pd.w, th.slot, jb + jj, 8 * o2);
+                            const uint16_t *p2 = a_paged(pd.w, pcache, cached, ptb, j0, j, 8 * o2);
                             if (p2) aw[jj] = load16(p2);
                         }
                     }
@@ -289,9 +348,10 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Ar
     constexpr int W = kMfmaShrinkThreads / 64;
     constexpr int U = 8 / MTX;  // k-steps in flight per wavefront
     __shared__ float red[W * 1024];
+    __shared__ int pcache[PAGED ? kPageCache : 1];
     const Item it = work(a);
     if (!it.ok) return;
-    const ProjDev &pd = a.p[it.p];
+    const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
     const int j0 = it.slice * 16;
     if (j0 >= pd.w.r_max) return;
     const TileHead th = tile_head<false>(a.ts, pd.w, it.tile);
@@ -302,6 +362,13 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Ar
     const int MT = min((th.nrows + 15) >> 4, MTX);
     const int jcol = j0 + li;                        // this lane's rank column (B operand)
     const bool jload = jcol < (PAGED ? rank : pd.w.r_max);
+    bool cached = false;
+    int64_t ptb = 0;
+    if (PAGED) {
+        ptb = pt_base<false>(pd.w, th.slot);
+        const int j1 = min(j0 + 16, rank);
+        if (j0 < j1) cached = cache_a_pages<kMfmaShrinkThreads>(pd.w, th.slot, j0, j1, pcache);
+    }
     int xrow[MTX];
 #pragma unroll
     for (int mt = 0; mt < MTX; ++mt) {
@@ -322,8 +389,12 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Ar
             const bool kin = k < d_in;
             bq[u] = z4;
             if (kin && jload) {
-                const uint16_t *p = rank_row_ptr<PAGED, false>(pd.w, th.slot, jcol, k);
-                if (p) bq[u] = load16(p);
+                if (!PAGED) {
+                    bq[u] = load16(dense_row<false>(pd.w, th.slot, jcol) + k);
+                } else {
+                    const uint16_t *p = a_paged(pd.w, pcache, cached, ptb, j0, jcol, k);
+                    if (p) bq[u] = load16(p);
+                }
             }
 #pragma unroll
             for (int mt = 0; mt < MTX; ++mt)
@@ -362,13 +433,35 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Ar
 // VALU expand.  Workgroup = one tile x 512 columns; wavefront w holds rank-rows
 // w, w+4, ... of B (loaded once, all in flight); NR rows per pass; the four partial
 // sums are added in LDS and wavefront q updates row q of the pass.
+template <bool PERROW, int NR>
+struct ExpandPass {
+    int rows[NR];
+    float sv[NR];  // lane j holds v[row][j]
+    int my_row;    // row this wavefront updates
+    uint4 yv;      // its y octet
+
+    __device__ void load(const Args &a, const ProjDev &pd, const TileHead &th, int rg, int c, bool cin)
+    {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int q = 0; q < NR; ++q)
+            rows[q] = (rg + q < th.nrows) ? row_of<PERROW>(a.ts, th.pos0 + rg + q, a.n_rows) : -1;
+        my_row = (wave < NR && rg + wave < th.nrows) ? row_of<PERROW>(a.ts, th.pos0 + rg + wave, a.n_rows) : -1;
+#pragma unroll
+        for (int q = 0; q < NR; ++q)
+            sv[q] = (rows[q] >= 0 && lane < pd.w.r_max) ? pd.v[(int64_t)rows[q] * pd.ldv + lane] : 0.f;
+        yv = make_uint4(0, 0, 0, 0);
+        if (my_row >= 0 && cin) yv = load16(pd.y + (int64_t)my_row * pd.ldy + c);
+    }
+};
+
 template <bool PAGED, bool PERROW, int NR>
 __global__ __launch_bounds__(kThreads) void lora_expand_valu_kernel(Args a)
 {
     __shared__ float red[kWaves * NR * 8 * 64];
     const Item it = work(a);
     if (!it.ok) return;
-    const ProjDev &pd = a.p[it.p];
+    const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
     const TileHead th = tile_head<PERROW>(a.ts, pd.w, it.tile);
     if (!th.valid) return;
     const int rank = slot_rank(pd.w, th.slot);
@@ -377,30 +470,39 @@ __global__ __launch_bounds__(kThreads) void lora_expand_valu_kernel(Args a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = it.slice * kCols + 8 * lane;
     const bool cin = c < pd.w.d_out;
+    // the first pass's rows, v and y first: their loads are not queued behind B's
+    ExpandPass<PERROW, NR> ps;
+    ps.load(a, pd, th, 0, c, cin);
     uint4 bv[kMaxRankPerWave];
+    if (!PAGED) {
 #pragma unroll
-    for (int u = 0; u < kMaxRankPerWave; ++u) {
-        const int j = wave + kWaves * u;
-        bv[u] = make_uint4(0, 0, 0, 0);
-        if (cin && j < jlim) {
-            const uint16_t *p = rank_row_ptr<PAGED, true>(pd.w, th.slot, j, c);
-            if (p) bv[u] = load16(p);
+        for (int u = 0; u < kMaxRankPerWave; ++u) {
+            const int j = wave + kWaves * u;
+            bv[u] = make_uint4(0, 0, 0, 0);
+            if (cin && j < jlim) bv[u] = load16(dense_row<true>(pd.w, th.slot, j) + c);
+        }
+    } else {
+        // page ids of all this wavefront's rank-rows, then all the data
+        const int P = pd.w.page_elems, q = c / P, within = c - q * P;
+        const int64_t ptb = pt_base<true>(pd.w, th.slot);
+        int pg[kMaxRankPerWave];
+#pragma unroll
+        for (int u = 0; u < kMaxRankPerWave; ++u) {
+            const int j = wave + kWaves * u;
+            pg[u] = (cin && j < jlim) ? page_entry<true>(pd.w, ptb, j, q) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kMaxRankPerWave; ++u) {
+            bv[u] = make_uint4(0, 0, 0, 0);
+            const int g = page_ok(pd.w, pg[u]);
+            if (g >= 0) bv[u] = load16(page_ptr(pd.w, g, within));
         }
     }
     for (int rg = 0; rg < th.nrows; rg += NR) {
-        int rows[NR];
-        float sv[NR];  // lane j holds v[row][j]
+        if (rg > 0) ps.load(a, pd, th, rg, c, cin);
+        float sv[NR];
 #pragma unroll
-        for (int q = 0; q < NR; ++q) {
-            rows[q] = (rg + q < th.nrows) ? row_of<PERROW>(a.ts, th.pos0 + rg + q, a.n_rows) : -1;
-            sv[q] = (rows[q] >= 0 && lane < pd.w.r_max) ? pd.v[(int64_t)rows[q] * pd.ldv + lane] : 0.f;
-        }
-        // the wavefront that updates row `wave` of the pass fetches that y octet now
-        const int my_row = (wave < NR && rg + wave < th.nrows) ? row_of<PERROW>(a.ts, th.pos0 + rg + wave, a.n_rows) : -1;
-        uint4 yv = make_uint4(0, 0, 0, 0);
-        if (my_row >= 0 && cin) yv = load16(pd.y + (int64_t)my_row * pd.ldy + c);
-#pragma unroll
-        for (int q = 0; q < NR; ++q) sv[q] = lane < rank ? sc * sv[q] : 0.f;
+        for (int q = 0; q < NR; ++q) sv[q] = lane < rank ? sc * ps.sv[q] : 0.f;
         float acc[NR][8];
 #pragma unroll
         for (int q = 0; q < NR; ++q)
@@ -429,9 +531,9 @@ __global__ __launch_bounds__(kThreads) void lora_expand_valu_kernel(Args a)
 #pragma unroll
             for (int e = 0; e < 8; ++e) red[((wave * NR + q) * 8 + e) * 64 + lane] = acc[q][e];
         __syncthreads();
-        if (my_row >= 0 && cin && rank > 0) {
+        if (ps.my_row >= 0 && cin && rank > 0) {
             const int q = wave;
-            const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w};
+            const uint32_t yw[4] = {ps.yv.x, ps.yv.y, ps.yv.z, ps.yv.w};
             uint32_t out[4];
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
@@ -446,7 +548,8 @@ __global__ __launch_bounds__(kThreads) void lora_expand_valu_kernel(Args a)
                 const float hi = h2f((uint16_t)(yw[e2] >> 16)) + d[1];
                 out[e2] = (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
             }
-            *reinterpret_cast<uint4 *>(pd.y + (int64_t)my_row * pd.ldy + c) = make_uint4(out[0], out[1], out[2], out[3]);
+            *reinterpret_cast<uint4 *>(pd.y + (int64_t)ps.my_row * pd.ldy + c) =
+                make_uint4(out[0], out[1], out[2], out[3]);
         }
         __syncthreads();
     }
@@ -464,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args a)
     uint16_t *lds_b = reinterpret_cast<uint16_t *>(smem);
     const Item it = work(a);
     if (!it.ok) return;
-    const ProjDev &pd = a.p[it.p];
+    const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
     const TileHead th = tile_head<false>(a.ts, pd.w, it.tile);
     if (!th.valid) return;
     const int rank = slot_rank(pd.w, th.slot);
@@ -478,17 +581,14 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args a)
     for (int mt = 0; mt < MT; ++mt) {
         const int rr = 16 * mt + li;
         const int row = rr < th.nrows ? row_of<false>(a.ts, th.pos0 + rr, a.n_rows) : -1;
-        // y (accumulator start) and v for this slice: lane holds y[row][cw + 16 nt + 4 lg .. +3]
-        f4_t acc[8];
+        // y (accumulator start) and v for this slice: lane holds y[row][cw + 16 nt + 4 lg .. +3];
+        // every load is issued before any of them is used
+        uint2 yq[8];
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
             const int col = cw + 16 * nt + 4 * lg;
-            acc[nt] = f4_t{0.f, 0.f, 0.f, 0.f};
-            if (row >= 0 && col < pd.w.d_out) {
-                const uint2 yq = *reinterpret_cast<const uint2 *>(pd.y + (int64_t)row * pd.ldy + col);
-                acc[nt] = f4_t{h2f((uint16_t)(yq.x & 0xffff)), h2f((uint16_t)(yq.x >> 16)),
-                               h2f((uint16_t)(yq.y & 0xffff)), h2f((uint16_t)(yq.y >> 16))};
-            }
+            yq[nt] = make_uint2(0, 0);
+            if (row >= 0 && col < pd.w.d_out) yq[nt] = *reinterpret_cast<const uint2 *>(pd.y + (int64_t)row * pd.ldy + col);
         }
         float4 vq[RQ];
 #pragma unroll
@@ -501,13 +601,29 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args a)
             // stage B while the y and v loads are in flight: all loads first, then LDS;
             // rows past the rank become 0, rows past r_max (dense) are not read
             uint4 q[kStage];
+            if (!PAGED) {
 #pragma unroll
-            for (int i = 0; i < kStage; ++i) {
-                const int o = tid + i * kThreads, k = o >> 6, oc = (o & 63) * 8;
-                q[i] = make_uint4(0, 0, 0, 0);
-                if (k < rstage && c0 + oc < pd.w.d_out && k < (PAGED ? rank : pd.w.r_max)) {
-                    const uint16_t *p = rank_row_ptr<PAGED, true>(pd.w, th.slot, k, c0 + oc);
-                    if (p) q[i] = load16(p);
+                for (int i = 0; i < kStage; ++i) {
+                    const int o = tid + i * kThreads, k = o >> 6, oc = (o & 63) * 8;
+                    q[i] = make_uint4(0, 0, 0, 0);
+                    if (k < pd.w.r_max && c0 + oc < pd.w.d_out) q[i] = load16(dense_row<true>(pd.w, th.slot, k) + c0 + oc);
+                }
+            } else {
+                // page ids first, then all the data
+                const int64_t ptb = pt_base<true>(pd.w, th.slot);
+                const int P = pd.w.page_elems;
+                int pg[kStage];
+#pragma unroll
+                for (int i = 0; i < kStage; ++i) {
+                    const int o = tid + i * kThreads, k = o >> 6, c = c0 + (o & 63) * 8;
+                    pg[i] = (k < rank && c < pd.w.d_out) ? page_entry<true>(pd.w, ptb, k, c / P) : -1;
+                }
+#pragma unroll
+                for (int i = 0; i < kStage; ++i) {
+                    const int o = tid + i * kThreads, c = c0 + (o & 63) * 8;
+                    q[i] = make_uint4(0, 0, 0, 0);
+                    const int g = page_ok(pd.w, pg[i]);
+                    if (g >= 0) q[i] = load16(page_ptr(pd.w, g, c % P));
                 }
             }
 #pragma unroll
@@ -520,6 +636,11 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args a)
             __syncthreads();
             if (rank <= 0) return;
         }
+        f4_t acc[8];
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+            acc[nt] = f4_t{h2f((uint16_t)(yq[nt].x & 0xffff)), h2f((uint16_t)(yq[nt].x >> 16)),
+                           h2f((uint16_t)(yq[nt].y & 0xffff)), h2f((uint16_t)(yq[nt].y >> 16))};
 #pragma unroll
         for (int kq = 0; kq < RQ; ++kq) {
             if (16 * kq >= rank) break;

@@ -74,7 +74,7 @@ def run_bgmv(w: B.Weights, dc: DeviceCase, idx, split_calls=False):
     return dc.results()
 
 
-def run_sgmv(w: B.Weights, dc: DeviceCase, idx=None, seg_ptr=None, seg_slot=None, max_tile_rows=64):
+def run_sgmv(w: B.Weights, dc: DeviceCase, idx=None, seg_ptr=None, seg_slot=None, max_tile_rows=None):
     """Segment form.  With idx: rows are grouped by the library's builder (row_map);
     with seg_ptr/seg_slot: contiguous segments, no row map."""
     if idx is not None:
@@ -85,6 +85,8 @@ def run_sgmv(w: B.Weights, dc: DeviceCase, idx=None, seg_ptr=None, seg_slot=None
         n_pos = n_act
     else:
         row_map, n_pos = None, dc.n
+    if max_tile_rows is None:
+        max_tile_rows = B.lora_pick_tile_rows(seg_ptr)
     tiles = B.lora_build_tiles(seg_ptr, seg_slot, max_tile_rows)
     nprob, msgs = oracle.check_tiles(tiles, seg_ptr, seg_slot, max_tile_rows)
     assert nprob == 0, msgs[:3]

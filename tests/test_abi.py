@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 18 and set(names) == set(B.EXPORTS)
+    assert len(names) == 19 and set(names) == set(B.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", build_mod.LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (lora_\w+)", out))
@@ -277,3 +277,10 @@ def test_multi_projection_errors():
     assert L.lora_bgmv_expand_multi(None, FAKE, 8, 2, arr) == B.LORA_E_SHAPE
     arr[1].ldy = 1024
     assert L.lora_bgmv_expand_multi(None, FAKE, 0, 2, arr) == B.LORA_OK                     # no rows: no launch
+
+
+def test_pick_tile_rows():
+    assert B.lora_pick_tile_rows(np.array([0, 1, 4, 6, 8], np.int32)) == 4
+    assert B.lora_pick_tile_rows(np.array([0, 127, 140], np.int32)) == 4
+    assert B.lora_pick_tile_rows(np.array([0, 5, 133], np.int32)) == 16
+    assert B.lora_pick_tile_rows(np.array([0], np.int32)) == 4
