@@ -12,7 +12,9 @@ Per adapted projection with n_act active rows, d_in -> d_out, distinct slots D
                  (B once per distinct slot, y read + written, v read)
   flops        = 2 * sum_{active rows} r_row * (d_in + d_out)
 
-Split-K partials are an implementation cost and are not counted.
+A launch that serves several projections sharing one x (q/k/v, gate/up) reads x
+once; bench.py counts it once per launch.  Nothing the method avoids is counted
+(no padding to r_max, no gathered weight copies, no merged d_in x d_out matrix).
 """
 from __future__ import annotations
 
