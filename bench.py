@@ -138,56 +138,44 @@ def make_ops(spec, layers, device, tile_rows=None):
     return groups
 
 
-def launch_group(ops, kernel, grouped):
-    """One launch for the whole group (grouped) or one launch per projection."""
+def launch_unit(kind, ops, fused_chunks):
+    """One launch over `ops` (projections sharing x): kind is "shrink", "expand" or
+    "fused" (both steps of the per-row form in one launch)."""
     from segmented_gather_matmul_amd import binding as B
     op0 = ops[0]
-    if not grouped or len(ops) == 1:
-        for op in ops:
-            if op.segs is None:
-                if kernel == "shrink":
-                    B.lora_bgmv_shrink(op.v, op.x, op.idx, op.w)
-                else:
-                    B.lora_bgmv_expand(op.y, op.v, op.idx, op.w)
-            else:
-                if kernel == "shrink":
-                    B.lora_sgmv_shrink(op.v, op.x, op.w, op.segs)
-                else:
-                    B.lora_sgmv_expand(op.y, op.v, op.w, op.segs)
-        return
     items = [(op.w, op.v, op.y) for op in ops]
     n = op0.x.shape[0]
-    if op0.segs is None:
-        if kernel == "shrink":
+    if kind == "fused":
+        B.lora_bgmv_multi(op0.x, op0.idx, items, chunks=fused_chunks)
+    elif op0.segs is None:
+        if kind == "shrink":
             B.lora_bgmv_shrink_multi(op0.x, op0.idx, items)
         else:
             B.lora_bgmv_expand_multi(op0.idx, items, n)
     else:
-        if kernel == "shrink":
+        if kind == "shrink":
             B.lora_sgmv_shrink_multi(op0.x, op0.segs, items)
         else:
             B.lora_sgmv_expand_multi(op0.segs, items, n)
 
 
-def launches(groups, grouped):
-    """(kernel, ops) of every launch of one step, in order."""
+def launches(groups, grouped, fused_chunks):
+    """(kind, ops) of every launch of one step, in order.  With fused_chunks >= 1 the
+    per-row form runs each unit as one fused launch."""
     out = []
     for ops in groups:
         units = [ops] if grouped else [[op] for op in ops]
-        for k in ("shrink", "expand"):
-            out += [(k, u) for u in units]
+        for u in units:
+            if u[0].segs is None and fused_chunks >= 1:
+                out.append(("fused", u))
+            else:
+                out += [("shrink", u), ("expand", u)]
     return out
 
 
-def step(groups, grouped):
-    for ops in groups:
-        if grouped:
-            launch_group(ops, "shrink", True)
-            launch_group(ops, "expand", True)
-        else:
-            for op in ops:
-                launch_group([op], "shrink", False)
-                launch_group([op], "expand", False)
+def step(plan, fused_chunks):
+    for kind, ops in plan:
+        launch_unit(kind, ops, fused_chunks)
 
 
 # ------------------------------------------------------------------ HIP events (raw handles)
@@ -214,7 +202,7 @@ class HipEvents:
         self.hip.hipEventDestroy(e)
 
 
-def kernel_durations(groups, grouped, steps):
+def kernel_durations(plan, fused_chunks, steps):
     """Duration of every launch, from event pairs attached to the launches themselves
     (hipExtLaunchKernel records start and stop on the launch stream)."""
     from segmented_gather_matmul_amd import binding as B
@@ -222,20 +210,53 @@ def kernel_durations(groups, grouped, steps):
     ev = HipEvents()
     recs = []
     for _ in range(steps):
-        for ops in groups:
-            units = [ops] if grouped else [[op] for op in ops]
-            for u in units:
-                for k in ("shrink", "expand"):
-                    e0, e1 = ev.create(), ev.create()
-                    B.lora_set_launch_events(e0, e1)
-                    launch_group(u, k, grouped)
-                    recs.append((k, u, e0, e1))
+        for kind, u in plan:
+            e0, e1 = ev.create(), ev.create()
+            B.lora_set_launch_events(e0, e1)
+            launch_unit(kind, u, fused_chunks)
+            recs.append((kind, u, e0, e1))
     torch.cuda.synchronize()
-    out = {"shrink": [], "expand": []}
+    out = {}
     for k, u, e0, e1 in recs:
-        out[k].append((u, ev.elapsed_ms(e0, e1)))
+        out.setdefault(k, []).append((u, ev.elapsed_ms(e0, e1)))
         ev.destroy(e0)
         ev.destroy(e1)
+    return out
+
+
+def reference_floors(plan, spec, steps):
+    """Context for the roofline, timed like the step (graph replay, events around the
+    replays): the same number of launches (a) doing nothing (an empty spin kernel) and
+    (b) each a plain device copy moving the bytes of the launch it stands for (half
+    read, half written; distinct buffers, so the copies stream from HBM as the step
+    does)."""
+    import torch
+    sizes = [unit_counts(spec, u)[f"{k}_bytes"] for k, u in plan]
+    bufs = [(torch.empty(b // 4 + 1, dtype=torch.float16, device="cuda"),
+             torch.empty(b // 4 + 1, dtype=torch.float16, device="cuda")) for b in sizes]
+    out = {"launches": len(plan)}
+    for name, body in (("empty", lambda: [torch.cuda._sleep(0) for _ in plan]),
+                       ("copy", lambda: [d.copy_(s_) for s_, d in bufs])):
+        body()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body()
+        for _ in range(3):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"{name}_ms_per_step"] = round(e0.elapsed_time(e1) / steps, 5)
+        del g
+    moved = sum(2 * (b // 4 + 1) * 2 for b in sizes)
+    out["copy_bytes_per_step"] = moved
+    out["copy_gbs"] = round(moved / (out["copy_ms_per_step"] * 1e-3) / 1e9, 1)
+    del bufs
+    torch.cuda.empty_cache()
     return out
 
 
@@ -251,7 +272,8 @@ def unit_counts(spec, ops):
     eb = sum(cm.expand_bytes(idx, rank, o.d_out, r_max) for o in ops)
     sf = sum(cm.shrink_flops(idx, rank, o.d_in) for o in ops)
     ef = sum(cm.expand_flops(idx, rank, o.d_out) for o in ops)
-    return dict(shrink_bytes=sb, expand_bytes=eb, shrink_flops=sf, expand_flops=ef)
+    return dict(shrink_bytes=sb, expand_bytes=eb, shrink_flops=sf, expand_flops=ef,
+                fused_bytes=sb + eb, fused_flops=sf + ef)
 
 
 def kernel_source_sha():
@@ -329,6 +351,10 @@ def main():
                     help="tile height for the segment form (default: lora_pick_tile_rows)")
     ap.add_argument("--form", choices=["bgmv", "sgmv"], default=None,
                     help="per-row slots (bgmv) or rows grouped by adapter (sgmv); default: the workload's own")
+    ap.add_argument("--fused-chunks", type=int, default=-1,
+                    help="per-row form: -1 = separate shrink and expand launches (the library's choice); c >= 1 = "
+                         "one launch per unit, each workgroup covering c 512-column chunks")
+    ap.add_argument("--no-floors", action="store_true", help="skip the empty-launch and copy reference steps")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (byte-counter calibration)")
     args = ap.parse_args()
@@ -367,18 +393,19 @@ def main():
     counts = [unit_counts(spec, ops) for ops in groups]
     step_bytes = sum(c["shrink_bytes"] + c["expand_bytes"] for c in counts)
     step_flops = sum(c["shrink_flops"] + c["expand_flops"] for c in counts)
-    n_launch = len(launches(groups, grouped))
+    plan = launches(groups, grouped, args.fused_chunks)
+    n_launch = len(plan)
 
     log(f"[bench] {n_launch} launches/step, {step_bytes / 1e6:.1f} MB algorithmic per step; warmup {args.warmup}")
     stream = torch.cuda.current_stream()
     if args.no_graph:
-        run = lambda: step(groups, grouped)
+        run = lambda: step(plan, args.fused_chunks)
     else:
-        step(groups, grouped)  # first eager pass (loads kernels)
+        step(plan, args.fused_chunks)  # first eager pass (loads kernels)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(groups, grouped)
+            step(plan, args.fused_chunks)
         run = g.replay
     for _ in range(args.warmup):
         run()
@@ -395,9 +422,9 @@ def main():
     log(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step (wall {wall_ms:.4f})")
 
     log(f"[bench] per-launch event pass: {args.kernel_steps} steps")
-    kd = kernel_durations(groups, grouped, args.kernel_steps)
+    kd = kernel_durations(plan, args.fused_chunks, args.kernel_steps)
     per_kernel, totals = {}, {}
-    for k in ("shrink", "expand"):
+    for k in kd:
         recs = kd[k]
         us = np.array([1e3 * t for _, t in recs])
         kb = sum(unit_counts(spec, u)[f"{k}_bytes"] for u, _ in recs)
@@ -409,7 +436,7 @@ def main():
                              gbs=round(kb / (totals[k] * 1e-6) / 1e9, 1),
                              tflops=round(kf / (totals[k] * 1e-6) / 1e12, 3))
     by_shape = {}
-    for k in ("shrink", "expand"):
+    for k in kd:
         for u, t in kd[k]:
             key = f"{k} {'+'.join(o.proj for o in u)} {u[0].d_in}->{'/'.join(str(o.d_out) for o in u)}"
             rec = by_shape.setdefault(key, [0, 0.0, unit_counts(spec, u)[f"{k}_bytes"]])
@@ -419,11 +446,16 @@ def main():
                 for key, (n, t, nb) in by_shape.items()}
     dom = max(per_kernel, key=lambda k: totals[k])
     pk = per_kernel[dom]
-    kernel_name = {"shrink": "lora_shrink_kernel", "expand": "lora_expand_kernel"}[dom]
+    kernel_name = {"shrink": "lora_shrink_kernel", "expand": "lora_expand_kernel", "fused": "lora_fused_row_kernel"}[dom]
     traffic = traffic_from_profile(args.workload, dom)
     roofline = dict(bound="hbm", achieved=pk["gbs"], peak=cm.HBM_PEAK_GBS, unit="GB/s",
                     frac=round(pk["gbs"] / cm.HBM_PEAK_GBS, 4), traffic=traffic, kernel=kernel_name,
                     avg_launch_us=pk["avg_us"], algorithmic_bytes_per_launch=pk["bytes_per_launch"])
+
+    floors = None
+    if not args.no_floors:
+        log("[bench] reference steps: empty launches, plain copies of the same bytes")
+        floors = reference_floors(plan, spec, min(args.steps, 20))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -448,7 +480,8 @@ def main():
                    "projections": list(spec["shapes"]), "batch_rows": spec["batch"].n,
                    "num_slots": spec["num_slots"], "rank": sorted(set(int(r) for r in spec["rank"])),
                    "popularity": spec["popularity"], "form": spec["form"], "layout": spec["layout"],
-                   "grouped": grouped, "launches_per_step": n_launch, "tile_rows": args.tile_rows, "graph": not args.no_graph,
+                   "grouped": grouped, "launches_per_step": n_launch, "tile_rows": args.tile_rows,
+                   "fused_chunks": args.fused_chunks if spec["form"] == "bgmv" else None, "graph": not args.no_graph,
                    "parallelism": "none"},
         "us_per_layer": round(1e3 * ms / layers, 3),
         "tflops": round(step_flops / (ms * 1e-3) / 1e12, 4),
@@ -459,6 +492,7 @@ def main():
         "kernels": per_kernel,
         "launch_shapes": by_shape,
         "roofline": roofline,
+        "floors": floors,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -229,9 +229,10 @@ int lora_bgmv_expand(void *stream, void *y, int64_t ldy, const float *v, int64_t
                      const int32_t *idx, int32_t n_rows, const lora_weights *w);
 
 /*
- * The whole add-on in decode form: lora_bgmv_shrink then lora_bgmv_expand on the
- * same stream (two launches).  v (device fp32 [n_rows][ldv]) receives the shrink
- * result as documented above.
+ * The whole add-on in decode form (Punica digest, section 5.5, BGMV; blog reference
+ * loop): the result of lora_bgmv_shrink followed by lora_bgmv_expand, bit for bit.
+ * v (device fp32 [n_rows][ldv]) receives the shrink result as documented above.
+ * Same as lora_bgmv_multi with one projection and chunks = 0.
  */
 int lora_bgmv(void *stream, void *y, int64_t ldy, const void *x, int64_t ldx, const int32_t *idx,
               int32_t n_rows, const lora_weights *w, float *v, int64_t ldv);
@@ -256,13 +257,31 @@ int lora_bgmv_shrink_multi(void *stream, const void *x, int64_t ldx, const int32
 int lora_bgmv_expand_multi(void *stream, const int32_t *idx, int32_t n_rows, int32_t n_proj,
                            const lora_proj *proj);
 
+/*
+ * Shrink and expand of the decode form for up to LORA_MAX_PROJ projections sharing x:
+ * every projection p gets, bit for bit, the v and y of lora_bgmv_shrink_multi followed
+ * by lora_bgmv_expand_multi.  Argument rules are the union of theirs, all checked
+ * before anything is launched.
+ *   chunks = -1: those two launches;
+ *   chunks >= 1: one launch.  Each workgroup covers `chunks` 512-column pieces of one
+ *                row's d_out and recomputes that row's v itself, so no step waits for
+ *                another workgroup; the workgroup holding the row's first piece
+ *                stores v;
+ *   chunks = 0:  the library chooses (currently the two launches, which measure faster
+ *                at the Llama-2 decode shapes).
+ * With one launch, v must not overlap x, y or the weights (it is written while they
+ * are read).
+ */
+int lora_bgmv_multi(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows,
+                    int32_t n_proj, const lora_proj *proj, int32_t chunks);
+
 /* ---------------------------------------------------------------- diagnostics */
 /*
  * Timing hook: attach two hipEvent_t (created by the caller; either may be NULL) to
  * the next kernel launch made by the calling thread (launched with
  * hipExtLaunchKernelGGL, which records `start_event` when the kernel starts and
  * `stop_event` when it ends, on the launch stream).  The pair is consumed by that
- * one launch; for lora_bgmv it is the shrink launch.  This is the library's only
+ * one launch; where a call makes two launches, it is the first.  This is the library's only
  * other per-thread state.  Returns LORA_OK.
  */
 int lora_set_launch_events(void *start_event, void *stop_event);

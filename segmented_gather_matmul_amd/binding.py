@@ -31,7 +31,7 @@ EXPORTS = ["lora_build_segments", "lora_tiles_bound", "lora_build_tiles", "lora_
            "lora_validate_segments_host", "lora_sgmv_shrink", "lora_sgmv_expand",
            "lora_bgmv_shrink", "lora_bgmv_expand", "lora_bgmv", "lora_last_error", "lora_status_str",
            "lora_abi_version", "lora_set_launch_events", "lora_sgmv_shrink_multi", "lora_sgmv_expand_multi",
-           "lora_bgmv_shrink_multi", "lora_bgmv_expand_multi", "lora_pick_tile_rows"]
+           "lora_bgmv_shrink_multi", "lora_bgmv_expand_multi", "lora_pick_tile_rows", "lora_bgmv_multi"]
 MAX_PROJ = 4
 
 
@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
             "lora_bgmv_shrink_multi": [P, P, I64, P, I32, I32, P],
             "lora_bgmv_expand_multi": [P, P, I32, I32, P],
             "lora_pick_tile_rows": [P, I32],
+            "lora_bgmv_multi": [P, P, I64, P, I32, I32, P, I32],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -320,3 +321,11 @@ def lora_bgmv_shrink_multi(x, idx, items, stream=None):
 def lora_bgmv_expand_multi(idx, items, n_rows, stream=None):
     arr = proj_list(items)
     _check(lib().lora_bgmv_expand_multi(_stream(stream), _ptr(idx), int(n_rows), len(items), arr))
+
+
+def lora_bgmv_multi(x, idx, items, chunks=0, stream=None):
+    """Shrink and expand of the decode form; chunks: 0 library's choice, -1 two launches,
+    c >= 1 one launch with c 512-column chunks per workgroup."""
+    arr = proj_list(items)
+    _check(lib().lora_bgmv_multi(_stream(stream), _ptr(x), _ld(x), _ptr(idx), int(x.shape[0]), len(items), arr,
+                                 int(chunks)))

@@ -22,6 +22,10 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 // projection) pairs: 1, 2 or 4, to keep the grid near kTargetGroups workgroups.
 int32_t plan_shrink_jw(int32_t work_tiles, int32_t r_max);
 
+// Chunks of 512 columns per workgroup of the fused per-row launch, or -1 for two
+// launches (shrink, then expand); both give the same bits.
+int32_t plan_fused_chunks(int32_t n_rows, int32_t n_proj, const lora_proj *proj);
+
 constexpr int32_t kMfmaMinRows = 8;      // launches with a tile this tall run the MFMA kernels
 constexpr int32_t kTargetGroups = 1024;  // shrink workgroups to aim for
 constexpr int32_t kLongSegment = 128;    // segments this long get 16-row (MFMA) tiles

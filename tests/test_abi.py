@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 19 and set(names) == set(B.EXPORTS)
+    assert len(names) == 20 and set(names) == set(B.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", build_mod.LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (lora_\w+)", out))
@@ -277,6 +277,35 @@ def test_multi_projection_errors():
     assert L.lora_bgmv_expand_multi(None, FAKE, 8, 2, arr) == B.LORA_E_SHAPE
     arr[1].ldy = 1024
     assert L.lora_bgmv_expand_multi(None, FAKE, 0, 2, arr) == B.LORA_OK                     # no rows: no launch
+
+
+def test_one_launch_decode_errors():
+    """lora_bgmv_multi checks what both steps need before launching anything."""
+    L = B.lib()
+    c1, c2 = _desc(), _desc(d_in=2048)
+    arr = (B.CProj * 2)()
+    for i in range(2):
+        arr[i].w, arr[i].v, arr[i].ldv, arr[i].y, arr[i].ldy = ctypes.addressof(c1), FAKE, 16, FAKE, 1024
+    call = lambda x=FAKE, ldx=1024, idx=FAKE, n=8, n_proj=2, a=arr, chunks=0: \
+        L.lora_bgmv_multi(None, x, ldx, idx, n, n_proj, a, chunks)
+    assert call(idx=None) == B.LORA_E_NULL
+    assert call(n_proj=0) == B.LORA_E_SHAPE
+    assert call(a=None) == B.LORA_E_NULL
+    assert call(chunks=-2) == B.LORA_E_SHAPE
+    assert call(n=-1) == B.LORA_E_SHAPE
+    assert call(x=None) == B.LORA_E_NULL
+    assert call(x=FAKE + 8) == B.LORA_E_ALIGN
+    assert call(ldx=1000) == B.LORA_E_SHAPE
+    arr[1].ldy = 1000                                   # y checked even though x is fine
+    assert call() == B.LORA_E_SHAPE and "y" in B.last_error()
+    arr[1].ldy = 1024
+    arr[1].ldv = 12                                     # v leading dimension < r_max
+    assert call() == B.LORA_E_SHAPE
+    arr[1].ldv = 16
+    arr[1].w = ctypes.addressof(c2)
+    assert call() == B.LORA_E_SHAPE and "share x" in B.last_error()
+    arr[1].w = ctypes.addressof(c1)
+    assert call(n=0) == B.LORA_OK and call(n=0, chunks=-1) == B.LORA_OK and call(n=0, chunks=3) == B.LORA_OK
 
 
 def test_pick_tile_rows():
