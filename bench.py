@@ -355,6 +355,9 @@ def main():
                     help="per-row form: -1 = separate shrink and expand launches (the library's choice); c >= 1 = "
                          "one launch per unit, each workgroup covering c 512-column chunks")
     ap.add_argument("--no-floors", action="store_true", help="skip the empty-launch and copy reference steps")
+    ap.add_argument("--plan", type=int, default=0, metavar="JW",
+                    help="fix rank-rows per VALU shrink workgroup (0 = library's choice; results are "
+                         "bit-identical either way)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (byte-counter calibration)")
     args = ap.parse_args()
@@ -387,6 +390,7 @@ def main():
             raise SystemExit("the prefill workload is given as contiguous segments")
         spec["form"] = args.form
     layers = args.layers or spec["layers"]
+    B.lora_set_plan(args.plan)
     log(f"[bench] workload={args.workload} layers={layers} grouped={grouped} building inputs")
     groups = make_ops(spec, layers, device, args.tile_rows)
     torch.cuda.synchronize()
@@ -481,7 +485,8 @@ def main():
                    "num_slots": spec["num_slots"], "rank": sorted(set(int(r) for r in spec["rank"])),
                    "popularity": spec["popularity"], "form": spec["form"], "layout": spec["layout"],
                    "grouped": grouped, "launches_per_step": n_launch, "tile_rows": args.tile_rows,
-                   "fused_chunks": args.fused_chunks if spec["form"] == "bgmv" else None, "graph": not args.no_graph,
+                   "fused_chunks": args.fused_chunks if spec["form"] == "bgmv" else None, "plan": args.plan,
+                   "graph": not args.no_graph,
                    "parallelism": "none"},
         "us_per_layer": round(1e3 * ms / layers, 3),
         "tflops": round(step_flops / (ms * 1e-3) / 1e12, 4),

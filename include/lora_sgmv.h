@@ -24,7 +24,7 @@
  *    given leading dimension (in elements).
  *  - The caller owns every buffer.  The library never allocates or frees device memory,
  *    never synchronises, and keeps no state except a thread-local error message
- *    (and the one-shot timing events of lora_set_launch_events).
+ *    (and the thread-local diagnostics of lora_set_launch_events and lora_set_plan).
  *    Launching calls are asynchronous on `stream` (a hipStream_t; NULL = default).
  *    Inputs, outputs and metadata must stay alive until the work on `stream` ends.
  *  - Return value: LORA_OK (0) or a negative LORA_E_* code; lora_last_error() then
@@ -160,8 +160,9 @@ int lora_build_segments(const int32_t *idx, int32_t n, int32_t num_slots, int32_
 int32_t lora_tiles_bound(int32_t n_pos, int32_t n_seg, int32_t max_tile_rows);
 
 /*
- * Tile height suited to a batch: 16 (the MFMA kernels' slice) when some segment
- * has at least 128 rows, else 4 (the VALU kernels spread short segments widest).
+ * Tile height suited to a batch: 64 (four MFMA slices, fewest re-reads of each
+ * adapter) when some segment has at least 128 rows, else 4 (the VALU kernels spread
+ * short segments widest).
  * seg_ptr: host [n_seg + 1].  Any value in 1..LORA_MAX_TILE_ROWS gives the same
  * results within the stated tolerance; this only picks the faster launch shape.
  */
@@ -281,10 +282,18 @@ int lora_bgmv_multi(void *stream, const void *x, int64_t ldx, const int32_t *idx
  * the next kernel launch made by the calling thread (launched with
  * hipExtLaunchKernelGGL, which records `start_event` when the kernel starts and
  * `stop_event` when it ends, on the launch stream).  The pair is consumed by that
- * one launch; where a call makes two launches, it is the first.  This is the library's only
- * other per-thread state.  Returns LORA_OK.
+ * one launch; where a call makes two launches, it is the first.  Returns LORA_OK.
  */
 int lora_set_launch_events(void *start_event, void *stop_event);
+
+/*
+ * Tuning hook: for the calling thread's later launches, fixes the number of rank-rows
+ * each VALU shrink workgroup computes (1..64); 0 restores the library's choice.
+ * Results do not depend on it, bit for bit: every element of v is summed in the same
+ * order whatever the split.  Returns LORA_E_SHAPE outside 0..64.  Per-thread state,
+ * like the event pair.
+ */
+int lora_set_plan(int32_t shrink_rank_rows);
 
 const char *lora_last_error(void);   /* message of this thread's last failed call */
 const char *lora_status_str(int status);

@@ -31,7 +31,8 @@ EXPORTS = ["lora_build_segments", "lora_tiles_bound", "lora_build_tiles", "lora_
            "lora_validate_segments_host", "lora_sgmv_shrink", "lora_sgmv_expand",
            "lora_bgmv_shrink", "lora_bgmv_expand", "lora_bgmv", "lora_last_error", "lora_status_str",
            "lora_abi_version", "lora_set_launch_events", "lora_sgmv_shrink_multi", "lora_sgmv_expand_multi",
-           "lora_bgmv_shrink_multi", "lora_bgmv_expand_multi", "lora_pick_tile_rows", "lora_bgmv_multi"]
+           "lora_bgmv_shrink_multi", "lora_bgmv_expand_multi", "lora_pick_tile_rows", "lora_bgmv_multi",
+           "lora_set_plan"]
 MAX_PROJ = 4
 
 
@@ -93,6 +94,7 @@ def lib() -> ctypes.CDLL:
             "lora_bgmv_expand_multi": [P, P, I32, I32, P],
             "lora_pick_tile_rows": [P, I32],
             "lora_bgmv_multi": [P, P, I64, P, I32, I32, P, I32],
+            "lora_set_plan": [I32],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -284,6 +286,12 @@ def lora_bgmv_expand(y, v, idx, weights: Weights, stream=None):
 def lora_bgmv(y, x, idx, weights: Weights, v, stream=None):
     _check(lib().lora_bgmv(_stream(stream), _ptr(y), _ld(y), _ptr(x), _ld(x), _ptr(idx), int(y.shape[0]),
                            weights.ref, _ptr(v), _ld(v)))
+
+
+def lora_set_plan(shrink_rank_rows=0):
+    """Fix (or, with 0, release) the rank-rows per VALU shrink workgroup for this
+    thread's later launches; results are bit-identical either way."""
+    _check(lib().lora_set_plan(int(shrink_rank_rows)))
 
 
 def lora_set_launch_events(start_event, stop_event):

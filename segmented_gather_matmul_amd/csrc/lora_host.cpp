@@ -123,9 +123,10 @@ int32_t lora_pick_tile_rows(const int32_t *seg_ptr, int32_t n_seg)
 {
     int32_t longest = 0;
     for (int32_t g = 0; seg_ptr && g < n_seg; ++g) longest = std::max(longest, seg_ptr[g + 1] - seg_ptr[g]);
-    // Long segments (prefill) feed the MFMA kernels 16-row tiles; short ones (decode
-    // groups) run on the VALU kernels, where 4-row tiles spread the work widest.
-    return longest >= kLongSegment ? 16 : 4;
+    // Long segments (prefill) feed the MFMA kernels 64-row tiles, which re-read each
+    // adapter's A and B least; short ones (decode groups) run on the VALU kernels,
+    // where 4-row tiles spread the work widest.
+    return longest >= kLongSegment ? LORA_MAX_TILE_ROWS : 4;
 }
 
 int lora_build_tiles(const int32_t *seg_ptr, const int32_t *seg_slot, int32_t n_seg,

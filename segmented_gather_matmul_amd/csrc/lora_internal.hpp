@@ -19,8 +19,10 @@ int check_weights_desc(const lora_weights *w);
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Rank-rows per workgroup of a VALU shrink launch over `work_tiles` (tile,
-// projection) pairs: 1, 2 or 4, to keep the grid near kTargetGroups workgroups.
+// projection) pairs: 1, 2 or 4, to keep the grid near kTargetGroups workgroups, unless
+// lora_set_plan fixed it for the calling thread (t_plan_jw > 0).
 int32_t plan_shrink_jw(int32_t work_tiles, int32_t r_max);
+extern thread_local int32_t t_plan_jw;
 
 // Chunks of 512 columns per workgroup of the fused per-row launch, or -1 for two
 // launches (shrink, then expand); both give the same bits.
@@ -28,6 +30,6 @@ int32_t plan_fused_chunks(int32_t n_rows, int32_t n_proj, const lora_proj *proj)
 
 constexpr int32_t kMfmaMinRows = 8;      // launches with a tile this tall run the MFMA kernels
 constexpr int32_t kTargetGroups = 1024;  // shrink workgroups to aim for
-constexpr int32_t kLongSegment = 128;    // segments this long get 16-row (MFMA) tiles
+constexpr int32_t kLongSegment = 128;    // segments this long get 64-row (MFMA) tiles
 
 }  // namespace lora

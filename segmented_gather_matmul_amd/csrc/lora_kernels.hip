@@ -89,7 +89,6 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kRowsPerPass = 4;     // rows per pass of the VALU kernels (segment form)
 constexpr int kCols = 512;           // expand columns per workgroup
-constexpr int kBStride = kCols;      // LDS row stride of the staged B chunk (halves)
 constexpr int kMaxRankPerWave = LORA_MAX_RANK / kWaves;
 constexpr int kMfmaShrinkThreads = 1024;  // 16 wavefronts split d_in in the MFMA shrink
 constexpr int kFusedGroups = 4;            // 256-lane groups of a fused workgroup
@@ -253,8 +252,54 @@ __device__ inline Item work(const Args &a)
 }
 
 // ------------------------------------------------------------------------ shrink
+// Operands of one half-pair of the VALU shrink: octet o of x for NR rows and of A^T for
+// RJ rank-rows [jb, jb + RJ), zero past the end of d_in, for rows < 0 and for rank-rows
+// at or past jload.
+struct ShrinkSrc {
+    const WeightsDev &w;
+    const uint16_t *x;
+    int64_t ldx;
+    int slot, jb, jload, j0, n_oct;
+    int64_t ptb;
+    const int *pcache;
+    bool cached;
+};
+
+template <int NR, int RJ>
+struct ShrinkHalf {
+    uint4 x[NR], a[RJ];
+};
+
+template <bool PAGED, int NR, int RJ>
+__device__ inline ShrinkHalf<NR, RJ> load_half(const ShrinkSrc &s, const int (&rows)[NR], int o)
+{
+    ShrinkHalf<NR, RJ> h;
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
+    const bool in = o < s.n_oct;
+#pragma unroll
+    for (int q = 0; q < NR; ++q) h.x[q] = (in && rows[q] >= 0) ? load16(s.x + (int64_t)rows[q] * s.ldx + 8 * o) : z4;
+#pragma unroll
+    for (int jj = 0; jj < RJ; ++jj) {
+        const int j = s.jb + jj;
+        h.a[jj] = z4;
+        if (!in || j >= s.jload) continue;
+        if (!PAGED) {
+            h.a[jj] = load16(dense_row<false>(s.w, s.slot, j) + 8 * o);
+        } else {
+            const uint16_t *p = a_paged(s.w, s.pcache, s.cached, s.ptb, s.j0, j, 8 * o);
+            if (p) h.a[jj] = load16(p);
+        }
+    }
+    return h;
+}
+
 // VALU shrink.  Workgroup = one tile x rank-rows [j0, j0 + jw); NR rows and RJ
 // rank-rows per pass; d_in striped over the 256 lanes, 16 bytes per lane per load.
+// Lane l sums octets l, l + 256, l + 512, ... of d_in in that order, the octets taken
+// in pairs (o, o + 256) with a zero second term when o + 256 is past the end; then the
+// wavefront's lanes are added by an xor butterfly and the 4 wavefronts in order.  The
+// loads of the next half of a pair (256 octets) are in flight while the current half
+// is summed, so a workgroup streams its rank-rows instead of waiting once per pair.
 template <bool PAGED, bool PERROW, int RJ, int NR>
 __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
 {
@@ -277,6 +322,7 @@ __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
     }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_oct = pd.w.d_in >> 3;
+    const int n_half = 2 * ((n_oct + 2 * kThreads - 1) / (2 * kThreads));  // halves of octet pairs, even
     const uint4 z4 = make_uint4(0, 0, 0, 0);
     for (int rg = 0; rg < th.nrows; rg += NR) {
         int rows[NR];
@@ -289,39 +335,24 @@ __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
             for (int q = 0; q < NR; ++q)
 #pragma unroll
                 for (int jj = 0; jj < RJ; ++jj) acc[q][jj] = 0.f;
-            // two octets per lane per iteration keep more loads in flight
-            for (int o = tid; o < n_oct; o += 2 * kThreads) {
-                const int o2 = o + kThreads;
-                const bool in2 = o2 < n_oct;
-                uint4 xv[NR], xw[NR], av[RJ], aw[RJ];
+            const ShrinkSrc src{pd.w, a.x, a.ldx, th.slot, jb, jload, j0, n_oct, ptb, pcache, cached};
+            ShrinkHalf<NR, RJ> ha = load_half<PAGED, NR, RJ>(src, rows, tid), hb;
+            for (int h = 0; h < n_half; h += 2) {
+                hb = load_half<PAGED, NR, RJ>(src, rows, tid + kThreads * (h + 1));
+                const bool run = tid + kThreads * h < n_oct;  // first octet of the pair exists
+                if (run) {
 #pragma unroll
-                for (int q = 0; q < NR; ++q) {
-                    const uint16_t *xr = a.x + (int64_t)(rows[q] < 0 ? 0 : rows[q]) * a.ldx;
-                    xv[q] = rows[q] >= 0 ? load16(xr + 8 * o) : z4;
-                    xw[q] = (rows[q] >= 0 && in2) ? load16(xr + 8 * o2) : z4;
+                    for (int q = 0; q < NR; ++q)
+#pragma unroll
+                        for (int jj = 0; jj < RJ; ++jj) acc[q][jj] = dot8(ha.x[q], ha.a[jj], acc[q][jj]);
                 }
+                if (h + 2 < n_half) ha = load_half<PAGED, NR, RJ>(src, rows, tid + kThreads * (h + 2));
+                if (run) {
 #pragma unroll
-                for (int jj = 0; jj < RJ; ++jj) {
-                    av[jj] = aw[jj] = z4;
-                    const int j = jb + jj;
-                    if (j >= jload) continue;
-                    if (!PAGED) {
-                        const uint16_t *r = dense_row<false>(pd.w, th.slot, j);
-                        av[jj] = load16(r + 8 * o);
-                        if (in2) aw[jj] = load16(r + 8 * o2);
-                    } else {
-                        const uint16_t *p = a_paged(pd.w, pcache, cached, ptb, j0, j, 8 * o);
-                        if (p) av[jj] = load16(p);
-                        if (in2) {
-                            const uint16_t *p2 = a_paged(pd.w, pcache, cached, ptb, j0, j, 8 * o2);
-                            if (p2) aw[jj] = load16(p2);
-                        }
-                    }
+                    for (int q = 0; q < NR; ++q)
+#pragma unroll
+                        for (int jj = 0; jj < RJ; ++jj) acc[q][jj] = dot8(hb.x[q], hb.a[jj], acc[q][jj]);
                 }
-#pragma unroll
-                for (int q = 0; q < NR; ++q)
-#pragma unroll
-                    for (int jj = 0; jj < RJ; ++jj) acc[q][jj] = dot8(xw[q], aw[jj], dot8(xv[q], av[jj], acc[q][jj]));
             }
 #pragma unroll
             for (int q = 0; q < NR; ++q)
@@ -333,9 +364,12 @@ __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
             __syncthreads();
             if (tid < NR * RJ && rank > 0) {
                 const int q = tid / RJ, jj = tid - q * RJ, j = jb + jj;
+                int row = rows[0];  // rows[q] without a dynamically indexed register array
+#pragma unroll
+                for (int qq = 1; qq < NR; ++qq) row = q == qq ? rows[qq] : row;
                 // wavefront order: the same sum for every launch of this shape
                 const float s = red[tid] + red[NR * RJ + tid] + red[2 * NR * RJ + tid] + red[3 * NR * RJ + tid];
-                if (rows[q] >= 0 && j < jend) pd.v[(int64_t)rows[q] * pd.ldv + j] = j < rank ? s : 0.f;
+                if (row >= 0 && j < jend) pd.v[(int64_t)row * pd.ldv + j] = j < rank ? s : 0.f;
             }
             __syncthreads();
         }
@@ -343,34 +377,52 @@ __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
 }
 
 // MFMA shrink for tiles of up to 64 rows: v_mfma_f32_16x16x32_f16 over (16-row
-// slices) x (ranks j0 .. j0+15).  16 wavefronts take interleaved 32-wide k-steps,
-// 8 / MTX of them in flight each, and their sums are added in LDS in wavefront order.
-template <bool PAGED, int MTX>
+// slices) x (16-rank slices).  A workgroup takes NS consecutive rank slices of the
+// launch's slice list (projection by projection), so the projections of one launch
+// share each read of the tile's x rows.  16 wavefronts take interleaved 32-wide
+// k-steps, U of them in flight each, and their sums are added in LDS in wavefront
+// order, one rank slice at a time.  Neither NS nor MTX changes the order in which any
+// element is summed, so every split gives the same bits.
+template <bool PAGED, int MTX, int NS>
 __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Args a)
 {
     constexpr int W = kMfmaShrinkThreads / 64;
-    constexpr int U = 8 / MTX;  // k-steps in flight per wavefront
+    // k-steps in flight per wavefront: ~16 loads, or one step when the accumulators are large
+    constexpr int U = MTX * NS >= 12 ? 1 : 16 / (MTX + NS);
     __shared__ float red[W * 1024];
     __shared__ int pcache[PAGED ? kPageCache : 1];
-    const Item it = work(a);
-    if (!it.ok) return;
-    const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
-    const int j0 = it.slice * 16;
-    if (j0 >= pd.w.r_max) return;
-    const TileHead th = tile_head<false>(a.ts, pd.w, it.tile);
-    if (!th.valid) return;
-    const int rank = slot_rank(pd.w, th.slot);
+    const int wi = work_item(blockIdx.x, a.grid);
+    const int groups = (a.per_tile + NS - 1) / NS;
+    const int tile = wi / groups, g0 = (wi - tile * groups) * NS;
+    if (tile >= a.n_tiles) return;
+    const TileHead th = tile_head<false>(a.ts, a.p[0].w, tile);
+    if (th.slot < 0 || th.nrows <= 0) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;       // operand row/col, k-group of the lane
     const int MT = min((th.nrows + 15) >> 4, MTX);
-    const int jcol = j0 + li;                        // this lane's rank column (B operand)
-    const bool jload = jcol < (PAGED ? rank : pd.w.r_max);
+    // this workgroup's rank slices: projection, first rank-row, this lane's A^T rank-row
+    int sp[NS], sj0[NS], srank[NS];
+    const uint16_t *arow[NS];
+    bool sok[NS];
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+        const int sl = g0 + q;
+        sp[q] = proj_of(a, min(sl, a.per_tile - 1));
+        sj0[q] = 16 * (sl - a.off[sp[q]]);
+        const WeightsDev &w = a.p[sp[q]].w;
+        sok[q] = sl < a.per_tile && th.slot < w.num_slots && sj0[q] < w.r_max;
+        srank[q] = sok[q] ? slot_rank(w, th.slot) : 0;
+        const int jcol = sj0[q] + li;
+        arow[q] = (!PAGED && sok[q] && jcol < w.r_max) ? dense_row<false>(w, th.slot, jcol) : nullptr;
+    }
+    // paged weights: one rank slice per workgroup (NS == 1), its descriptor by value
+    const WeightsDev w0 = a.p[sp[0]].w;
     bool cached = false;
     int64_t ptb = 0;
     if (PAGED) {
-        ptb = pt_base<false>(pd.w, th.slot);
-        const int j1 = min(j0 + 16, rank);
-        if (j0 < j1) cached = cache_a_pages<kMfmaShrinkThreads>(pd.w, th.slot, j0, j1, pcache);
+        ptb = sok[0] ? pt_base<false>(w0, th.slot) : 0;
+        const int j1 = min(sj0[0] + 16, srank[0]);
+        if (sok[0] && sj0[0] < j1) cached = cache_a_pages<kMfmaShrinkThreads>(w0, th.slot, sj0[0], j1, pcache);
     }
     int xrow[MTX];
 #pragma unroll
@@ -378,25 +430,29 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Ar
         const int rr = 16 * mt + li;
         xrow[mt] = (mt < MT && rr < th.nrows) ? row_of<false>(a.ts, th.pos0 + rr, a.n_rows) : -1;
     }
-    f4_t acc[MTX];
+    f4_t acc[NS][MTX];
 #pragma unroll
-    for (int mt = 0; mt < MTX; ++mt) acc[mt] = f4_t{0.f, 0.f, 0.f, 0.f};
-    const int d_in = pd.w.d_in;
+    for (int q = 0; q < NS; ++q)
+#pragma unroll
+        for (int mt = 0; mt < MTX; ++mt) acc[q][mt] = f4_t{0.f, 0.f, 0.f, 0.f};
+    const int d_in = a.p[0].w.d_in;
     const int steps = (d_in + 31) >> 5;
     const uint4 z4 = make_uint4(0, 0, 0, 0);
     for (int s0 = wave; s0 < steps; s0 += W * U) {
-        uint4 bq[U], xq[U][MTX];
+        uint4 bq[U][NS], xq[U][MTX];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int k = 32 * (s0 + W * u) + 8 * lg;
             const bool kin = k < d_in;
-            bq[u] = z4;
-            if (kin && jload) {
+#pragma unroll
+            for (int q = 0; q < NS; ++q) {
+                bq[u][q] = z4;
+                if (!kin) continue;
                 if (!PAGED) {
-                    bq[u] = load16(dense_row<false>(pd.w, th.slot, jcol) + k);
-                } else {
-                    const uint16_t *p = a_paged(pd.w, pcache, cached, ptb, j0, jcol, k);
-                    if (p) bq[u] = load16(p);
+                    if (arow[q]) bq[u][q] = load16(arow[q] + k);
+                } else if (sok[q] && sj0[q] + li < srank[q]) {
+                    const uint16_t *p = a_paged(w0, pcache, cached, ptb, sj0[q], sj0[q] + li, k);
+                    if (p) bq[u][q] = load16(p);
                 }
             }
 #pragma unroll
@@ -404,291 +460,43 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Ar
                 xq[u][mt] = (kin && xrow[mt] >= 0) ? load16(a.x + (int64_t)xrow[mt] * a.ldx + k) : z4;
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const h8_t bop = __builtin_bit_cast(h8_t, bq[u]);
+        for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int mt = 0; mt < MTX; ++mt)
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xq[u][mt]), bop, acc[mt], 0,
-                                                                 0, 0);
-        }
+            for (int q = 0; q < NS; ++q) {
+                const h8_t bop = __builtin_bit_cast(h8_t, bq[u][q]);
+#pragma unroll
+                for (int mt = 0; mt < MTX; ++mt)
+                    acc[q][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xq[u][mt]), bop,
+                                                                        acc[q][mt], 0, 0, 0);
+            }
     }
     // D layout: lane holds rows 4*lg + e of the slice, rank column li.
 #pragma unroll
-    for (int mt = 0; mt < MTX; ++mt)
+    for (int q = 0; q < NS; ++q) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[wave * 1024 + mt * 256 + (4 * lg + e) * 16 + li] = acc[mt][e];
-    __syncthreads();
-    if (rank <= 0) return;
-    for (int o = tid; o < MT * 256; o += kMfmaShrinkThreads) {
-        const int mt = o >> 8, i = (o >> 4) & 15, j = o & 15;
-        const int rr = 16 * mt + i, col = j0 + j;
-        if (rr >= th.nrows || col >= pd.w.r_max) continue;
-        const int row = row_of<false>(a.ts, th.pos0 + rr, a.n_rows);
-        if (row < 0) continue;
-        float s = 0.f;
+        for (int mt = 0; mt < MTX; ++mt)
 #pragma unroll
-        for (int w = 0; w < W; ++w) s += red[w * 1024 + o];
-        pd.v[(int64_t)row * pd.ldv + col] = col < rank ? s : 0.f;
+            for (int e = 0; e < 4; ++e) red[wave * 1024 + mt * 256 + (4 * lg + e) * 16 + li] = acc[q][mt][e];
+        __syncthreads();
+        if (sok[q] && srank[q] > 0) {
+            const ProjDev &pd = a.p[sp[q]];
+            for (int o = tid; o < MT * 256; o += kMfmaShrinkThreads) {
+                const int mt = o >> 8, i = (o >> 4) & 15, j = o & 15;
+                const int rr = 16 * mt + i, col = sj0[q] + j;
+                if (rr >= th.nrows || col >= pd.w.r_max) continue;
+                const int row = row_of<false>(a.ts, th.pos0 + rr, a.n_rows);
+                if (row < 0) continue;
+                float s = 0.f;
+#pragma unroll
+                for (int w = 0; w < W; ++w) s += red[w * 1024 + o];
+                pd.v[(int64_t)row * pd.ldv + col] = col < srank[q] ? s : 0.f;
+            }
+        }
+        __syncthreads();
     }
 }
 
 // ------------------------------------------------------------------------ expand
-// VALU expand.  Workgroup = one tile x 512 columns; wavefront w holds rank-rows
-// w, w+4, ... of B (loaded once, all in flight); NR rows per pass; the four partial
-// sums are added in LDS and wavefront q updates row q of the pass.
-template <bool PERROW, int NR>
-struct ExpandPass {
-    int rows[NR];
-    float sv[NR];  // lane j holds v[row][j]
-    int my_row;    // row this wavefront updates
-    uint4 yv;      // its y octet
-
-    __device__ void load(const Args &a, const ProjDev &pd, const TileHead &th, int rg, int c, bool cin)
-    {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-        for (int q = 0; q < NR; ++q)
-            rows[q] = (rg + q < th.nrows) ? row_of<PERROW>(a.ts, th.pos0 + rg + q, a.n_rows) : -1;
-        my_row = (wave < NR && rg + wave < th.nrows) ? row_of<PERROW>(a.ts, th.pos0 + rg + wave, a.n_rows) : -1;
-#pragma unroll
-        for (int q = 0; q < NR; ++q)
-            sv[q] = (rows[q] >= 0 && lane < pd.w.r_max) ? pd.v[(int64_t)rows[q] * pd.ldv + lane] : 0.f;
-        yv = make_uint4(0, 0, 0, 0);
-        if (my_row >= 0 && cin) yv = load16(pd.y + (int64_t)my_row * pd.ldy + c);
-    }
-};
-
-template <bool PAGED, bool PERROW, int NR>
-__global__ __launch_bounds__(kThreads) void lora_expand_valu_kernel(Args a)
-{
-    __shared__ float red[kWaves * NR * 8 * 64];
-    const Item it = work(a);
-    if (!it.ok) return;
-    const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
-    const TileHead th = tile_head<PERROW>(a.ts, pd.w, it.tile);
-    if (!th.valid) return;
-    const int rank = slot_rank(pd.w, th.slot);
-    const int jlim = PAGED ? rank : pd.w.r_max;
-    const float sc = pd.w.scale[th.slot];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = it.slice * kCols + 8 * lane;
-    const bool cin = c < pd.w.d_out;
-    // the first pass's rows, v and y first: their loads are not queued behind B's
-    ExpandPass<PERROW, NR> ps;
-    ps.load(a, pd, th, 0, c, cin);
-    uint4 bv[kMaxRankPerWave];
-    if (!PAGED) {
-#pragma unroll
-        for (int u = 0; u < kMaxRankPerWave; ++u) {
-            const int j = wave + kWaves * u;
-            bv[u] = make_uint4(0, 0, 0, 0);
-            if (cin && j < jlim) bv[u] = load16(dense_row<true>(pd.w, th.slot, j) + c);
-        }
-    } else {
-        // page ids of all this wavefront's rank-rows, then all the data
-        const int P = pd.w.page_elems, q = c / P, within = c - q * P;
-        const int64_t ptb = pt_base<true>(pd.w, th.slot);
-        int pg[kMaxRankPerWave];
-#pragma unroll
-        for (int u = 0; u < kMaxRankPerWave; ++u) {
-            const int j = wave + kWaves * u;
-            pg[u] = (cin && j < jlim) ? page_entry<true>(pd.w, ptb, j, q) : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < kMaxRankPerWave; ++u) {
-            bv[u] = make_uint4(0, 0, 0, 0);
-            const int g = page_ok(pd.w, pg[u]);
-            if (g >= 0) bv[u] = load16(page_ptr(pd.w, g, within));
-        }
-    }
-    for (int rg = 0; rg < th.nrows; rg += NR) {
-        if (rg > 0) ps.load(a, pd, th, rg, c, cin);
-        float sv[NR];
-#pragma unroll
-        for (int q = 0; q < NR; ++q) sv[q] = lane < rank ? sc * ps.sv[q] : 0.f;
-        float acc[NR][8];
-#pragma unroll
-        for (int q = 0; q < NR; ++q)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
-#pragma unroll
-        for (int u = 0; u < kMaxRankPerWave; ++u) {
-            const int j = wave + kWaves * u;
-            if (j >= rank) break;
-            const uint32_t bw[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
-            float bf[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bf[2 * e] = h2f((uint16_t)(bw[e] & 0xffff));
-                bf[2 * e + 1] = h2f((uint16_t)(bw[e] >> 16));
-            }
-#pragma unroll
-            for (int q = 0; q < NR; ++q) {
-                const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv[q]), j));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[q][e] = __builtin_fmaf(s, bf[e], acc[q][e]);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < NR; ++q)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) red[((wave * NR + q) * 8 + e) * 64 + lane] = acc[q][e];
-        __syncthreads();
-        if (ps.my_row >= 0 && cin && rank > 0) {
-            const int q = wave;
-            const uint32_t yw[4] = {ps.yv.x, ps.yv.y, ps.yv.z, ps.yv.w};
-            uint32_t out[4];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                float d[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int e = 2 * e2 + h;
-                    d[h] = red[((0 * NR + q) * 8 + e) * 64 + lane] + red[((1 * NR + q) * 8 + e) * 64 + lane] +
-                           red[((2 * NR + q) * 8 + e) * 64 + lane] + red[((3 * NR + q) * 8 + e) * 64 + lane];
-                }
-                const float lo = h2f((uint16_t)(yw[e2] & 0xffff)) + d[0];
-                const float hi = h2f((uint16_t)(yw[e2] >> 16)) + d[1];
-                out[e2] = (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
-            }
-            *reinterpret_cast<uint4 *>(pd.y + (int64_t)ps.my_row * pd.ldy + c) =
-                make_uint4(out[0], out[1], out[2], out[3]);
-        }
-        __syncthreads();
-    }
-}
-
-// MFMA expand for tiles of up to 64 rows.  B[0:r][512 columns] is staged in LDS
-// (rank-row k at a column rotation of 8 * ((k >> 2) & 3) halves, so the 4 k-groups of
-// a wavefront read different banks); per 16-row slice D^T[cols][rows] = B^T (s v)^T
-// runs with s*v split into fp16 hi + lo/2048 operands; the accumulator starts from y.
-template <bool PAGED, int RQ>
-__global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args a)
-{
-    constexpr int kStage = RQ * 16 * (kCols / 8) / kThreads;  // 16-byte loads per lane to stage B
-    extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t *lds_b = reinterpret_cast<uint16_t *>(smem);
-    const Item it = work(a);
-    if (!it.ok) return;
-    const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
-    const TileHead th = tile_head<false>(a.ts, pd.w, it.tile);
-    if (!th.valid) return;
-    const int rank = slot_rank(pd.w, th.slot);
-    const float sc = pd.w.scale[th.slot];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int li = lane & 15, lg = lane >> 4;
-    const int c0 = it.slice * kCols;
-    const int cw = c0 + 128 * wave;  // this wavefront's 128 columns = 8 slices of 16
-    const int MT = (th.nrows + 15) >> 4;
-    const int rstage = PAGED ? ((rank + 15) & ~15) : ((pd.w.r_max + 15) & ~15);
-    for (int mt = 0; mt < MT; ++mt) {
-        const int rr = 16 * mt + li;
-        const int row = rr < th.nrows ? row_of<false>(a.ts, th.pos0 + rr, a.n_rows) : -1;
-        // y (accumulator start) and v for this slice: lane holds y[row][cw + 16 nt + 4 lg .. +3];
-        // every load is issued before any of them is used
-        uint2 yq[8];
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const int col = cw + 16 * nt + 4 * lg;
-            yq[nt] = make_uint2(0, 0);
-            if (row >= 0 && col < pd.w.d_out) yq[nt] = *reinterpret_cast<const uint2 *>(pd.y + (int64_t)row * pd.ldy + col);
-        }
-        float4 vq[RQ];
-#pragma unroll
-        for (int kq = 0; kq < RQ; ++kq) {
-            const int j = 16 * kq + 4 * lg;
-            vq[kq] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (row >= 0 && j < pd.w.r_max) vq[kq] = *reinterpret_cast<const float4 *>(pd.v + (int64_t)row * pd.ldv + j);
-        }
-        if (mt == 0) {
-            // stage B while the y and v loads are in flight: all loads first, then LDS;
-            // rows past the rank become 0, rows past r_max (dense) are not read
-            uint4 q[kStage];
-            if (!PAGED) {
-#pragma unroll
-                for (int i = 0; i < kStage; ++i) {
-                    const int o = tid + i * kThreads, k = o >> 6, oc = (o & 63) * 8;
-                    q[i] = make_uint4(0, 0, 0, 0);
-                    if (k < pd.w.r_max && c0 + oc < pd.w.d_out) q[i] = load16(dense_row<true>(pd.w, th.slot, k) + c0 + oc);
-                }
-            } else {
-                // page ids first, then all the data
-                const int64_t ptb = pt_base<true>(pd.w, th.slot);
-                const int P = pd.w.page_elems;
-                int pg[kStage];
-#pragma unroll
-                for (int i = 0; i < kStage; ++i) {
-                    const int o = tid + i * kThreads, k = o >> 6, c = c0 + (o & 63) * 8;
-                    pg[i] = (k < rank && c < pd.w.d_out) ? page_entry<true>(pd.w, ptb, k, c / P) : -1;
-                }
-#pragma unroll
-                for (int i = 0; i < kStage; ++i) {
-                    const int o = tid + i * kThreads, c = c0 + (o & 63) * 8;
-                    q[i] = make_uint4(0, 0, 0, 0);
-                    const int g = page_ok(pd.w, pg[i]);
-                    if (g >= 0) q[i] = load16(page_ptr(pd.w, g, c % P));
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < kStage; ++i) {
-                const int o = tid + i * kThreads, k = o >> 6, oc = (o & 63) * 8;
-                if (k >= rstage) continue;
-                const int pc = (oc + 8 * ((k >> 2) & 3)) & (kCols - 1);
-                *reinterpret_cast<uint4 *>(lds_b + k * kBStride + pc) = k < rank ? q[i] : make_uint4(0, 0, 0, 0);
-            }
-            __syncthreads();
-            if (rank <= 0) return;
-        }
-        f4_t acc[8];
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-            acc[nt] = f4_t{h2f((uint16_t)(yq[nt].x & 0xffff)), h2f((uint16_t)(yq[nt].x >> 16)),
-                           h2f((uint16_t)(yq[nt].y & 0xffff)), h2f((uint16_t)(yq[nt].y >> 16))};
-#pragma unroll
-        for (int kq = 0; kq < RQ; ++kq) {
-            if (16 * kq >= rank) break;
-            const int j = 16 * kq + 4 * lg;
-            const float sv[4] = {vq[kq].x, vq[kq].y, vq[kq].z, vq[kq].w};
-            h4_t vhi, vlo;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float m = (j + e < rank) ? sc * sv[e] : 0.f;
-                const _Float16 h = (_Float16)m;
-                vhi[e] = h;
-                vlo[e] = (_Float16)((m - (float)h) * 2048.f);
-            }
-#pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
-                // A operand: B^T, lane holds column cw + 16 nt + li, ranks j .. j+3
-                const int lc = 128 * wave + 16 * nt + li;
-                h4_t bop;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int k = j + e;
-                    const int pc = (lc + 8 * ((k >> 2) & 3)) & (kCols - 1);
-                    bop[e] = __builtin_bit_cast(_Float16, lds_b[k * kBStride + pc]);
-                }
-                f4_t lo = f4_t{0.f, 0.f, 0.f, 0.f};
-                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(bop, vhi, acc[nt], 0, 0, 0);
-                lo = __builtin_amdgcn_mfma_f32_16x16x16f16(bop, vlo, lo, 0, 0, 0);
-                acc[nt] += lo * (1.f / 2048.f);
-            }
-        }
-        if (row < 0) continue;
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            const int col = cw + 16 * nt + 4 * lg;
-            if (col >= pd.w.d_out) continue;
-            uint16_t o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = f2h(acc[nt][e]);
-            *reinterpret_cast<uint2 *>(pd.y + (int64_t)row * pd.ldy + col) =
-                make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
-        }
-    }
-}
-
-// ------------------------------------------------------------------------ fused (per-row form)
 // Rank-rows j = w + 4 u, u0 <= u < u0 + RU, that wavefront w of a 256-lane group loads
 // for its 8 columns at c: B[slot][j][c .. c+7], zero where j >= jlim or the columns
 // are out of range.  Paged
@@ -721,6 +529,285 @@ __device__ inline void load_b_octets(const WeightsDev &w, int slot, int jlim, in
     }
 }
 
+// VALU expand.  Workgroup = one tile x 512 columns; wavefront w holds rank-rows
+// w, w+4, ... of B (loaded once, all in flight); NR rows per pass; the four partial
+// sums are added in LDS and wavefront q updates row q of the pass.
+template <bool PERROW, int NR>
+struct ExpandPass {
+    int rows[NR];
+    float sv[NR];  // lane j holds v[row][j]
+    int my_row;    // row this wavefront updates
+
+    __device__ void load(const Args &a, const ProjDev &pd, const TileHead &th, int rg)
+    {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int q = 0; q < NR; ++q)
+            rows[q] = (rg + q < th.nrows) ? row_of<PERROW>(a.ts, th.pos0 + rg + q, a.n_rows) : -1;
+        my_row = (wave < NR && rg + wave < th.nrows) ? row_of<PERROW>(a.ts, th.pos0 + rg + wave, a.n_rows) : -1;
+#pragma unroll
+        for (int q = 0; q < NR; ++q)
+            sv[q] = (rows[q] >= 0 && lane < pd.w.r_max) ? pd.v[(int64_t)rows[q] * pd.ldv + lane] : 0.f;
+    }
+
+    __device__ uint4 load_y(const ProjDev &pd, int c, bool cin) const
+    {
+        return (my_row >= 0 && cin) ? load16(pd.y + (int64_t)my_row * pd.ldy + c) : make_uint4(0, 0, 0, 0);
+    }
+};
+
+// One pass of the VALU expand on one chunk: y rows of `ps` at columns c .. c+7 of each
+// lane += scale v B, with the rank-rows of B in bv (wavefront w: j = w + 4 u).
+template <bool PERROW, int NR, int RU>
+__device__ inline void expand_pass(const ProjDev &pd, const ExpandPass<PERROW, NR> &ps, float sc, int rank,
+                                   const uint4 *bv, uint4 yv, int c, bool cin, float *red)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float sv[NR];
+#pragma unroll
+    for (int q = 0; q < NR; ++q) sv[q] = lane < rank ? sc * ps.sv[q] : 0.f;
+    float acc[NR][8];
+#pragma unroll
+    for (int q = 0; q < NR; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[q][e] = 0.f;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+        const int j = wave + kWaves * u;
+        if (j >= rank) break;
+        const uint32_t bw[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
+        float bf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            bf[2 * e] = h2f((uint16_t)(bw[e] & 0xffff));
+            bf[2 * e + 1] = h2f((uint16_t)(bw[e] >> 16));
+        }
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+            const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv[q]), j));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[q][e] = __builtin_fmaf(s, bf[e], acc[q][e]);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < NR; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[((wave * NR + q) * 8 + e) * 64 + lane] = acc[q][e];
+    __syncthreads();
+    if (ps.my_row >= 0 && cin && rank > 0) {
+        const int q = wave;
+        const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w};
+        uint32_t out[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            float d[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int e = 2 * e2 + h;
+                d[h] = red[((0 * NR + q) * 8 + e) * 64 + lane] + red[((1 * NR + q) * 8 + e) * 64 + lane] +
+                       red[((2 * NR + q) * 8 + e) * 64 + lane] + red[((3 * NR + q) * 8 + e) * 64 + lane];
+            }
+            const float lo = h2f((uint16_t)(yw[e2] & 0xffff)) + d[0];
+            const float hi = h2f((uint16_t)(yw[e2] >> 16)) + d[1];
+            out[e2] = (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
+        }
+        *reinterpret_cast<uint4 *>(pd.y + (int64_t)ps.my_row * pd.ldy + c) = make_uint4(out[0], out[1], out[2], out[3]);
+    }
+    __syncthreads();
+}
+
+template <bool PAGED, bool PERROW, int NR, int RU>
+__global__ __launch_bounds__(kThreads) void lora_expand_valu_kernel(Args a)
+{
+    __shared__ float red[kWaves * NR * 8 * 64];
+    const Item it = work(a);
+    if (!it.ok) return;
+    const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
+    const TileHead th = tile_head<PERROW>(a.ts, pd.w, it.tile);
+    if (!th.valid) return;
+    const int rank = slot_rank(pd.w, th.slot);
+    const int jlim = PAGED ? rank : pd.w.r_max;
+    const float sc = pd.w.scale[th.slot];
+    const int c = it.slice * kCols + 8 * (threadIdx.x & 63), wave = threadIdx.x >> 6;
+    const bool cin = c < pd.w.d_out;
+    // the first pass's rows, v and y first: their loads are not queued behind B's
+    ExpandPass<PERROW, NR> ps;
+    ps.load(a, pd, th, 0);
+    uint4 yv = ps.load_y(pd, c, cin);
+    uint4 bv[RU];
+    load_b_octets<PAGED, RU>(pd.w, th.slot, jlim, wave, 0, c, cin, bv);
+    for (int rg = 0; rg < th.nrows; rg += NR) {
+        if (rg > 0) {
+            ps.load(a, pd, th, rg);
+            yv = ps.load_y(pd, c, cin);
+        }
+        expand_pass<PERROW, NR, RU>(pd, ps, sc, rank, bv, yv, c, cin, red);
+    }
+}
+
+// MFMA expand for tiles of up to 64 rows.  B[0:r][512 columns] is staged in LDS
+// transposed, column-major with a padded stride (kBtPad), so the 4 consecutive ranks a
+// lane feeds to an MFMA are one 8-byte LDS read.  Per 16-row slice D^T[cols][rows] =
+// B^T (s v)^T runs with s*v split into fp16 hi + lo/2048 operands (two MFMAs, ~22
+// bits kept) and the accumulator starts from y.  MFMAs go in pairs whose output
+// columns are interleaved so that each lane ends up with 8 consecutive columns of one
+// row: y is read and written with 16-byte accesses.  The next slice's y and v are
+// requested before the current slice's products.
+constexpr int kBtPad = 4;  // halves of padding per column of the transposed B chunk
+
+__host__ __device__ constexpr int bt_stride(int rq) { return 16 * rq + kBtPad; }
+
+template <bool PAGED, int RQ>
+__global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args a)
+{
+    constexpr int kStage = RQ * 16 * (kCols / 8) / kThreads;  // 16-byte loads per lane to stage B
+    constexpr int KS = bt_stride(RQ);
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t *bt = reinterpret_cast<uint16_t *>(smem);  // bt[col * KS + k] = B[k][c0 + col]
+    const Item it = work(a);
+    if (!it.ok) return;
+    const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
+    const TileHead th = tile_head<false>(a.ts, pd.w, it.tile);
+    if (!th.valid) return;
+    const int rank = slot_rank(pd.w, th.slot);
+    const float sc = pd.w.scale[th.slot];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int c0 = it.slice * kCols;
+    const int cw = c0 + 128 * wave;  // this wavefront's 128 columns = 4 pairs of 16x16 products
+    const int MT = (th.nrows + 15) >> 4;
+    // Row, y (accumulator start) and v of 16-row slice mt: lane holds y[row][cw + 32 p +
+    // 8 lg .. +7] for pair p and v[row][16 kq + 4 lg .. +3].
+    auto slice_row = [&](int mt) {
+        const int rr = 16 * mt + li;
+        return (mt < MT && rr < th.nrows) ? row_of<false>(a.ts, th.pos0 + rr, a.n_rows) : -1;
+    };
+    auto load_yv = [&](int row, uint4 (&yq)[4], float4 (&vq)[RQ]) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int col = cw + 32 * p + 8 * lg;
+            yq[p] = (row >= 0 && col < pd.w.d_out) ? load16(pd.y + (int64_t)row * pd.ldy + col) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int kq = 0; kq < RQ; ++kq) {
+            const int j = 16 * kq + 4 * lg;
+            vq[kq] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (row >= 0 && j < pd.w.r_max) vq[kq] = *reinterpret_cast<const float4 *>(pd.v + (int64_t)row * pd.ldv + j);
+        }
+    };
+    int row = slice_row(0);
+    uint4 yq[4];
+    float4 vq[RQ];
+    load_yv(row, yq, vq);
+    {
+        // stage B while the y and v loads are in flight: all loads first, then LDS;
+        // rows past the rank become 0, rows past r_max (dense) are not read
+        uint4 q[kStage];
+        if (!PAGED) {
+#pragma unroll
+            for (int i = 0; i < kStage; ++i) {
+                const int o = tid + i * kThreads, k = o >> 6, oc = (o & 63) * 8;
+                q[i] = make_uint4(0, 0, 0, 0);
+                if (k < pd.w.r_max && k < rank && c0 + oc < pd.w.d_out) q[i] = load16(dense_row<true>(pd.w, th.slot, k) + c0 + oc);
+            }
+        } else {
+            // page ids first, then all the data
+            const int64_t ptb = pt_base<true>(pd.w, th.slot);
+            const int P = pd.w.page_elems;
+            int pg[kStage];
+#pragma unroll
+            for (int i = 0; i < kStage; ++i) {
+                const int o = tid + i * kThreads, k = o >> 6, c = c0 + (o & 63) * 8;
+                pg[i] = (k < rank && c < pd.w.d_out) ? page_entry<true>(pd.w, ptb, k, c / P) : -1;
+            }
+#pragma unroll
+            for (int i = 0; i < kStage; ++i) {
+                const int o = tid + i * kThreads, c = c0 + (o & 63) * 8;
+                q[i] = make_uint4(0, 0, 0, 0);
+                const int g = page_ok(pd.w, pg[i]);
+                if (g >= 0) q[i] = load16(page_ptr(pd.w, g, c % P));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int o = tid + i * kThreads, k = o >> 6, oc = (o & 63) * 8;
+            const uint32_t w4[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bt[(oc + 2 * e) * KS + k] = (uint16_t)(w4[e] & 0xffff);
+                bt[(oc + 2 * e + 1) * KS + k] = (uint16_t)(w4[e] >> 16);
+            }
+        }
+        __syncthreads();
+        if (rank <= 0) return;
+    }
+    for (int mt = 0; mt < MT; ++mt) {
+        // the next slice's loads go out before this slice's products
+        const int row_n = slice_row(mt + 1);
+        uint4 yn[4];
+        float4 vn[RQ];
+        if (mt + 1 < MT) load_yv(row_n, yn, vn);
+        f4_t acc[4][2];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t yw[4] = {yq[p].x, yq[p].y, yq[p].z, yq[p].w};
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                acc[p][h] = f4_t{h2f((uint16_t)(yw[2 * h] & 0xffff)), h2f((uint16_t)(yw[2 * h] >> 16)),
+                                 h2f((uint16_t)(yw[2 * h + 1] & 0xffff)), h2f((uint16_t)(yw[2 * h + 1] >> 16))};
+        }
+#pragma unroll
+        for (int kq = 0; kq < RQ; ++kq) {
+            if (16 * kq >= rank) break;
+            const int j = 16 * kq + 4 * lg;
+            const float sv[4] = {vq[kq].x, vq[kq].y, vq[kq].z, vq[kq].w};
+            h4_t vhi, vlo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float m = (j + e < rank) ? sc * sv[e] : 0.f;
+                const _Float16 hv = (_Float16)m;
+                vhi[e] = hv;
+                vlo[e] = (_Float16)((m - (float)hv) * 2048.f);
+            }
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    // A operand: B^T row li of this product = column 32 p + 8 (li / 4) + 4 h + li % 4
+                    // of the wavefront's range, ranks j .. j+3 (one 8-byte LDS read)
+                    const int lc = 128 * wave + 32 * p + 8 * (li >> 2) + 4 * h + (li & 3);
+                    const h4_t bop = *reinterpret_cast<const h4_t *>(bt + lc * KS + j);
+                    f4_t lo = f4_t{0.f, 0.f, 0.f, 0.f};
+                    acc[p][h] = __builtin_amdgcn_mfma_f32_16x16x16f16(bop, vhi, acc[p][h], 0, 0, 0);
+                    lo = __builtin_amdgcn_mfma_f32_16x16x16f16(bop, vlo, lo, 0, 0, 0);
+                    acc[p][h] += lo * (1.f / 2048.f);
+                }
+        }
+        if (row >= 0) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int col = cw + 32 * p + 8 * lg;
+                if (col >= pd.w.d_out) continue;
+                uint32_t o[4];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e2 = 0; e2 < 2; ++e2)
+                        o[2 * h + e2] = (uint32_t)f2h(acc[p][h][2 * e2]) | ((uint32_t)f2h(acc[p][h][2 * e2 + 1]) << 16);
+                *reinterpret_cast<uint4 *>(pd.y + (int64_t)row * pd.ldy + col) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+        if (mt + 1 < MT) {
+            row = row_n;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) yq[p] = yn[p];
+#pragma unroll
+            for (int kq = 0; kq < RQ; ++kq) vq[kq] = vn[kq];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------ fused (per-row form)
 // Shrink and expand of the per-row form in one launch.  Workgroup = one row x one
 // projection x `gc` consecutive 512-column chunks of d_out, as four 256-lane groups.
 //   1. v of the row: each batch of 16 rank-rows gives group g rank-rows
@@ -1018,17 +1105,23 @@ int shrink_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSr
     hipStream_t s = static_cast<hipStream_t>(stream);
     constexpr int NR = PERROW ? 1 : kRowsPerPass;
     if (mfma) {
-        const int slices = (max_rows + 15) / 16;
-        if (slices <= 1) {
-            if (paged) launch(lora_shrink_mfma_kernel<true, 1>, grid, kMfmaShrinkThreads, 0, s, a);
-            else launch(lora_shrink_mfma_kernel<false, 1>, grid, kMfmaShrinkThreads, 0, s, a);
-        } else if (slices == 2) {
-            if (paged) launch(lora_shrink_mfma_kernel<true, 2>, grid, kMfmaShrinkThreads, 0, s, a);
-            else launch(lora_shrink_mfma_kernel<false, 2>, grid, kMfmaShrinkThreads, 0, s, a);
-        } else {
-            if (paged) launch(lora_shrink_mfma_kernel<true, 4>, grid, kMfmaShrinkThreads, 0, s, a);
-            else launch(lora_shrink_mfma_kernel<false, 4>, grid, kMfmaShrinkThreads, 0, s, a);
-        }
+        // rank slices per workgroup: all of the tile's (up to 4) share one read of x
+        const int ns = paged ? 1 : (a.per_tile + (a.per_tile + 3) / 4 - 1) / ((a.per_tile + 3) / 4);
+        a.grid = pad8((int64_t)n_tiles * ((a.per_tile + ns - 1) / ns));
+        const dim3 g((unsigned)a.grid);
+        const int mtx = (max_rows + 15) / 16;
+#define LORA_SHRINK_MFMA(MTX)                                                                         \
+    do {                                                                                             \
+        if (paged) launch(lora_shrink_mfma_kernel<true, MTX, 1>, g, kMfmaShrinkThreads, 0, s, a);    \
+        else if (ns == 1) launch(lora_shrink_mfma_kernel<false, MTX, 1>, g, kMfmaShrinkThreads, 0, s, a); \
+        else if (ns == 2) launch(lora_shrink_mfma_kernel<false, MTX, 2>, g, kMfmaShrinkThreads, 0, s, a); \
+        else if (ns == 3) launch(lora_shrink_mfma_kernel<false, MTX, 3>, g, kMfmaShrinkThreads, 0, s, a); \
+        else launch(lora_shrink_mfma_kernel<false, MTX, 4>, g, kMfmaShrinkThreads, 0, s, a);          \
+    } while (0)
+        if (mtx <= 1) LORA_SHRINK_MFMA(1);
+        else if (mtx == 2) LORA_SHRINK_MFMA(2);
+        else LORA_SHRINK_MFMA(4);
+#undef LORA_SHRINK_MFMA
     } else if (a.jw == 1) {
         if (paged) launch(lora_shrink_valu_kernel<true, PERROW, 1, NR>, grid, kThreads, 0, s, a);
         else launch(lora_shrink_valu_kernel<false, PERROW, 1, NR>, grid, kThreads, 0, s, a);
@@ -1053,20 +1146,18 @@ int expand_impl(void *stream, int32_t n_rows, TileSrc ts, int32_t n_tiles, int32
     if (n_rows < 0) return fail(LORA_E_SHAPE, "n_rows = %d", n_rows);
     if (n_rows == 0 || n_tiles == 0) return LORA_OK;
     int32_t r_max = 0;
-    for (int32_t p = 0; p < n_proj; ++p) {
-        a.p[p].slices = (proj[p].w->d_out + kCols - 1) / kCols;
-        r_max = std::max(r_max, proj[p].w->r_max);
-    }
+    for (int32_t p = 0; p < n_proj; ++p) r_max = std::max(r_max, proj[p].w->r_max);
+    const bool mfma = !PERROW && max_rows >= kMfmaMinRows;
+    for (int32_t p = 0; p < n_proj; ++p) a.p[p].slices = (proj[p].w->d_out + kCols - 1) / kCols;
     if ((st = finish_layout(a, n_tiles))) return st;
     a.n_rows = n_rows;
     a.n_tiles = n_tiles;
-    const bool mfma = !PERROW && max_rows >= kMfmaMinRows;
     a.ts = ts;
     const dim3 grid((unsigned)a.grid);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (mfma) {
         const int rq = (r_max + 15) / 16;
-        const size_t lds = (size_t)rq * 16 * kBStride * sizeof(uint16_t);
+        const size_t lds = (size_t)kCols * bt_stride(rq) * sizeof(uint16_t);
 #define LORA_EXPAND_MFMA(RQ)                                                        \
     (paged ? launch(lora_expand_mfma_kernel<true, RQ>, grid, kThreads, lds, s, a)   \
            : launch(lora_expand_mfma_kernel<false, RQ>, grid, kThreads, lds, s, a))
@@ -1077,8 +1168,13 @@ int expand_impl(void *stream, int32_t n_rows, TileSrc ts, int32_t n_tiles, int32
 #undef LORA_EXPAND_MFMA
     } else {
         constexpr int NR = PERROW ? 1 : kRowsPerPass;
-        if (paged) launch(lora_expand_valu_kernel<true, PERROW, NR>, grid, kThreads, 0, s, a);
-        else launch(lora_expand_valu_kernel<false, PERROW, NR>, grid, kThreads, 0, s, a);
+#define LORA_EXPAND_VALU(RU)                                                                  \
+    (paged ? launch(lora_expand_valu_kernel<true, PERROW, NR, RU>, grid, kThreads, 0, s, a)  \
+           : launch(lora_expand_valu_kernel<false, PERROW, NR, RU>, grid, kThreads, 0, s, a))
+        if (r_max <= 16) LORA_EXPAND_VALU(4);
+        else if (r_max <= 32) LORA_EXPAND_VALU(8);
+        else LORA_EXPAND_VALU(16);
+#undef LORA_EXPAND_VALU
     }
     return launch_status("expand");
 }
@@ -1147,6 +1243,8 @@ lora_proj one_proj(const lora_weights *w, float *v, int64_t ldv, void *y, int64_
 
 }  // namespace
 
+thread_local int32_t t_plan_jw = 0;
+
 int32_t plan_fused_chunks(int32_t n_rows, int32_t n_proj, const lora_proj *proj)
 {
     // Two launches.  Measured on MI355X at the Llama-2 7B and 70B decode shapes, the one-
@@ -1161,10 +1259,12 @@ int32_t plan_fused_chunks(int32_t n_rows, int32_t n_proj, const lora_proj *proj)
 
 int32_t plan_shrink_jw(int32_t work_tiles, int32_t r_max)
 {
-    // The smallest rank-row group that keeps the grid near kTargetGroups workgroups.
+    // The narrowest rank-row group (most workgroups in flight) that keeps the grid at
+    // or below kTargetGroups.  Measured on MI355X, more and shorter workgroups beat
+    // wider groups that re-read x less, and also beat longer streaming ones.
     int32_t jw = 1;
     while (jw < 4 && (int64_t)work_tiles * ((r_max + jw - 1) / jw) > kTargetGroups) jw *= 2;
-    return jw;
+    return t_plan_jw > 0 ? t_plan_jw : jw;
 }
 
 }  // namespace lora
@@ -1178,6 +1278,15 @@ int lora_set_launch_events(void *start_event, void *stop_event)
     clear_error();
     t_ev_start = static_cast<hipEvent_t>(start_event);
     t_ev_stop = static_cast<hipEvent_t>(stop_event);
+    return LORA_OK;
+}
+
+int lora_set_plan(int32_t shrink_rank_rows)
+{
+    clear_error();
+    if (shrink_rank_rows < 0 || shrink_rank_rows > LORA_MAX_RANK)
+        return fail(LORA_E_SHAPE, "shrink_rank_rows = %d outside 0..%d", shrink_rank_rows, LORA_MAX_RANK);
+    t_plan_jw = shrink_rank_rows;
     return LORA_OK;
 }
 

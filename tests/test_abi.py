@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 20 and set(names) == set(B.EXPORTS)
+    assert len(names) == 21 and set(names) == set(B.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", build_mod.LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (lora_\w+)", out))
@@ -308,8 +308,16 @@ def test_one_launch_decode_errors():
     assert call(n=0) == B.LORA_OK and call(n=0, chunks=-1) == B.LORA_OK and call(n=0, chunks=3) == B.LORA_OK
 
 
+def test_set_plan_ranges():
+    L = B.lib()
+    assert L.lora_set_plan(-1) == B.LORA_E_SHAPE
+    assert L.lora_set_plan(65) == B.LORA_E_SHAPE
+    assert L.lora_set_plan(64) == B.LORA_OK
+    assert L.lora_set_plan(0) == B.LORA_OK
+
+
 def test_pick_tile_rows():
     assert B.lora_pick_tile_rows(np.array([0, 1, 4, 6, 8], np.int32)) == 4
     assert B.lora_pick_tile_rows(np.array([0, 127, 140], np.int32)) == 4
-    assert B.lora_pick_tile_rows(np.array([0, 5, 133], np.int32)) == 16
+    assert B.lora_pick_tile_rows(np.array([0, 5, 133], np.int32)) == 64
     assert B.lora_pick_tile_rows(np.array([0], np.int32)) == 4
