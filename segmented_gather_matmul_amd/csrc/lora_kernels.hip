@@ -298,11 +298,13 @@ __device__ inline ShrinkHalf<NR, RJ> load_half(const ShrinkSrc &s, const int (&r
 // Lane l sums octets l, l + 256, l + 512, ... of d_in in that order, the octets taken
 // in pairs (o, o + 256) with a zero second term when o + 256 is past the end; then the
 // wavefront's lanes are added by an xor butterfly and the 4 wavefronts in order.  The
-// loads of the next half of a pair (256 octets) are in flight while the current half
-// is summed, so a workgroup streams its rank-rows instead of waiting once per pair.
+// loads of several halves of pairs (256 octets each, about 16 loads per lane) are
+// issued together before any is summed, so a long d_in costs few round trips.
 template <bool PAGED, bool PERROW, int RJ, int NR>
 __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
 {
+    // halves in flight together: about 16 loads per lane, an even count (whole pairs)
+    constexpr int D = (16 / (NR + RJ)) & ~1 ? (16 / (NR + RJ)) & ~1 : 2;
     __shared__ float red[kWaves * NR * RJ];
     __shared__ int pcache[PAGED ? kPageCache : 1];
     const Item it = work(a);
@@ -336,22 +338,22 @@ __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
 #pragma unroll
                 for (int jj = 0; jj < RJ; ++jj) acc[q][jj] = 0.f;
             const ShrinkSrc src{pd.w, a.x, a.ldx, th.slot, jb, jload, j0, n_oct, ptb, pcache, cached};
-            ShrinkHalf<NR, RJ> ha = load_half<PAGED, NR, RJ>(src, rows, tid), hb;
-            for (int h = 0; h < n_half; h += 2) {
-                hb = load_half<PAGED, NR, RJ>(src, rows, tid + kThreads * (h + 1));
-                const bool run = tid + kThreads * h < n_oct;  // first octet of the pair exists
-                if (run) {
+            // D halves (whole pairs) are requested together, then summed in order
+            for (int h0 = 0; h0 < n_half; h0 += D) {
+                ShrinkHalf<NR, RJ> hf[D];
 #pragma unroll
-                    for (int q = 0; q < NR; ++q)
+                for (int d = 0; d < D; ++d)
+                    if (d == 0 || h0 + d < n_half) hf[d] = load_half<PAGED, NR, RJ>(src, rows, tid + kThreads * (h0 + d));
 #pragma unroll
-                        for (int jj = 0; jj < RJ; ++jj) acc[q][jj] = dot8(ha.x[q], ha.a[jj], acc[q][jj]);
-                }
-                if (h + 2 < n_half) ha = load_half<PAGED, NR, RJ>(src, rows, tid + kThreads * (h + 2));
-                if (run) {
+                for (int d = 0; d < D; ++d) {
+                    // a pair runs when its first octet exists; its second term may be zero
+                    const int h = h0 + d;
+                    if (h < n_half && tid + kThreads * (h & ~1) < n_oct) {
 #pragma unroll
-                    for (int q = 0; q < NR; ++q)
+                        for (int q = 0; q < NR; ++q)
 #pragma unroll
-                        for (int jj = 0; jj < RJ; ++jj) acc[q][jj] = dot8(hb.x[q], hb.a[jj], acc[q][jj]);
+                            for (int jj = 0; jj < RJ; ++jj) acc[q][jj] = dot8(hf[d].x[q], hf[d].a[jj], acc[q][jj]);
+                    }
                 }
             }
 #pragma unroll
@@ -1167,6 +1169,8 @@ int expand_impl(void *stream, int32_t n_rows, TileSrc ts, int32_t n_tiles, int32
         else LORA_EXPAND_MFMA(4);
 #undef LORA_EXPAND_MFMA
     } else {
+        // 4 rows per pass even at 16 rank-rows per wavefront: measured faster than fewer
+        // rows at higher occupancy (B is loaded once per tile, not once per row)
         constexpr int NR = PERROW ? 1 : kRowsPerPass;
 #define LORA_EXPAND_VALU(RU)                                                                  \
     (paged ? launch(lora_expand_valu_kernel<true, PERROW, NR, RU>, grid, kThreads, 0, s, a)  \
