@@ -335,6 +335,120 @@ def cpu_baseline(spec, groups, budget_s=10.0):
 
 
 # ------------------------------------------------------------------ main
+# ------------------------------------------------------------------ operator sweep
+def sweep_assign(pop, n, seed):
+    """Row -> adapter of the pages' popularity sweep, rows grouped by adapter (segment order):
+    distinct (one adapter per row), uniform (ceil(sqrt n) adapters, uniform draw), skewed
+    (Zipf s = 1.5 over n adapters), identical (one adapter)."""
+    from segmented_gather_matmul_amd import workloads as wl
+    rng = wl.rng_for(6, 0, seed)
+    if pop == "distinct":
+        idx = wl.assign_distinct(n)
+    elif pop == "identical":
+        idx = wl.assign_identical(n)
+    elif pop == "uniform":
+        idx = wl.assign_uniform(rng, n, int(np.ceil(np.sqrt(n))))
+    else:
+        idx = wl.assign_zipf(rng, n, n, 1.5)
+    return np.sort(idx).astype(np.int32)
+
+
+def operator_sweep(args):
+    """One LoRA operator (shrink + expand, h -> r -> h) per configuration, timed for four
+    implementations on the same inputs: this library's segment form (one shrink and one
+    expand launch over contiguous segments) and per-row form, a loop over adapters (two
+    fp16 GEMMs and an add per segment) and Gather-BMM (per-row copies of A and B, then two
+    batched products).  Each implementation's L layers (distinct weights, so the adapters
+    stream from HBM) are captured in one graph and replayed; the result is us per operator.
+    The last two are plain PyTorch, timing context only."""
+    import torch
+    from segmented_gather_matmul_amd import binding as B
+    h, L, K = args.sweep_h, args.sweep_layers, args.steps
+    ns = [int(v) for v in args.sweep_batches.split(",")]
+    rs = [int(v) for v in args.sweep_ranks.split(",")]
+    pops = args.sweep_pops.split(",")
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    results = []
+    for r in rs:
+        for pop in pops:
+            for n in ns:
+                idx = sweep_assign(pop, n, n * 100 + r)
+                S = int(idx.max()) + 1
+                seg_slot, counts = np.unique(idx, return_counts=True)
+                seg_ptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+                seg_slot = seg_slot.astype(np.int32)
+                tiles = B.lora_build_tiles(seg_ptr, seg_slot)
+                segs = B.segments_to_device(tiles, None, n, dev)
+                idx_d = torch.from_numpy(idx).to(dev)
+                idx_l = idx_d.long()
+                scale = 32.0 / r
+                rank_d = torch.full((S,), r, dtype=torch.int32, device=dev)
+                scale_d = torch.full((S,), scale, dtype=torch.float32, device=dev)
+                gen.manual_seed(n * 7919 + r * 31 + len(pop))
+                rnd = lambda *sh: (torch.randn(*sh, generator=gen, device=dev, dtype=torch.float32) * 0.02).half()
+                layers = []
+                for _ in range(L):
+                    a_t, b = rnd(S, r, h), rnd(S, r, h)
+                    lay = dict(x=rnd(n, h), y=rnd(n, h), a_t=a_t, b=b, a=a_t.transpose(1, 2).contiguous(),
+                               v=torch.zeros((n, max(4, -(-r // 4) * 4)), dtype=torch.float32, device=dev))
+                    lay["w"] = B.Weights(num_slots=S, d_in=h, d_out=h, r_max=r, rank=rank_d, scale=scale_d, a_t=a_t,
+                                         b=b)
+                    layers.append(lay)
+
+                def ours_sgmv(lay, y):
+                    B.lora_sgmv_shrink(lay["v"], lay["x"], lay["w"], segs)
+                    B.lora_sgmv_expand(y, lay["v"], lay["w"], segs)
+
+                def ours_bgmv(lay, y):
+                    B.lora_bgmv(y, lay["x"], idx_d, lay["w"], lay["v"])
+
+                def loop(lay, y):
+                    for g in range(len(seg_slot)):
+                        a0, a1, s_ = int(seg_ptr[g]), int(seg_ptr[g + 1]), int(seg_slot[g])
+                        y[a0:a1].add_((lay["x"][a0:a1] @ lay["a"][s_]) @ lay["b"][s_], alpha=scale)
+
+                def gather_bmm(lay, y):
+                    ag = lay["a"].index_select(0, idx_l).contiguous()
+                    bg = lay["b"].index_select(0, idx_l).contiguous()
+                    vv = torch.bmm(lay["x"].unsqueeze(1), ag)
+                    y.add_(torch.bmm(vv, bg).squeeze(1), alpha=scale)
+
+                impls = dict(ours_sgmv=ours_sgmv, ours_bgmv=ours_bgmv, loop=loop, gather_bmm=gather_bmm)
+                rec = dict(h=h, r=r, popularity=pop, n=n, adapters=len(seg_slot))
+                # the same result from each, on a fresh copy of layer 0's y
+                outs = {}
+                for name, fn in impls.items():
+                    y = layers[0]["y"].clone()
+                    fn(layers[0], y)
+                    outs[name] = y.float()
+                torch.cuda.synchronize()
+                ref = outs["gather_bmm"]
+                rec["max_abs_vs_gather_bmm"] = {k: float((v - ref).abs().max()) for k, v in outs.items()}
+                for name, fn in impls.items():
+                    fn(layers[0], layers[0]["y"])
+                    torch.cuda.synchronize()
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        for lay in layers:
+                            fn(lay, lay["y"])
+                    for _ in range(3):
+                        g.replay()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(K):
+                        g.replay()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    rec[f"{name}_us"] = round(1e3 * e0.elapsed_time(e1) / (K * L), 3)
+                    del g
+                log(f"[sweep] r={r} {pop} n={n}: " + " ".join(f"{k}={rec[k + '_us']}" for k in impls))
+                results.append(rec)
+                del layers
+                torch.cuda.empty_cache()
+    print(json.dumps({"sweep": "operator", "h": h, "layers": L, "steps": K, "results": results}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,11 +469,19 @@ def main():
                     help="per-row form: -1 = separate shrink and expand launches (the library's choice); c >= 1 = "
                          "one launch per unit, each workgroup covering c 512-column chunks")
     ap.add_argument("--no-floors", action="store_true", help="skip the empty-launch and copy reference steps")
-    ap.add_argument("--plan", type=int, default=0, metavar="JW",
-                    help="fix rank-rows per VALU shrink workgroup (0 = library's choice; results are "
-                         "bit-identical either way)")
+    ap.add_argument("--plan", default="0,0", metavar="JW,NR",
+                    help="fix rank-rows per VALU shrink workgroup and rows per pass of the segment-form VALU "
+                         "kernels (0 = library's choice; results are bit-identical either way)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (byte-counter calibration)")
+    ap.add_argument("--sweep", choices=["operator"], default=None,
+                    help="instead of the step: time one LoRA operator across batch sizes, popularity and ranks "
+                         "against a loop over adapters and Gather-BMM")
+    ap.add_argument("--sweep-h", type=int, default=4096)
+    ap.add_argument("--sweep-layers", type=int, default=16)
+    ap.add_argument("--sweep-batches", default="1,2,4,8,16,32,64")
+    ap.add_argument("--sweep-ranks", default="8,16,32,64")
+    ap.add_argument("--sweep-pops", default="distinct,uniform,skewed,identical")
     args = ap.parse_args()
     if args.calibrate_copy:
         import torch
@@ -382,6 +504,9 @@ def main():
     B.lib()
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible")
+    if args.sweep:
+        operator_sweep(args)
+        return
     device = "cuda"
     grouped = not args.no_group
     spec = workload_spec(args.workload)
@@ -390,7 +515,7 @@ def main():
             raise SystemExit("the prefill workload is given as contiguous segments")
         spec["form"] = args.form
     layers = args.layers or spec["layers"]
-    B.lora_set_plan(args.plan)
+    B.lora_set_plan(*(int(v) for v in args.plan.split(",")))
     log(f"[bench] workload={args.workload} layers={layers} grouped={grouped} building inputs")
     groups = make_ops(spec, layers, device, args.tile_rows)
     torch.cuda.synchronize()

@@ -288,12 +288,13 @@ int lora_set_launch_events(void *start_event, void *stop_event);
 
 /*
  * Tuning hook: for the calling thread's later launches, fixes the number of rank-rows
- * each VALU shrink workgroup computes (1..64); 0 restores the library's choice.
- * Results do not depend on it, bit for bit: every element of v is summed in the same
- * order whatever the split.  Returns LORA_E_SHAPE outside 0..64.  Per-thread state,
- * like the event pair.
+ * each VALU shrink workgroup computes (1..64) and the number of rows each pass of the
+ * segment-form VALU kernels takes (1, 2 or 4); 0 restores the library's choice.
+ * Results do not depend on either, bit for bit: every element is summed in the same
+ * order whatever the split.  Returns LORA_E_SHAPE for other values.  Per-thread
+ * state, like the event pair.
  */
-int lora_set_plan(int32_t shrink_rank_rows);
+int lora_set_plan(int32_t shrink_rank_rows, int32_t rows_per_pass);
 
 const char *lora_last_error(void);   /* message of this thread's last failed call */
 const char *lora_status_str(int status);

@@ -94,7 +94,7 @@ def lib() -> ctypes.CDLL:
             "lora_bgmv_expand_multi": [P, P, I32, I32, P],
             "lora_pick_tile_rows": [P, I32],
             "lora_bgmv_multi": [P, P, I64, P, I32, I32, P, I32],
-            "lora_set_plan": [I32],
+            "lora_set_plan": [I32, I32],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -288,10 +288,11 @@ def lora_bgmv(y, x, idx, weights: Weights, v, stream=None):
                            weights.ref, _ptr(v), _ld(v)))
 
 
-def lora_set_plan(shrink_rank_rows=0):
-    """Fix (or, with 0, release) the rank-rows per VALU shrink workgroup for this
-    thread's later launches; results are bit-identical either way."""
-    _check(lib().lora_set_plan(int(shrink_rank_rows)))
+def lora_set_plan(shrink_rank_rows=0, rows_per_pass=0):
+    """Fix (or, with 0, release) the rank-rows per VALU shrink workgroup and the rows per
+    pass of the segment-form VALU kernels for this thread's later launches; results are
+    bit-identical either way."""
+    _check(lib().lora_set_plan(int(shrink_rank_rows), int(rows_per_pass)))
 
 
 def lora_set_launch_events(start_event, stop_event):

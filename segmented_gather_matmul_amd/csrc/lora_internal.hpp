@@ -22,7 +22,10 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 // projection) pairs: 1, 2 or 4, to keep the grid near kTargetGroups workgroups, unless
 // lora_set_plan fixed it for the calling thread (t_plan_jw > 0).
 int32_t plan_shrink_jw(int32_t work_tiles, int32_t r_max);
-extern thread_local int32_t t_plan_jw;
+
+// Overrides set by lora_set_plan for the calling thread: rank-rows per VALU shrink
+// workgroup and rows per pass of the segment-form VALU kernels (0 = planned).
+extern thread_local int32_t t_plan_jw, t_plan_nr;
 
 // Chunks of 512 columns per workgroup of the fused per-row launch, or -1 for two
 // launches (shrink, then expand); both give the same bits.

@@ -1077,6 +1077,38 @@ int finish_layout(Args &a, int32_t n_tiles)
     return LORA_OK;
 }
 
+// Rows per pass of the VALU kernels in the segment form: the tiles' height rounded up to
+// 1, 2 or 4 (no pass computes on rows a tile does not have), unless lora_set_plan fixed it.
+int rows_per_pass(int32_t max_rows)
+{
+    if (t_plan_nr > 0) return t_plan_nr;
+    return max_rows <= 1 ? 1 : max_rows <= 2 ? 2 : kRowsPerPass;
+}
+
+template <bool PERROW, int NR>
+void shrink_valu_launch(bool paged, int32_t jw, dim3 grid, hipStream_t s, const Args &a)
+{
+#define LORA_SHRINK_VALU(RJ)                                                                   \
+    (paged ? launch(lora_shrink_valu_kernel<true, PERROW, RJ, NR>, grid, kThreads, 0, s, a)   \
+           : launch(lora_shrink_valu_kernel<false, PERROW, RJ, NR>, grid, kThreads, 0, s, a))
+    if (jw == 1) LORA_SHRINK_VALU(1);
+    else if (jw == 2) LORA_SHRINK_VALU(2);
+    else LORA_SHRINK_VALU(4);
+#undef LORA_SHRINK_VALU
+}
+
+template <bool PERROW, int NR>
+void expand_valu_launch(bool paged, int32_t r_max, dim3 grid, hipStream_t s, const Args &a)
+{
+#define LORA_EXPAND_VALU(RU)                                                                  \
+    (paged ? launch(lora_expand_valu_kernel<true, PERROW, NR, RU>, grid, kThreads, 0, s, a)  \
+           : launch(lora_expand_valu_kernel<false, PERROW, NR, RU>, grid, kThreads, 0, s, a))
+    if (r_max <= 16) LORA_EXPAND_VALU(4);
+    else if (r_max <= 32) LORA_EXPAND_VALU(8);
+    else LORA_EXPAND_VALU(16);
+#undef LORA_EXPAND_VALU
+}
+
 template <bool PERROW>
 int shrink_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSrc ts, int32_t n_tiles,
                 int32_t max_rows, int32_t n_proj, const lora_proj *proj)
@@ -1105,7 +1137,6 @@ int shrink_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSr
     a.ts = ts;
     const dim3 grid((unsigned)a.grid);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    constexpr int NR = PERROW ? 1 : kRowsPerPass;
     if (mfma) {
         // rank slices per workgroup: all of the tile's (up to 4) share one read of x
         const int ns = paged ? 1 : (a.per_tile + (a.per_tile + 3) / 4 - 1) / ((a.per_tile + 3) / 4);
@@ -1124,15 +1155,13 @@ int shrink_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSr
         else if (mtx == 2) LORA_SHRINK_MFMA(2);
         else LORA_SHRINK_MFMA(4);
 #undef LORA_SHRINK_MFMA
-    } else if (a.jw == 1) {
-        if (paged) launch(lora_shrink_valu_kernel<true, PERROW, 1, NR>, grid, kThreads, 0, s, a);
-        else launch(lora_shrink_valu_kernel<false, PERROW, 1, NR>, grid, kThreads, 0, s, a);
-    } else if (a.jw == 2) {
-        if (paged) launch(lora_shrink_valu_kernel<true, PERROW, 2, NR>, grid, kThreads, 0, s, a);
-        else launch(lora_shrink_valu_kernel<false, PERROW, 2, NR>, grid, kThreads, 0, s, a);
+    } else if constexpr (PERROW) {
+        shrink_valu_launch<true, 1>(paged, a.jw, grid, s, a);
     } else {
-        if (paged) launch(lora_shrink_valu_kernel<true, PERROW, 4, NR>, grid, kThreads, 0, s, a);
-        else launch(lora_shrink_valu_kernel<false, PERROW, 4, NR>, grid, kThreads, 0, s, a);
+        const int nr = rows_per_pass(max_rows);
+        if (nr == 1) shrink_valu_launch<false, 1>(paged, a.jw, grid, s, a);
+        else if (nr == 2) shrink_valu_launch<false, 2>(paged, a.jw, grid, s, a);
+        else shrink_valu_launch<false, 4>(paged, a.jw, grid, s, a);
     }
     return launch_status("shrink");
 }
@@ -1168,17 +1197,13 @@ int expand_impl(void *stream, int32_t n_rows, TileSrc ts, int32_t n_tiles, int32
         else if (rq == 3) LORA_EXPAND_MFMA(3);
         else LORA_EXPAND_MFMA(4);
 #undef LORA_EXPAND_MFMA
+    } else if constexpr (PERROW) {
+        expand_valu_launch<true, 1>(paged, r_max, grid, s, a);
     } else {
-        // 4 rows per pass even at 16 rank-rows per wavefront: measured faster than fewer
-        // rows at higher occupancy (B is loaded once per tile, not once per row)
-        constexpr int NR = PERROW ? 1 : kRowsPerPass;
-#define LORA_EXPAND_VALU(RU)                                                                  \
-    (paged ? launch(lora_expand_valu_kernel<true, PERROW, NR, RU>, grid, kThreads, 0, s, a)  \
-           : launch(lora_expand_valu_kernel<false, PERROW, NR, RU>, grid, kThreads, 0, s, a))
-        if (r_max <= 16) LORA_EXPAND_VALU(4);
-        else if (r_max <= 32) LORA_EXPAND_VALU(8);
-        else LORA_EXPAND_VALU(16);
-#undef LORA_EXPAND_VALU
+        const int nr = rows_per_pass(max_rows);
+        if (nr == 1) expand_valu_launch<false, 1>(paged, r_max, grid, s, a);
+        else if (nr == 2) expand_valu_launch<false, 2>(paged, r_max, grid, s, a);
+        else expand_valu_launch<false, 4>(paged, r_max, grid, s, a);
     }
     return launch_status("expand");
 }
@@ -1247,7 +1272,7 @@ lora_proj one_proj(const lora_weights *w, float *v, int64_t ldv, void *y, int64_
 
 }  // namespace
 
-thread_local int32_t t_plan_jw = 0;
+thread_local int32_t t_plan_jw = 0, t_plan_nr = 0;
 
 int32_t plan_fused_chunks(int32_t n_rows, int32_t n_proj, const lora_proj *proj)
 {
@@ -1285,12 +1310,15 @@ int lora_set_launch_events(void *start_event, void *stop_event)
     return LORA_OK;
 }
 
-int lora_set_plan(int32_t shrink_rank_rows)
+int lora_set_plan(int32_t shrink_rank_rows, int32_t rows_per_pass)
 {
     clear_error();
     if (shrink_rank_rows < 0 || shrink_rank_rows > LORA_MAX_RANK)
         return fail(LORA_E_SHAPE, "shrink_rank_rows = %d outside 0..%d", shrink_rank_rows, LORA_MAX_RANK);
+    if (rows_per_pass != 0 && rows_per_pass != 1 && rows_per_pass != 2 && rows_per_pass != 4)
+        return fail(LORA_E_SHAPE, "rows_per_pass = %d is not 0, 1, 2 or 4", rows_per_pass);
     t_plan_jw = shrink_rank_rows;
+    t_plan_nr = rows_per_pass;
     return LORA_OK;
 }
 

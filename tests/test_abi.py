@@ -310,10 +310,12 @@ def test_one_launch_decode_errors():
 
 def test_set_plan_ranges():
     L = B.lib()
-    assert L.lora_set_plan(-1) == B.LORA_E_SHAPE
-    assert L.lora_set_plan(65) == B.LORA_E_SHAPE
-    assert L.lora_set_plan(64) == B.LORA_OK
-    assert L.lora_set_plan(0) == B.LORA_OK
+    assert L.lora_set_plan(-1, 0) == B.LORA_E_SHAPE
+    assert L.lora_set_plan(65, 0) == B.LORA_E_SHAPE
+    assert L.lora_set_plan(0, 3) == B.LORA_E_SHAPE
+    assert L.lora_set_plan(0, -1) == B.LORA_E_SHAPE
+    assert L.lora_set_plan(64, 4) == B.LORA_OK
+    assert L.lora_set_plan(0, 0) == B.LORA_OK
 
 
 def test_pick_tile_rows():

@@ -1,6 +1,6 @@
-"""GPU: the shrink's work split (rank-rows per workgroup, fixed with lora_set_plan)
-changes no bit of v or y, for both call forms, dense and paged weights, and tiles of
-1 to 64 rows."""
+"""GPU: the work split fixed with lora_set_plan (rank-rows per shrink workgroup, rows
+per pass of the segment-form VALU kernels) changes no bit of v or y, for both call
+forms, dense and paged weights, and tiles of 1 to 64 rows."""
 import numpy as np
 import pytest
 
@@ -10,7 +10,7 @@ from segmented_gather_matmul_amd import workloads as wl
 from tests import gpu_cases as G
 
 pytestmark = pytest.mark.gpu
-PLANS = [0, 1, 2, 3, 4, 8, 16, 64]
+PLANS = [(0, 0), (1, 1), (2, 2), (3, 4), (4, 1), (8, 2), (16, 4), (64, 0)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -20,7 +20,7 @@ def _gpu():
         pytest.skip("no GPU")
     B.lib()
     yield
-    B.lora_set_plan(0)
+    B.lora_set_plan(0, 0)
 
 
 def _segs(idx, S, tile_rows):
@@ -48,8 +48,8 @@ def test_plan_changes_no_bits(layout, form):
     segs = None if form == "bgmv" else _segs(idx, S, int(form[4:]))
     G.say(f"case plan layout={layout} form={form}")
     results = []
-    for jw in PLANS:
-        B.lora_set_plan(jw)
+    for jw, nr in PLANS:
+        B.lora_set_plan(jw, nr)
         for dc in dcs:
             dc.reset()
         items = [(w, dc.v, dc.y) for w, dc in zip(ws, dcs)]
@@ -60,11 +60,11 @@ def test_plan_changes_no_bits(layout, form):
             B.lora_sgmv_shrink_multi(dcs[0].x, segs, items)
             B.lora_sgmv_expand_multi(segs, items, len(idx))
         results.append([dc.results() for dc in dcs])
-    B.lora_set_plan(0)
-    for jw, res in zip(PLANS, results):
+    B.lora_set_plan(0, 0)
+    for plan, res in zip(PLANS, results):
         for p, ((yb, vb), (yg, vg)) in enumerate(zip(results[0], res)):
-            assert np.array_equal(yb.view(np.uint16), yg.view(np.uint16)), f"plan {jw} proj {p}: y"
-            assert np.array_equal(vb.view(np.uint32), vg.view(np.uint32)), f"plan {jw} proj {p}: v"
+            assert np.array_equal(yb.view(np.uint16), yg.view(np.uint16)), f"plan {plan} proj {p}: y"
+            assert np.array_equal(vb.view(np.uint32), vg.view(np.uint32)), f"plan {plan} proj {p}: v"
     for p, (st, dc) in enumerate(zip(stores, dcs)):
         y_ref, v_ref = oracle.bgmv(st, x, y0s[p], idx, nthreads=16)
         G.check(dc, *results[0][p], y_ref, v_ref, G.active_rows(idx, st.rank), f"plan-{layout}-{form}-p{p}")
