@@ -13,22 +13,24 @@
 // contiguous range of items, so the x row and v row of a tile stay in one L2.
 //
 // Shrink.  The output is only r wide, so parallelism comes from splitting rank-rows
-// over workgroups (jw per workgroup) and d_in over the 4 wavefronts of a workgroup;
-// the 4 partial sums are added in LDS in wavefront order.  No cross-workgroup
-// reduction, no atomics, no workspace, and results do not depend on scheduling.
+// over workgroups and d_in over the wavefronts of a workgroup; the partial sums are
+// added in LDS in wavefront order.  No cross-workgroup reduction, no atomics, no
+// workspace, and results do not depend on scheduling or on the work split.
 //   - tiles of < 8 rows (decode): fp16 dot2 (v_dot2_f32_f16) on 16-byte coalesced
-//     loads of x rows and A^T rank-rows, both contiguous in d_in;
-//   - tiles of 8..64 rows: v_mfma_f32_16x16x32_f16 on a 16-rank slice; each lane
-//     loads 8 consecutive k of an x row and of an A^T rank-row straight from memory,
-//     four k-steps in flight.
+//     loads of x rows and A^T rank-rows, both contiguous in d_in, many in flight;
+//   - tiles of 8..64 rows: v_mfma_f32_16x16x32_f16 over 16-rank slices, up to four of
+//     them (across the launch's projections) sharing each read of the tile's x rows;
+//     16 wavefronts split d_in.
 // Expand.  A workgroup owns 512 output columns of one tile.
 //   - tiles of < 8 rows: each wavefront loads its quarter of the rank-rows of B once
 //     (16-byte loads, contiguous in d_out, all in flight together), the quarters are
 //     added in LDS, and one fp32 -> fp16 rounding updates y;
-//   - tiles of 8..64 rows: B[0:r][512 columns] is staged in LDS and reused by every
-//     16-row slice; D^T = B^T (s v)^T runs on v_mfma_f32_16x16x16_f16 with s*v split
-//     into fp16 hi + lo/2048 parts (two MFMAs, ~22 bits kept); the accumulator starts
-//     from y and each lane updates 4 consecutive y elements of one row.
+//   - tiles of 8..64 rows: B[0:r][512 columns] is staged transposed in LDS and reused
+//     by every 16-row slice; D^T = B^T (s v)^T runs on v_mfma_f32_16x16x16_f16 with s*v
+//     split into fp16 hi + lo/2048 parts (two MFMAs, ~22 bits kept); the accumulator
+//     starts from y and each lane moves 8 consecutive y elements of one row.
+// Optionally, the per-row form runs both steps in one launch, each workgroup
+// recomputing its row's v (lora_fused_row_kernel); the bits match the two launches.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -89,7 +91,6 @@ constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kRowsPerPass = 4;     // rows per pass of the VALU kernels (segment form)
 constexpr int kCols = 512;           // expand columns per workgroup
-constexpr int kMaxRankPerWave = LORA_MAX_RANK / kWaves;
 constexpr int kMfmaShrinkThreads = 1024;  // 16 wavefronts split d_in in the MFMA shrink
 constexpr int kFusedGroups = 4;            // 256-lane groups of a fused workgroup
 constexpr int kFusedThreads = kFusedGroups * kThreads;
