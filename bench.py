@@ -255,6 +255,7 @@ def reference_floors(plan, spec, steps):
     moved = sum(2 * (b // 4 + 1) * 2 for b in sizes)
     out["copy_bytes_per_step"] = moved
     out["copy_gbs"] = round(moved / (out["copy_ms_per_step"] * 1e-3) / 1e9, 1)
+    out["copy_frac_of_peak"] = round(out["copy_gbs"] / 8000.0, 4)
     del bufs
     torch.cuda.empty_cache()
     return out
@@ -313,28 +314,36 @@ def cpu_baseline(spec, groups, budget_s=10.0):
     if spec["form"] != "bgmv":
         rm, sp, ss, _ = oracle.build_segments(b.idx, S)
     n_layers = len(set(h[0] for h in host))
-    t_total, bytes_total, layers_done = 0.0, 0, 0
-    while t_total < budget_s:
-        for lay in range(n_layers):
-            for _, x, stores, nbytes in (h for h in host if h[0] == lay):
-                t0 = time.perf_counter()
-                for store, y0 in stores:
-                    if spec["form"] == "bgmv":
-                        oracle.bgmv(store, x, y0, b.idx, nthreads=cores)
-                    else:
-                        oracle.sgmv(store, x, y0, sp, ss, rm, nthreads=cores)
-                t_total += time.perf_counter() - t0
-                bytes_total += nbytes
-            layers_done += 1
-            if t_total >= budget_s:
-                break
+
+    def timed(threads, budget):
+        t_total, bytes_total, layers_done = 0.0, 0, 0
+        while t_total < budget:
+            for lay in range(n_layers):
+                for _, x, stores, nbytes in (h for h in host if h[0] == lay):
+                    t0 = time.perf_counter()
+                    for store, y0 in stores:
+                        if spec["form"] == "bgmv":
+                            oracle.bgmv(store, x, y0, b.idx, nthreads=threads)
+                        else:
+                            oracle.sgmv(store, x, y0, sp, ss, rm, nthreads=threads)
+                    t_total += time.perf_counter() - t0
+                    bytes_total += nbytes
+                layers_done += 1
+                if t_total >= budget:
+                    break
+        return t_total, bytes_total, layers_done
+
+    t_total, bytes_total, layers_done = timed(cores, budget_s)
+    t1, b1, l1 = timed(1, budget_s / 4)
     return dict(value=round(bytes_total / t_total / 1e9, 4), unit="GB/s", cores=cores, kind="oracle",
                 us_per_layer=round(1e6 * t_total / layers_done, 1),
                 sample=f"{layers_done} layer passes over the {n_layers} layers x {len(spec['shapes'])} projections "
-                       f"of the step ({b.n} rows each), fp64 C loops with OpenMP over rows, {t_total:.1f} s")
+                       f"of the step ({b.n} rows each), fp64 C loops with OpenMP over rows, {t_total:.1f} s",
+                single_thread=dict(value=round(b1 / t1 / 1e9, 4), unit="GB/s", cores=1,
+                                   us_per_layer=round(1e6 * t1 / l1, 1),
+                                   sample=f"{l1} layer passes, one thread, {t1:.1f} s"))
 
 
-# ------------------------------------------------------------------ main
 # ------------------------------------------------------------------ operator sweep
 def sweep_assign(pop, n, seed):
     """Row -> adapter of the pages' popularity sweep, rows grouped by adapter (segment order):
@@ -449,6 +458,7 @@ def operator_sweep(args):
     print(json.dumps({"sweep": "operator", "h": h, "layers": L, "steps": K, "results": results}), flush=True)
 
 
+# ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -585,6 +595,7 @@ def main():
     if not args.no_floors:
         log("[bench] reference steps: empty launches, plain copies of the same bytes")
         floors = reference_floors(plan, spec, min(args.steps, 20))
+        floors["step_vs_copy"] = round(floors["copy_ms_per_step"] / ms, 4)  # our speed as a fraction of the copies
 
     cpu = None
     if not args.no_cpu_baseline:
