@@ -458,6 +458,111 @@ def operator_sweep(args):
     print(json.dumps({"sweep": "operator", "h": h, "layers": L, "steps": K, "results": results}), flush=True)
 
 
+# ------------------------------------------------------------------ adapter loading
+def load_sweep(args):
+    """Loading adapters into one paged pool (lora_pool_load: one host-to-device copy of a
+    page-locked blob, one scatter kernel).  A Llama-2-7B adapter set (32 layers x 7
+    projections, rank 16, 256-element pages) per model; `--sweep-batches` models per call.
+    Reported next to a plain host-to-device copy of the same blob (the link's rate) and to
+    the 7B decode step's time with and without a load running on a side stream."""
+    import torch
+    from segmented_gather_matmul_amd import binding as B
+    from segmented_gather_matmul_amd import workloads as wl
+    dev, P, r = "cuda", 256, 16
+    shapes = wl.LLAMA2_7B
+    layers = 32
+    out = {"sweep": "load", "model": "Llama-2-7B", "rank": r, "page_elems": P, "layers": layers, "results": []}
+    # the decode step, to see what a concurrent load costs it
+    spec = workload_spec("decode_distinct_7b")
+    groups = make_ops(spec, spec["layers"], dev)
+    plan = launches(groups, True, -1)
+    step(plan, -1)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(plan, -1)
+    side = torch.cuda.Stream()
+    for models in [int(v) for v in args.sweep_batches.split(",")]:
+        per_model_pages = layers * sum(r * (di // P + do // P) for di, do in shapes.values())
+        num_pages = models * per_model_pages
+        pool = torch.empty((num_pages, P), dtype=torch.float16, device=dev)
+        rank_t = torch.zeros(models, dtype=torch.int32, device=dev)
+        scale_t = torch.zeros(models, dtype=torch.float32, device=dev)
+        st = B.PoolState(num_pages)
+        targets = []
+        for layer in range(layers):
+            for name, (di, do) in shapes.items():
+                cap = r * (di // P + do // P)
+                w = B.Weights(num_slots=models, d_in=di, d_out=do, r_max=r, rank=rank_t, scale=scale_t, pool=pool,
+                              page_elems=P, page_table=torch.zeros(models * cap, dtype=torch.int32, device=dev),
+                              a_pt_off=torch.zeros(models, dtype=torch.int64, device=dev),
+                              b_pt_off=torch.zeros(models, dtype=torch.int64, device=dev))
+                targets.append((w, cap, di, do))
+        rng = np.random.default_rng(models)
+        ads = []
+        for m in range(models):
+            for w, cap, di, do in targets:
+                ads.append(dict(w=w, slot=m, rank=r, scale=2.0, pt_off=m * cap,
+                                a_t=(rng.standard_normal((r, di), dtype=np.float32) * 0.02).astype(np.float16),
+                                b=(rng.standard_normal((r, do), dtype=np.float32) * 0.02).astype(np.float16),
+                                pages=st.alloc(r * (di // P + do // P))))
+        blob, jobs = B.pack_adapters(ads, pinned=True)
+        staging = torch.empty(blob.numel(), dtype=torch.uint8, device=dev)
+        weight_bytes = sum(2 * r * (di + do) for _, _, di, do in targets) * models
+
+        def timed(fn, reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(side):
+                fn()
+                e0.record(side)
+                for _ in range(reps):
+                    fn()
+                e1.record(side)
+            side.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        load_ms = timed(lambda: B.lora_pool_load(jobs, blob, staging, stream=side), 5)
+        copy_ms = timed(lambda: staging.copy_(blob, non_blocking=True), 5)
+        # decode step alone, then with loads running on the side stream meanwhile
+        reps = 20
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        step_ms = e0.elapsed_time(e1) / reps
+        def step_during(fn, per_ms):
+            """Decode step time while `fn` runs back to back on the side stream."""
+            e0.record()
+            with torch.cuda.stream(side):
+                for _ in range(max(1, int(reps * step_ms / max(per_ms, 1e-3)))):
+                    fn()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            side.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        step_ms_loaded = step_during(lambda: B.lora_pool_load(jobs, blob, staging, stream=side), load_ms)
+        step_ms_copies = step_during(lambda: staging.copy_(blob, non_blocking=True), copy_ms)
+        rec = dict(models=models, jobs=len(jobs), weight_bytes=weight_bytes, blob_bytes=int(blob.numel()),
+                   load_ms=round(load_ms, 4), load_gbs=round(weight_bytes / (load_ms * 1e-3) / 1e9, 2),
+                   ms_per_model=round(load_ms / models, 4), h2d_copy_ms=round(copy_ms, 4),
+                   h2d_copy_gbs=round(blob.numel() / (copy_ms * 1e-3) / 1e9, 2),
+                   decode_step_ms=round(step_ms, 4), decode_step_ms_during_loads=round(step_ms_loaded, 4),
+                   decode_step_ms_during_copies=round(step_ms_copies, 4))
+        log(f"[load] {rec}")
+        out["results"].append(rec)
+        del pool, staging, blob, targets, ads
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
@@ -484,9 +589,10 @@ def main():
                          "kernels (0 = library's choice; results are bit-identical either way)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (byte-counter calibration)")
-    ap.add_argument("--sweep", choices=["operator"], default=None,
-                    help="instead of the step: time one LoRA operator across batch sizes, popularity and ranks "
-                         "against a loop over adapters and Gather-BMM")
+    ap.add_argument("--sweep", choices=["operator", "load"], default=None,
+                    help="instead of the step: 'operator' times one LoRA operator across batch sizes, popularity "
+                         "and ranks against a loop over adapters and Gather-BMM; 'load' times placing 7B adapter "
+                         "sets into a paged pool (--sweep-batches = models per call)")
     ap.add_argument("--sweep-h", type=int, default=4096)
     ap.add_argument("--sweep-layers", type=int, default=16)
     ap.add_argument("--sweep-batches", default="1,2,4,8,16,32,64")
@@ -514,8 +620,11 @@ def main():
     B.lib()
     if not torch.cuda.is_available():
         raise SystemExit("no GPU visible")
-    if args.sweep:
+    if args.sweep == "operator":
         operator_sweep(args)
+        return
+    if args.sweep == "load":
+        load_sweep(args)
         return
     device = "cuda"
     grouped = not args.no_group

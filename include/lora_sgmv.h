@@ -276,6 +276,70 @@ int lora_bgmv_expand_multi(void *stream, const int32_t *idx, int32_t n_rows, int
 int lora_bgmv_multi(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows,
                     int32_t n_proj, const lora_proj *proj, int32_t chunks);
 
+/* ---------------------------------------------------------------- adapter pool */
+/*
+ * Loading adapters into the paged layout (S-LoRA summary, "Unified Paging" and
+ * "Adapter Loading, Prefetching, and Overlapping I/O with Computation"; Punica
+ * summary, "On-Demand LoRA Weight Loading").  Pages all hold P fp16 elements, so
+ * taking and returning them never fragments the pool, and an adapter's rank-rows may
+ * sit in any free pages.
+ *
+ * Free-page list.  Its state lives in caller-owned host memory of
+ * lora_pool_state_bytes(num_pages) bytes (the library keeps none).  lora_pool_alloc
+ * hands out the most recently returned pages first.  Neither call is thread-safe on
+ * one state.
+ */
+size_t lora_pool_state_bytes(int64_t num_pages);
+int lora_pool_init(void *state, size_t state_bytes, int64_t num_pages);  /* num_pages in 1..2^31-1 */
+/* n free page ids into pages[0..n); LORA_E_CAPACITY, taking none, if fewer are free. */
+int lora_pool_alloc(void *state, int32_t n, int32_t *pages);
+/* Returns n pages; LORA_E_INDEX, returning none, for an id out of range, not taken, or listed twice. */
+int lora_pool_release(void *state, int32_t n, const int32_t *pages);
+int64_t lora_pool_free_count(const void *state);   /* -1 for an uninitialised state */
+
+/* Page-table entries (and pool pages) one adapter of rank r takes: r*(d_in + d_out)/P. */
+int64_t lora_pool_pages_for(int32_t rank, int32_t d_in, int32_t d_out, int32_t page_elems);
+
+/* One adapter to place into one projection's paged descriptor. */
+typedef struct lora_load_job {
+    const lora_weights *w;  /* host descriptor of the target (paged); its rank, scale, page_table,
+                               a_pt_off and b_pt_off arrays receive the adapter */
+    int32_t slot;           /* 0..num_slots-1 */
+    int32_t rank;           /* 0..r_max; 0 unloads the slot (only rank[slot] is written) */
+    float scale;            /* scale[slot] */
+    int32_t reserved;       /* 0 */
+    int64_t pt_off;         /* first of the adapter's page-table entries: A^T rank-rows
+                               (rank*d_in/P entries, rank-row-major), then B (rank*d_out/P) */
+    int64_t data_off;       /* byte offset in the blob of A^T [rank][d_in] followed by
+                               B [rank][d_out], fp16; multiple of 16 */
+    int64_t pages_off;      /* byte offset in the blob of the adapter's page ids (int32,
+                               page-table order); multiple of 4 */
+} lora_load_job;
+
+/* Bytes at the start of a blob that lora_pool_load fills with its job table (a multiple of 16). */
+size_t lora_pool_load_header_bytes(int32_t n_jobs);
+
+/*
+ * Places n_jobs adapters with one host-to-device copy and one kernel, in order on
+ * `stream`:
+ *   1. writes the job table into blob[0 .. lora_pool_load_header_bytes(n_jobs));
+ *   2. copies blob[0 .. blob_bytes) into staging (device, >= blob_bytes bytes, 16-byte
+ *      aligned; it must not be reused before the kernel has finished);
+ *   3. writes every job's rank-rows into its pages (A^T rank-row j, page q <- elements
+ *      q*P .. q*P+P-1), page_table[pt_off + e] <- the page ids, and the slot's
+ *      a_pt_off = pt_off, b_pt_off = pt_off + rank*d_in/P, rank and scale.
+ * blob: host memory, 16-byte aligned, page-locked (hipHostMalloc) for the copy to be
+ * asynchronous; it must stay unchanged until the copy has completed.  Every argument is
+ * checked on the host before anything is issued, page ids included (read from the
+ * blob): each in 0..num_pages-1 and no page named twice in the call; data and page-id
+ * ranges inside the blob and after the header; page-table ranges inside pt_entries;
+ * one job per (target, slot).  Pages are written in place, so a slot (and pages) being
+ * loaded must not be read by work that can run at the same time: order it with an
+ * event.  Page-table entries and pages of other slots are untouched.
+ */
+int lora_pool_load(void *stream, int32_t n_jobs, const lora_load_job *jobs, void *blob, size_t blob_bytes,
+                   void *staging, size_t staging_bytes);
+
 /* ---------------------------------------------------------------- diagnostics */
 /*
  * Timing hook: attach two hipEvent_t (created by the caller; either may be NULL) to

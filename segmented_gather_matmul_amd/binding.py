@@ -32,7 +32,8 @@ EXPORTS = ["lora_build_segments", "lora_tiles_bound", "lora_build_tiles", "lora_
            "lora_bgmv_shrink", "lora_bgmv_expand", "lora_bgmv", "lora_last_error", "lora_status_str",
            "lora_abi_version", "lora_set_launch_events", "lora_sgmv_shrink_multi", "lora_sgmv_expand_multi",
            "lora_bgmv_shrink_multi", "lora_bgmv_expand_multi", "lora_pick_tile_rows", "lora_bgmv_multi",
-           "lora_set_plan"]
+           "lora_set_plan", "lora_pool_state_bytes", "lora_pool_init", "lora_pool_alloc", "lora_pool_release",
+           "lora_pool_free_count", "lora_pool_pages_for", "lora_pool_load_header_bytes", "lora_pool_load"]
 MAX_PROJ = 4
 
 
@@ -54,6 +55,12 @@ class CWeights(ctypes.Structure):
 class CProj(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p), ("v", ctypes.c_void_p), ("ldv", ctypes.c_int64), ("y", ctypes.c_void_p),
                 ("ldy", ctypes.c_int64)]
+
+
+class CLoadJob(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("slot", ctypes.c_int32), ("rank", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("reserved", ctypes.c_int32), ("pt_off", ctypes.c_int64), ("data_off", ctypes.c_int64),
+                ("pages_off", ctypes.c_int64)]
 
 
 class CSegments(ctypes.Structure):
@@ -95,12 +102,22 @@ def lib() -> ctypes.CDLL:
             "lora_pick_tile_rows": [P, I32],
             "lora_bgmv_multi": [P, P, I64, P, I32, I32, P, I32],
             "lora_set_plan": [I32, I32],
+            "lora_pool_init": [P, ctypes.c_size_t, I64],
+            "lora_pool_alloc": [P, I32, P],
+            "lora_pool_release": [P, I32, P],
+            "lora_pool_load": [P, I32, P, P, ctypes.c_size_t, P, ctypes.c_size_t],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
         L.lora_tiles_bound.restype = ctypes.c_int32
+        for name, args, res in (("lora_pool_state_bytes", [I64], ctypes.c_size_t),
+                                ("lora_pool_free_count", [P], I64),
+                                ("lora_pool_pages_for", [I32, I32, I32, I32], I64),
+                                ("lora_pool_load_header_bytes", [I32], ctypes.c_size_t)):
+            fn = getattr(L, name)
+            fn.argtypes, fn.restype = args, res
         L.lora_pick_tile_rows.restype = ctypes.c_int32
         L.lora_last_error.restype = ctypes.c_char_p
         L.lora_status_str.restype = ctypes.c_char_p
@@ -338,3 +355,73 @@ def lora_bgmv_multi(x, idx, items, chunks=0, stream=None):
     arr = proj_list(items)
     _check(lib().lora_bgmv_multi(_stream(stream), _ptr(x), _ld(x), _ptr(idx), int(x.shape[0]), len(items), arr,
                                  int(chunks)))
+
+
+# ------------------------------------------------------------------ adapter pool
+class PoolState:
+    """Host free-page list (lora_pool_*) in a numpy buffer owned by this object."""
+
+    def __init__(self, num_pages):
+        n = lib().lora_pool_state_bytes(int(num_pages))
+        if n == 0:
+            raise LoraError(LORA_E_SHAPE, f"num_pages = {num_pages}")
+        self.buf = np.zeros(n, dtype=np.uint8)
+        _check(lib().lora_pool_init(self.buf.ctypes.data, n, int(num_pages)))
+
+    def alloc(self, n):
+        out = np.zeros(int(n), dtype=np.int32)
+        _check(lib().lora_pool_alloc(self.buf.ctypes.data, int(n), out.ctypes.data if n else None))
+        return out
+
+    def release(self, pages):
+        pages = np.ascontiguousarray(pages, dtype=np.int32)
+        _check(lib().lora_pool_release(self.buf.ctypes.data, len(pages), pages.ctypes.data if len(pages) else None))
+
+    @property
+    def free(self):
+        return int(lib().lora_pool_free_count(self.buf.ctypes.data))
+
+
+def lora_pool_pages_for(rank, d_in, d_out, page_elems):
+    n = int(lib().lora_pool_pages_for(int(rank), int(d_in), int(d_out), int(page_elems)))
+    if n < 0:
+        _check(n)
+    return n
+
+
+def pack_adapters(adapters, pinned=True):
+    """Blob for lora_pool_load.  adapters: sequence of dicts with keys w (Weights), slot,
+    rank, scale, pt_off, a_t (fp16 [rank][d_in] numpy), b (fp16 [rank][d_out]), pages
+    (int32 ids in page-table order); rank 0 entries unload.  Returns (blob uint8 tensor,
+    page-locked when pinned, and the ctypes job array)."""
+    import torch
+    n = len(adapters)
+    off = int(lib().lora_pool_load_header_bytes(n))
+    jobs = (CLoadJob * n)()
+    parts = []
+    for i, ad in enumerate(adapters):
+        j = jobs[i]
+        j.w = ctypes.addressof(ad["w"].c)
+        j.slot, j.rank, j.scale, j.reserved = int(ad["slot"]), int(ad["rank"]), float(ad["scale"]), 0
+        j.pt_off = int(ad.get("pt_off", 0))
+        if ad["rank"] == 0:
+            continue
+        data = np.concatenate([np.ascontiguousarray(ad["a_t"], np.float16).ravel(),
+                               np.ascontiguousarray(ad["b"], np.float16).ravel()]).view(np.uint8)
+        ids = np.ascontiguousarray(ad["pages"], np.int32).view(np.uint8)
+        j.data_off = off
+        parts.append((off, data))
+        off = -(-(off + len(data)) // 16) * 16
+        j.pages_off = off
+        parts.append((off, ids))
+        off = -(-(off + len(ids)) // 16) * 16
+    blob = torch.zeros(max(off, 16), dtype=torch.uint8, pin_memory=pinned)
+    view = blob.numpy()
+    for o, d in parts:
+        view[o:o + len(d)] = d
+    return blob, jobs
+
+
+def lora_pool_load(jobs, blob, staging, stream=None):
+    _check(lib().lora_pool_load(_stream(stream), len(jobs), jobs, _ptr(blob), int(blob.numel()), _ptr(staging),
+                                int(staging.numel())))

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblora_sgmv.so")
-SOURCES = [os.path.join(CSRC, "lora_kernels.hip"), os.path.join(CSRC, "lora_host.cpp")]
+SOURCES = [os.path.join(CSRC, "lora_kernels.hip"), os.path.join(CSRC, "lora_pool.hip"),
+           os.path.join(CSRC, "lora_host.cpp")]
 HEADERS = [os.path.join(INCLUDE, "lora_sgmv.h"), os.path.join(CSRC, "lora_internal.hpp")]
 ARCH = "gfx950"
 
