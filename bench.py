@@ -55,12 +55,14 @@ def workload_spec(name):
         return dict(cfg_id=4, shapes=wl.LLAMA2_7B, layers=4, num_slots=16, rank=np.full(16, 16, np.int32),
                     scale=np.full(16, 2.0, np.float32), batch=b, form="sgmv_contiguous", layout="dense",
                     model="Llama-2-7B", popularity="distinct")
-    if name == "paged_70b":
+    if name in ("paged_70b", "paged_70b_tp8"):
         rank = wl.paged_ranks(2000)
         b = wl.batch_paged_zipf(256, 2000)
-        return dict(cfg_id=5, shapes=wl.LLAMA2_70B, layers=2, num_slots=2000, rank=rank,
-                    scale=wl.scale_for_rank(rank), batch=b, form="bgmv", layout="paged", page_elems=1024,
-                    model="Llama-2-70B", popularity="zipf1.2")
+        tp8 = name.endswith("tp8")
+        return dict(cfg_id=5, shapes=wl.LLAMA2_70B_TP8 if tp8 else wl.LLAMA2_70B, layers=2, num_slots=2000,
+                    rank=rank, scale=wl.scale_for_rank(rank), batch=b, form="bgmv", layout="paged",
+                    page_elems=128 if tp8 else 1024, model="Llama-2-70B, one GPU of 8-way TP" if tp8 else "Llama-2-70B",
+                    popularity="zipf1.2")
     raise SystemExit(f"unknown workload {name}")
 
 

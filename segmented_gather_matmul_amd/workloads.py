@@ -198,6 +198,10 @@ LLAMA2_13B = {"q": (5120, 5120), "k": (5120, 5120), "v": (5120, 5120), "o": (512
 # 70B with grouped-query attention: k/v project 8192 -> 1024.
 LLAMA2_70B = {"q": (8192, 8192), "k": (8192, 1024), "v": (8192, 1024), "o": (8192, 8192),
               "gate": (8192, 28672), "up": (8192, 28672), "down": (28672, 8192)}
+# One GPU's shard of 70B under 8-way tensor parallelism: q/k/v/gate/up split by output
+# columns, o/down by input rows (their partial products join the base output's sum).
+LLAMA2_70B_TP8 = {"q": (8192, 1024), "k": (8192, 128), "v": (8192, 128), "o": (1024, 8192),
+                  "gate": (8192, 3584), "up": (8192, 3584), "down": (3584, 8192)}
 PROJ_IDS = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6}
 
 

@@ -112,6 +112,31 @@ def test_paged_mixed_rank_70b(d_out, form):
     G.check(dc, y, v, y_ref, v_ref, G.active_rows(b.idx, rank), f"paged-70b-{d_out}")
 
 
+@pytest.mark.parametrize("proj", ["k", "o", "down"])
+def test_paged_70b_tp8_shard_shapes(proj):
+    """One GPU's shard under 8-way tensor parallelism (k 8192->128, o 1024->8192, down
+    3584->8192) with 128-element pages, 256 rows by Zipf 1.2 over 2000 mixed-rank adapters."""
+    import torch
+    d_in, d_out = wl.LLAMA2_70B_TP8[proj]
+    P, S = 128, 2000
+    rank = wl.paged_ranks(S)
+    scale = wl.scale_for_rank(rank)
+    b = wl.batch_paged_zipf(256, S)
+    pid = wl.PROJ_IDS[proj] + 10
+    G.say(f"case paged-70b-tp8 {proj} {d_in}->{d_out}")
+    pool, pt, a_off, b_off, rows, compact_pt = G.paged_device_pool(5, pid, rank, d_in, d_out, P, b.idx)
+    ostore = wl.PagedStore(S, d_in, d_out, 64, P, rank, scale, rows, compact_pt, a_off, b_off)
+    x, y0 = wl.activations(5, pid, 256, d_in, d_out)
+    y_ref, v_ref = _oracle(ostore, x, y0, b.idx)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    w = B.Weights(num_slots=S, d_in=d_in, d_out=d_out, r_max=64, rank=dev(rank), scale=dev(scale), pool=pool,
+                  page_elems=P, page_table=dev(pt), a_pt_off=dev(a_off), b_pt_off=dev(b_off))
+    for form in ("bgmv", "sgmv_rowmap"):
+        dc = G.DeviceCase(x, y0, 64)
+        y, v = _run(form, w, dc, b.idx)
+        G.check(dc, y, v, y_ref, v_ref, G.active_rows(b.idx, rank), f"paged-70b-tp8-{proj}-{form}")
+
+
 # ------------------------------------------------------------------ edge cases
 def _mixed_rank_store(cfg, d_in, d_out, S=7, paged_P=None):
     rank = np.array([1, 64, 0, 17, 8, 33, 64], dtype=np.int32)[:S]

@@ -141,3 +141,44 @@ def test_one_call_two_projections_one_pool():
         _check_placed(ad["w"], pool, ad, ad["b"].shape[1])
     for p, ((w, _), d) in enumerate(zip(targets, outs)):
         _compute_and_check(w, rank, d, p, f"pool-proj{p}")
+
+
+@pytest.mark.parametrize("page_elems,d_in,d_out", [(56, 1288, 1064), (4096, 4096, 8192), (8, 64, 24)])
+def test_page_sizes(page_elems, d_in, d_out):
+    """Pages copied by 7 lanes (56 elements), by a whole workgroup in a loop (4096), and
+    by one lane each (8); every placed adapter checked bitwise and through the kernels."""
+    import torch
+    rank = np.array([3, 0, 17, 64, 1, 8], dtype=np.int32)
+    cap = R_MAX * (d_in // page_elems + d_out // page_elems)
+    need = int(sum(B.lora_pool_pages_for(int(r), d_in, d_out, page_elems) for r in rank))
+    num_pages = need + 7
+    pool = torch.full((num_pages, page_elems), float("nan"), dtype=torch.float16, device="cuda")
+    w = B.Weights(num_slots=S, d_in=d_in, d_out=d_out, r_max=R_MAX,
+                  rank=torch.zeros(S, dtype=torch.int32, device="cuda"),
+                  scale=torch.zeros(S, dtype=torch.float32, device="cuda"), pool=pool, page_elems=page_elems,
+                  page_table=torch.full((S * cap,), -1, dtype=torch.int32, device="cuda"),
+                  a_pt_off=torch.zeros(S, dtype=torch.int64, device="cuda"),
+                  b_pt_off=torch.zeros(S, dtype=torch.int64, device="cuda"))
+    st = _fragmented_pool(num_pages, page_elems)
+    G.say(f"case pool-pages P={page_elems} {d_in}->{d_out}")
+    ads = []
+    for s, r in enumerate(rank):
+        if r == 0:
+            continue
+        a_t, b = wl.slot_matrices(CFG, 9, s, int(r), d_in, d_out)
+        ads.append(dict(w=w, slot=s, rank=int(r), scale=float(wl.scale_for_rank(int(r))), pt_off=s * cap, a_t=a_t,
+                        b=b, pages=st.alloc(B.lora_pool_pages_for(int(r), d_in, d_out, page_elems))))
+    _load(ads)
+    for ad in ads:
+        r, ids = ad["rank"], ad["pages"]
+        got = pool[ids.astype(np.int64)].cpu().numpy().view(np.uint16)
+        want = np.concatenate([ad["a_t"].reshape(-1, page_elems), ad["b"].reshape(-1, page_elems)]).view(np.uint16)
+        assert np.array_equal(got, want), f"slot {ad['slot']}: page contents"
+    n = 60
+    idx = np.random.default_rng(page_elems).integers(-1, S, size=n).astype(np.int32)
+    store = wl.dense_store(CFG, 9, S, d_in, d_out, rank, wl.scale_for_rank(rank), r_max=R_MAX)
+    x, y0 = wl.activations(CFG, 9, n, d_in, d_out)
+    y_ref, v_ref = oracle.bgmv(store, x, y0, idx, nthreads=16)
+    dc = G.DeviceCase(x, y0, R_MAX)
+    y, v = G.run_bgmv(w, dc, idx)
+    G.check(dc, y, v, y_ref, v_ref, G.active_rows(idx, rank), f"pool-pages-{page_elems}")
