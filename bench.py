@@ -374,8 +374,8 @@ def operator_sweep(args):
     The last two are plain PyTorch, timing context only."""
     import torch
     from segmented_gather_matmul_amd import binding as B
-    h, L, K = args.sweep_h, args.sweep_layers, args.steps
-    ns = [int(v) for v in args.sweep_batches.split(",")]
+    h, L, K = args.sweep_h, args.sweep_layers or 16, args.steps
+    ns = [int(v) for v in (args.sweep_batches or "1,2,4,8,16,32,64").split(",")]
     rs = [int(v) for v in args.sweep_ranks.split(",")]
     pops = args.sweep_pops.split(",")
     dev = "cuda"
@@ -484,7 +484,7 @@ def load_sweep(args):
     with torch.cuda.graph(g):
         step(plan, -1)
     side = torch.cuda.Stream()
-    for models in [int(v) for v in args.sweep_batches.split(",")]:
+    for models in [int(v) for v in (args.sweep_batches or "1,2,4").split(",")]:
         per_model_pages = layers * sum(r * (di // P + do // P) for di, do in shapes.values())
         num_pages = models * per_model_pages
         pool = torch.empty((num_pages, P), dtype=torch.float16, device=dev)
@@ -565,6 +565,87 @@ def load_sweep(args):
     print(json.dumps(out), flush=True)
 
 
+# ------------------------------------------------------------------ decoder layer
+def layer_sweep(args):
+    """Decode step of whole Llama-2 decoder layers (RMSNorm, fused q/k/v GEMM, attention
+    over a key/value cache of `seq_len` positions, o GEMM, fused gate/up GEMM, SiLU
+    gating, down GEMM, residual adds; PyTorch on the GPU) with the seven LoRA add-ons of
+    each layer through this library, one metadata build per batch shared by all of them,
+    against the same layers without add-ons.  The layers are chained (each feeds the
+    next), have distinct weights and caches so nothing stays cached between layers, are
+    captured in one graph and replayed; the result is us per layer.  Rank 16, 32 resident
+    adapters, the popularity mixes of the operator sweep."""
+    import torch
+    from segmented_gather_matmul_amd import costmodel as cm
+    from segmented_gather_matmul_amd import layer as LY
+    ns = [int(v) for v in (args.sweep_batches or "1,2,4,8,16,32").split(",")]
+    seqs = [int(v) for v in args.sweep_seqs.split(",")]
+    pops = ["none"] + args.sweep_pops.split(",")
+    L, K, r, slots = args.sweep_layers or 4, args.steps, 16, 32
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    out = {"sweep": "layer", "form": args.layer_form, "rank": r, "resident_adapters": slots, "layers": L,
+           "steps": K, "results": []}
+    for model in args.sweep_models.split(","):
+        shape = LY.SHAPES[model]
+        log(f"[layer] {shape.name}: drawing {L} layers")
+        layers = [LY.random_layer(shape, slots, r, max(ns), gen) for _ in range(L)]
+        dims = LY.proj_dims(shape)
+        for seq in seqs:
+            for n in ns:
+                caches = [LY.KVCache.random(shape, n, seq, gen) for _ in range(L)]
+                hidden = torch.randn((n, shape.hidden), generator=gen, device="cuda").half()
+                rec = dict(model=shape.name, seq_len=seq, n=n)
+                for pop in pops:
+                    if pop == "none":
+                        meta, idx, build_us = None, None, 0.0
+                    else:
+                        idx = sweep_assign(pop, n, n * 100 + r)
+                        t0 = time.perf_counter()
+                        meta = LY.BatchMeta(idx, slots, args.layer_form)
+                        torch.cuda.synchronize()
+                        build_us = 1e6 * (time.perf_counter() - t0)
+
+                    def run():
+                        x = hidden
+                        for lay, c in zip(layers, caches):
+                            x = lay.forward(x, c, meta)
+                        return x
+
+                    eager = run().clone()
+                    torch.cuda.synchronize()
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        res = run()
+                    g.replay()
+                    torch.cuda.synchronize()
+                    same = bool(torch.equal(res, eager))
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(K):
+                        g.replay()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    us = 1e3 * e0.elapsed_time(e1) / (K * L)
+                    del g, res
+                    lora_b = 0 if idx is None else sum(cm.op_bytes(idx, np.full(slots, r), di, do, r)
+                                                       for di, do in dims.values())
+                    layer_b = LY.backbone_bytes(shape) + 2 * 2 * n * seq * shape.hidden + lora_b
+                    rec[pop] = dict(us=round(us, 2), lora_bytes=lora_b, gbs=round(layer_b / (us * 1e-6) / 1e9, 1),
+                                    graph_equals_eager=same)
+                    if pop != "none":
+                        rec[pop]["meta_build_us"] = round(build_us, 1)
+                        rec[pop]["overhead_vs_none"] = round(us / rec["none"]["us"] - 1.0, 4)
+                log(f"[layer] {shape.name} seq={seq} n={n}: " +
+                    " ".join(f"{p}={rec[p]['us']}" for p in pops))
+                out["results"].append(rec)
+                del caches
+                torch.cuda.empty_cache()
+        del layers
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
@@ -591,15 +672,21 @@ def main():
                          "kernels (0 = library's choice; results are bit-identical either way)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (byte-counter calibration)")
-    ap.add_argument("--sweep", choices=["operator", "load"], default=None,
+    ap.add_argument("--sweep", choices=["operator", "load", "layer"], default=None,
                     help="instead of the step: 'operator' times one LoRA operator across batch sizes, popularity "
                          "and ranks against a loop over adapters and Gather-BMM; 'load' times placing 7B adapter "
-                         "sets into a paged pool (--sweep-batches = models per call)")
+                         "sets into a paged pool (--sweep-batches = models per call); 'layer' times whole "
+                         "decoder layers with and without the seven add-ons")
     ap.add_argument("--sweep-h", type=int, default=4096)
-    ap.add_argument("--sweep-layers", type=int, default=16)
-    ap.add_argument("--sweep-batches", default="1,2,4,8,16,32,64")
+    ap.add_argument("--sweep-layers", type=int, default=None, help="layers per graph (operator 16, layer 4)")
+    ap.add_argument("--sweep-batches", default=None,
+                    help="batch sizes (operator 1..64, layer 1..32) or models per load call (load 1,2,4)")
     ap.add_argument("--sweep-ranks", default="8,16,32,64")
     ap.add_argument("--sweep-pops", default="distinct,uniform,skewed,identical")
+    ap.add_argument("--sweep-models", default="7b,13b", help="layer sweep: Llama-2 shapes")
+    ap.add_argument("--sweep-seqs", default="512,2048", help="layer sweep: cache lengths")
+    ap.add_argument("--layer-form", choices=["bgmv", "sgmv"], default="bgmv",
+                    help="layer sweep: add-ons in the per-row or the segment form")
     args = ap.parse_args()
     if args.calibrate_copy:
         import torch
@@ -627,6 +714,9 @@ def main():
         return
     if args.sweep == "load":
         load_sweep(args)
+        return
+    if args.sweep == "layer":
+        layer_sweep(args)
         return
     device = "cuda"
     grouped = not args.no_group
