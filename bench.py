@@ -37,12 +37,16 @@ def log(*a):
 
 
 # ------------------------------------------------------------------ workloads
-def workload_spec(name):
+def workload_spec(name, rows=None):
     from segmented_gather_matmul_amd import workloads as wl
+    if rows is not None and name != "decode_distinct_7b":
+        raise SystemExit("--rows applies to decode_distinct_7b only")
     if name == "decode_distinct_7b":
-        b = wl.batch_decode_distinct(32)
-        return dict(cfg_id=2, shapes=wl.LLAMA2_7B, layers=32, num_slots=32, rank=np.full(32, 16, np.int32),
-                    scale=np.full(32, 2.0, np.float32), batch=b, form="bgmv", layout="dense",
+        n = 32 if rows is None else int(rows)
+        S = max(32, n)
+        b = wl.batch_decode_distinct(n)
+        return dict(cfg_id=2, shapes=wl.LLAMA2_7B, layers=32, num_slots=S, rank=np.full(S, 16, np.int32),
+                    scale=np.full(S, 2.0, np.float32), batch=b, form="bgmv", layout="dense",
                     model="Llama-2-7B", popularity="distinct")
     if name.startswith("decode_") and name.endswith("_13b"):
         pop = name.split("_")[1]
@@ -571,40 +575,54 @@ def layer_sweep(args):
     over a key/value cache of `seq_len` positions, o GEMM, fused gate/up GEMM, SiLU
     gating, down GEMM, residual adds; PyTorch on the GPU) with the seven LoRA add-ons of
     each layer through this library, one metadata build per batch shared by all of them,
-    against the same layers without add-ons.  The layers are chained (each feeds the
-    next), have distinct weights and caches so nothing stays cached between layers, are
-    captured in one graph and replayed; the result is us per layer.  Rank 16, 32 resident
-    adapters, the popularity mixes of the operator sweep."""
+    against the same layers without add-ons.  Each mix runs twice: add-ons after each
+    GEMM on one stream, and with each shrink on a second stream overlapping its GEMM
+    ("+overlap", same bits).  The layers are chained (each feeds the next), have distinct
+    weights and caches so nothing stays cached between layers, are captured in one graph
+    and replayed; the result is us per layer.  Rank 16, 32 resident adapters, the
+    popularity mixes of the operator sweep."""
     import torch
     from segmented_gather_matmul_amd import costmodel as cm
     from segmented_gather_matmul_amd import layer as LY
     ns = [int(v) for v in (args.sweep_batches or "1,2,4,8,16,32").split(",")]
     seqs = [int(v) for v in args.sweep_seqs.split(",")]
-    pops = ["none"] + args.sweep_pops.split(",")
+    pops = args.sweep_pops.split(",")
+    variants = ["none"] + [p + sfx for p in pops for sfx in ("", "+overlap")]
     L, K, r, slots = args.sweep_layers or 4, args.steps, 16, 32
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
-    out = {"sweep": "layer", "form": args.layer_form, "rank": r, "resident_adapters": slots, "layers": L,
-           "steps": K, "results": []}
+    side = torch.cuda.Stream()
+    out = {"sweep": "layer", "form": args.layer_form, "chunks": args.layer_chunks, "rank": r,
+           "resident_adapters": slots, "layers": L, "steps": K, "results": []}
     for model in args.sweep_models.split(","):
         shape = LY.SHAPES[model]
         log(f"[layer] {shape.name}: drawing {L} layers")
         layers = [LY.random_layer(shape, slots, r, max(ns), gen) for _ in range(L)]
+        for lay in layers:
+            lay.chunks = args.layer_chunks
         dims = LY.proj_dims(shape)
         for seq in seqs:
             for n in ns:
                 caches = [LY.KVCache.random(shape, n, seq, gen) for _ in range(L)]
                 hidden = torch.randn((n, shape.hidden), generator=gen, device="cuda").half()
                 rec = dict(model=shape.name, seq_len=seq, n=n)
-                for pop in pops:
+                metas = {}
+                for var in variants:
+                    pop, overlap = var.split("+")[0], var.endswith("+overlap")
+                    build_us = 0.0
                     if pop == "none":
-                        meta, idx, build_us = None, None, 0.0
+                        meta, idx = None, None
+                    elif pop in metas:
+                        meta, idx, build_us = metas[pop]
                     else:
                         idx = sweep_assign(pop, n, n * 100 + r)
                         t0 = time.perf_counter()
                         meta = LY.BatchMeta(idx, slots, args.layer_form)
                         torch.cuda.synchronize()
                         build_us = 1e6 * (time.perf_counter() - t0)
+                        metas[pop] = (meta, idx, build_us)
+                    for lay in layers:
+                        lay.side = side if overlap else None
 
                     def run():
                         x = hidden
@@ -631,16 +649,19 @@ def layer_sweep(args):
                     lora_b = 0 if idx is None else sum(cm.op_bytes(idx, np.full(slots, r), di, do, r)
                                                        for di, do in dims.values())
                     layer_b = LY.backbone_bytes(shape) + 2 * 2 * n * seq * shape.hidden + lora_b
-                    rec[pop] = dict(us=round(us, 2), lora_bytes=lora_b, gbs=round(layer_b / (us * 1e-6) / 1e9, 1),
+                    rec[var] = dict(us=round(us, 2), lora_bytes=lora_b, gbs=round(layer_b / (us * 1e-6) / 1e9, 1),
                                     graph_equals_eager=same)
                     if pop != "none":
-                        rec[pop]["meta_build_us"] = round(build_us, 1)
-                        rec[pop]["overhead_vs_none"] = round(us / rec["none"]["us"] - 1.0, 4)
-                log(f"[layer] {shape.name} seq={seq} n={n}: " +
-                    " ".join(f"{p}={rec[p]['us']}" for p in pops))
+                        rec[var]["meta_build_us"] = round(build_us, 1)
+                        rec[var]["overhead_vs_none"] = round(us / rec["none"]["us"] - 1.0, 4)
+                if any(not rec[v]["graph_equals_eager"] for v in variants):
+                    raise SystemExit(f"graph replay differs from the eager run at {shape.name} seq={seq} n={n}")
+                log(f"[layer] {shape.name} seq={seq} n={n}: " + " ".join(f"{v}={rec[v]['us']}" for v in variants))
                 out["results"].append(rec)
                 del caches
                 torch.cuda.empty_cache()
+        for lay in layers:
+            lay.side = None
         del layers
         torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
@@ -654,6 +675,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_distinct_7b")
     ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--rows", type=int, default=None,
+                    help="decode_distinct_7b with this many rows (each its own adapter) instead of 32")
     ap.add_argument("--kernel-steps", type=int, default=5, help="steps of the per-launch event pass")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-group", action="store_true", help="one launch per projection (14 per layer)")
@@ -687,6 +710,8 @@ def main():
     ap.add_argument("--sweep-seqs", default="512,2048", help="layer sweep: cache lengths")
     ap.add_argument("--layer-form", choices=["bgmv", "sgmv"], default="bgmv",
                     help="layer sweep: add-ons in the per-row or the segment form")
+    ap.add_argument("--layer-chunks", type=int, default=0,
+                    help="layer sweep, per-row form: 0 = library's choice, -1 = two launches, c >= 1 = one launch")
     args = ap.parse_args()
     if args.calibrate_copy:
         import torch
@@ -720,7 +745,7 @@ def main():
         return
     device = "cuda"
     grouped = not args.no_group
-    spec = workload_spec(args.workload)
+    spec = workload_spec(args.workload, args.rows)
     if args.form and args.form != spec["form"].split("_")[0]:
         if spec["form"] == "sgmv_contiguous":
             raise SystemExit("the prefill workload is given as contiguous segments")
@@ -787,7 +812,7 @@ def main():
     dom = max(per_kernel, key=lambda k: totals[k])
     pk = per_kernel[dom]
     kernel_name = {"shrink": "lora_shrink_kernel", "expand": "lora_expand_kernel", "fused": "lora_fused_row_kernel"}[dom]
-    traffic = traffic_from_profile(args.workload, dom)
+    traffic = None if args.rows is not None else traffic_from_profile(args.workload, dom)
     roofline = dict(bound="hbm", achieved=pk["gbs"], peak=cm.HBM_PEAK_GBS, unit="GB/s",
                     frac=round(pk["gbs"] / cm.HBM_PEAK_GBS, 4), traffic=traffic, kernel=kernel_name,
                     avg_launch_us=pk["avg_us"], algorithmic_bytes_per_launch=pk["bytes_per_launch"])

@@ -11,7 +11,9 @@ work-list and row map of the segment form built once on the host from those ids
 q/k/v come from one backbone GEMM against a [h, 3h] weight and gate/up from one against
 [h, 2f]; their add-ons land in column slices of that output through the row-stride
 argument (ldy = 3h or 2f).  q/k/v share one call over three projections (same x), and
-gate/up another, so a layer makes four add-on calls.
+gate/up another, so a layer makes four add-on calls.  Optionally each shrink runs on a
+second stream while the backbone GEMM of the same input runs, so only the expands stay
+on the layer's critical path.
 
 Left out of the step on purpose: rotary position embedding (elementwise on q and k) and
 sampling.  The current token's k and v are written into the last position of the cache,
@@ -102,11 +104,18 @@ class LoraDecoderLayer:
     w_d [f, h] (all applied as x @ W), norm1 [h], norm2 [h].
     adapters: proj -> (a_t [S, r_max, d_in], b [S, r_max, d_out]) fp16 device tensors.
     rank (int32 [S]) and scale (fp32 [S]) are the slots' ranks and scales, shared by the
-    seven projections.  max_rows bounds the batch (it sizes the v buffers)."""
+    seven projections.  max_rows bounds the batch (it sizes the v buffers).  chunks is passed
+    to the per-row form's calls (0: the library's choice of one or two launches).  overlap:
+    each shrink runs on a second stream (default priority) concurrently with the backbone
+    GEMM of its projections, the expand after that GEMM; the results are the same bits as
+    without overlap (the same two launches, in the same data order)."""
 
-    def __init__(self, shape: LlamaShape, backbone: dict, adapters: dict, rank, scale, max_rows):
+    def __init__(self, shape: LlamaShape, backbone: dict, adapters: dict, rank, scale, max_rows, chunks=0,
+                 overlap=False):
         import torch
         self.shape = shape
+        self.chunks = int(chunks)
+        self.side = torch.cuda.Stream(device=rank.device) if overlap else None
         self.bb = backbone
         num_slots, r_max = adapters["q"][0].shape[:2]
         self.num_slots, self.r_max = int(num_slots), int(r_max)
@@ -123,15 +132,51 @@ class LoraDecoderLayer:
         self.v = {p: torch.empty((max_rows, ldv), dtype=torch.float32, device=rank.device) for p in PROJS}
         self.max_rows = int(max_rows)
 
-    def _add(self, meta: BatchMeta, x, names, outs):
-        """The add-ons of the projections `names` (all reading x) into the views `outs`."""
-        n = x.shape[0]
-        items = [(self.w[p], self.v[p][:n], y) for p, y in zip(names, outs)]
+    def _items(self, names, outs, n):
+        return [(self.w[p], self.v[p][:n], y) for p, y in zip(names, outs)]
+
+    def _shrink(self, meta: BatchMeta, x, names):
+        items = self._items(names, [None] * len(names), x.shape[0])
         if meta.form == "bgmv":
-            B.lora_bgmv_multi(x, meta.idx, items)
+            B.lora_bgmv_shrink_multi(x, meta.idx, items)
         else:
             B.lora_sgmv_shrink_multi(x, meta.segs, items)
+
+    def _expand(self, meta: BatchMeta, names, outs, n):
+        items = self._items(names, outs, n)
+        if meta.form == "bgmv":
+            B.lora_bgmv_expand_multi(meta.idx, items, n)
+        else:
             B.lora_sgmv_expand_multi(meta.segs, items, n)
+
+    def _project(self, meta: BatchMeta | None, x, w, names, widths):
+        """x @ w, then the add-ons of the projections `names` (all reading x) on the column
+        slices of the product (`widths` wide).  With overlap, the shrink runs on a second
+        stream while the backbone GEMM runs, and the expand follows the GEMM."""
+        import torch
+        n = x.shape[0]
+        side = self.side if meta is not None and self.side is not None else None
+        if side is not None:
+            cur = torch.cuda.current_stream()
+            side.wait_stream(cur)
+            with torch.cuda.stream(side):
+                self._shrink(meta, x, names)
+        y = torch.mm(x, w)
+        outs, c = [], 0
+        for wd in widths:
+            outs.append(y[:, c:c + wd])
+            c += wd
+        if side is not None:
+            cur.wait_stream(side)
+            self._expand(meta, names, outs, n)
+        elif meta is not None:
+            items = self._items(names, outs, n)
+            if meta.form == "bgmv":
+                B.lora_bgmv_multi(x, meta.idx, items, chunks=self.chunks)
+            else:
+                B.lora_sgmv_shrink_multi(x, meta.segs, items)
+                B.lora_sgmv_expand_multi(meta.segs, items, n)
+        return outs
 
     def forward(self, hidden, cache: KVCache, meta: BatchMeta | None, trace: dict | None = None):
         """hidden [n, h] fp16 -> [n, h] fp16.  meta None runs the backbone alone.  trace, if
@@ -147,36 +192,26 @@ class LoraDecoderLayer:
             raise ValueError(f"metadata for {meta.n} rows, batch of {n}")
 
         a = F.rms_norm(hidden, (h,), bb["norm1"], s.eps)
-        qkv = torch.mm(a, bb["w_qkv"])
-        q, k, v = qkv[:, :h], qkv[:, h:2 * h], qkv[:, 2 * h:]
-        if meta is not None:
-            self._add(meta, a, ("q", "k", "v"), (q, k, v))
+        q, k, v = self._project(meta, a, bb["w_qkv"], ("q", "k", "v"), (h, h, h))
         cache.k_t[:, :, :, -1] = k.view(n, H, dh)
         cache.v[:, :, -1, :] = v.view(n, H, dh)
         S = cache.seq_len
         scores = torch.bmm(q.reshape(n * H, 1, dh), cache.k_t.view(n * H, dh, S))
         probs = torch.softmax(scores.float() * (1.0 / math.sqrt(dh)), dim=-1).half()
         attn = torch.bmm(probs, cache.v.view(n * H, S, dh)).view(n, h)
-        o = torch.mm(attn, bb["w_o"])
-        if meta is not None:
-            self._add(meta, attn, ("o",), (o,))
+        (o,) = self._project(meta, attn, bb["w_o"], ("o",), (h,))
         h1 = hidden + o
         a2 = F.rms_norm(h1, (h,), bb["norm2"], s.eps)
-        gu = torch.mm(a2, bb["w_gu"])
-        g, u = gu[:, :f], gu[:, f:]
-        if meta is not None:
-            self._add(meta, a2, ("gate", "up"), (g, u))
+        g, u = self._project(meta, a2, bb["w_gu"], ("gate", "up"), (f, f))
         act = F.silu(g) * u
-        d = torch.mm(act, bb["w_d"])
-        if meta is not None:
-            self._add(meta, act, ("down",), (d,))
+        (d,) = self._project(meta, act, bb["w_d"], ("down",), (h,))
         if trace is not None:
             for name, t in zip(PROJS, (q, k, v, o, g, u, d)):
                 trace[name] = t.clone()
         return h1 + d
 
 
-def random_layer(shape: LlamaShape, num_slots, rank, max_rows, gen, device="cuda"):
+def random_layer(shape: LlamaShape, num_slots, rank, max_rows, gen, device="cuda", overlap=False):
     """A layer with N(0, 0.02) fp16 backbone and adapter weights drawn on the device, every
     slot of rank `rank` with scale 32 / rank."""
     import torch
@@ -191,4 +226,4 @@ def random_layer(shape: LlamaShape, num_slots, rank, max_rows, gen, device="cuda
     ads = {p: (rnd(num_slots, rank, di), rnd(num_slots, rank, do)) for p, (di, do) in proj_dims(shape).items()}
     rank_t = torch.full((num_slots,), rank, dtype=torch.int32, device=device)
     scale_t = torch.full((num_slots,), 32.0 / rank, dtype=torch.float32, device=device)
-    return LoraDecoderLayer(shape, bb, ads, rank_t, scale_t, max_rows)
+    return LoraDecoderLayer(shape, bb, ads, rank_t, scale_t, max_rows, overlap=overlap)

@@ -32,7 +32,7 @@ def _case(name):
     return case, R.reference(case)
 
 
-def _build(case):
+def _build(case, overlap=False):
     import torch
     from segmented_gather_matmul_amd import layer as LY
     h, f, H, dh, eps = case["dims"]
@@ -41,7 +41,7 @@ def _build(case):
     bb = {k: dev(v) for k, v in case["bb"].items()}
     ads = {p: (dev(st.a_t), dev(st.b)) for p, st in case["stores"].items()}
     n = case["hidden"].shape[0]
-    layer = LY.LoraDecoderLayer(shape, bb, ads, dev(case["rank"]), dev(case["scale"]), max_rows=n)
+    layer = LY.LoraDecoderLayer(shape, bb, ads, dev(case["rank"]), dev(case["scale"]), max_rows=n, overlap=overlap)
     return layer, LY.KVCache(dev(case["k_t"]), dev(case["v_cache"])), dev(case["hidden"])
 
 
@@ -70,15 +70,23 @@ def test_layer_step_matches_reference(name, form):
         got, b = trace[p].cpu().numpy(), base[p].cpu().numpy()
         assert np.array_equal(got[inact].view(np.uint16), b[inact].view(np.uint16)), f"{p}: inactive row changed"
         assert not np.array_equal(got[~inact].view(np.uint16), b[~inact].view(np.uint16)), f"{p}: no add-on landed"
+    # shrinks on a second stream, overlapping the backbone GEMMs: the same bits
+    layer2, cache2, _ = _build(case, overlap=True)
+    trace2 = {}
+    out2 = layer2.forward(hidden, cache2, meta, trace=trace2)
+    torch.cuda.synchronize()
+    for p in R.PROJS:
+        assert torch.equal(trace2[p], trace[p]), f"{p}: overlapped shrink changed the result"
+    assert torch.equal(out2, out)
 
 
-@pytest.mark.parametrize("form", ["bgmv", "sgmv"])
-def test_graph_replays_match_eager(form):
+@pytest.mark.parametrize("form,overlap", [("bgmv", False), ("sgmv", False), ("bgmv", True), ("sgmv", True)])
+def test_graph_replays_match_eager(form, overlap):
     import torch
     from segmented_gather_matmul_amd import layer as LY
     case, _ = _case("tiny")
-    G.say(f"case layer-graph form={form}")
-    layer, cache, hidden = _build(case)
+    G.say(f"case layer-graph form={form} overlap={overlap}")
+    layer, cache, hidden = _build(case, overlap)
     meta = LY.BatchMeta(case["idx"], layer.num_slots, form)
     other = LY.BatchMeta(case["idx"][::-1].copy(), layer.num_slots, "sgmv" if form == "bgmv" else "bgmv")
     eager = layer.forward(hidden, cache, meta).clone()
