@@ -197,11 +197,35 @@ __device__ inline float dot8(uint4 a, uint4 b, float acc)
 __device__ inline float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
 __device__ inline uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
+// One lane-shuffling step of wave_sum: x from the lane that DPP control CTRL names, in the
+// rows of ROWS (bit i = lanes 16i..16i+15); 0 in the other rows.
+template <int CTRL, int ROWS>
+__device__ inline float dpp_take(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, false));
+}
+
+constexpr int kDppSwap1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int kDppSwap2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int kDppRor4 = 0x124;     // row_ror:4
+constexpr int kDppRor8 = 0x128;     // row_ror:8
+constexpr int kDppBcast15 = 0x142;  // row_bcast:15 (lane 15 of each row into the next row)
+constexpr int kDppBcast31 = 0x143;  // row_bcast:31 (lane 31 into rows 2 and 3)
+
+// Sum over the 64 lanes of a wavefront, returned to every lane.  Data-parallel-primitive
+// moves instead of LDS permutes: within each row of 16 lanes, partners 1 and 2 apart,
+// then 4 and 8 apart (rotations), so every lane of a row holds the row's sum; then row 0
+// is added into row 1 and row 2 into row 3, and rows 0 + 1 into row 3.  Lane 63 ends
+// with the total, in an order fixed by this sequence alone.
 __device__ inline float wave_sum(float s)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-    return s;
+    s += dpp_take<kDppSwap1, 0xF>(s);
+    s += dpp_take<kDppSwap2, 0xF>(s);
+    s += dpp_take<kDppRor4, 0xF>(s);
+    s += dpp_take<kDppRor8, 0xF>(s);
+    s += dpp_take<kDppBcast15, 0xA>(s);
+    s += dpp_take<kDppBcast31, 0xC>(s);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 63));
 }
 
 // ------------------------------------------------------------------------ common head
@@ -298,7 +322,7 @@ __device__ inline ShrinkHalf<NR, RJ> load_half(const ShrinkSrc &s, const int (&r
 // rank-rows per pass; d_in striped over the 256 lanes, 16 bytes per lane per load.
 // Lane l sums octets l, l + 256, l + 512, ... of d_in in that order, the octets taken
 // in pairs (o, o + 256) with a zero second term when o + 256 is past the end; then the
-// wavefront's lanes are added by an xor butterfly and the 4 wavefronts in order.  The
+// wavefront's lanes are added by wave_sum and the 4 wavefronts in order.  The
 // loads of several halves of pairs (256 octets each, about 16 loads per lane) are
 // issued together before any is summed, so a long d_in costs few round trips.
 template <bool PAGED, bool PERROW, int RJ, int NR>
