@@ -526,8 +526,10 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Ar
 // ------------------------------------------------------------------------ expand
 // Rank-rows j = w + 4 u, u0 <= u < u0 + RU, that wavefront w of a 256-lane group loads
 // for its 8 columns at c: B[slot][j][c .. c+7], zero where j >= jlim or the columns
-// are out of range.  Paged
-// weights resolve all page ids first, so the data loads go out together.
+// are out of range.  Paged weights resolve all page ids first; the data loads are then
+// issued unconditionally (page 0, which always exists, stands in for a missing entry)
+// and masked, because a load under a per-lane branch is sunk by the compiler next to
+// its conditional use and waited on alone.
 template <bool PAGED, int RU>
 __device__ inline void load_b_octets(const WeightsDev &w, int slot, int jlim, int wave, int u0, int c, bool cin,
                                      uint4 *bv)
@@ -548,11 +550,16 @@ __device__ inline void load_b_octets(const WeightsDev &w, int slot, int jlim, in
             const int j = wave + kWaves * (u0 + u);
             pg[u] = (cin && j < jlim) ? page_entry<true>(w, ptb, j, q) : -1;
         }
+        // every load is issued, in bounds (page 0 stands in for a missing or invalid entry)
+        // and without a branch, then masked: all RU loads are in flight together
+        uint4 t[RU];
 #pragma unroll
-        for (int u = 0; u < RU; ++u) {
-            const int g = page_ok(w, pg[u]);
-            bv[u] = g >= 0 ? load16(page_ptr(w, g, within)) : z4;
-        }
+        for (int u = 0; u < RU; ++u) t[u] = load16(page_ptr(w, max(page_ok(w, pg[u]), 0), within));
+#pragma unroll
+        for (int u = 0; u < RU; ++u) bv[u] = page_ok(w, pg[u]) >= 0 ? t[u] : z4;
+        // keep the loads here: otherwise each is sunk next to its (conditional) use and waited on alone
+#pragma unroll
+        for (int u = 0; u < RU; ++u) asm volatile("" : "+v"(bv[u].x), "+v"(bv[u].y), "+v"(bv[u].z), "+v"(bv[u].w));
     }
 }
 
@@ -1225,7 +1232,9 @@ int expand_impl(void *stream, int32_t n_rows, TileSrc ts, int32_t n_tiles, int32
     } else if constexpr (PERROW) {
         expand_valu_launch<true, 1>(paged, r_max, grid, s, a);
     } else {
-        const int nr = rows_per_pass(max_rows);
+        // Paged B at r_max > 32: 16 page-addressed loads per wavefront in flight already
+        // need ~140 registers, and a second row per pass halves the resident wavefronts.
+        const int nr = paged && r_max > 32 && t_plan_nr == 0 ? 1 : rows_per_pass(max_rows);
         if (nr == 1) expand_valu_launch<false, 1>(paged, r_max, grid, s, a);
         else if (nr == 2) expand_valu_launch<false, 2>(paged, r_max, grid, s, a);
         else expand_valu_launch<false, 4>(paged, r_max, grid, s, a);
