@@ -403,6 +403,65 @@ __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
     }
 }
 
+// Rank slices of an MFMA shrink workgroup: slices g0 .. g0 + NS - 1 of the launch's
+// slice list, each with its projection, first rank-row, the slot's rank and validity.
+template <int NS>
+struct MfmaSlices {
+    int sp[NS], sj0[NS], srank[NS];
+    bool sok[NS];
+};
+
+template <int NS>
+__device__ inline MfmaSlices<NS> mfma_slices(const Args &a, int slot, int g0)
+{
+    MfmaSlices<NS> m;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+        const int sl = g0 + q;
+        m.sp[q] = proj_of(a, min(sl, a.per_tile - 1));
+        m.sj0[q] = 16 * (sl - a.off[m.sp[q]]);
+        const WeightsDev &w = a.p[m.sp[q]].w;
+        m.sok[q] = sl < a.per_tile && slot < w.num_slots && m.sj0[q] < w.r_max;
+        m.srank[q] = m.sok[q] ? slot_rank(w, slot) : 0;
+    }
+    return m;
+}
+
+// The MFMA shrinks' last step: every wavefront's 16x16 accumulators go to LDS and are
+// added in wavefront order, one rank slice at a time; columns at or past the rank are
+// written as 0.  red holds W * 1024 floats.
+template <int MTX, int NS>
+__device__ inline void mfma_shrink_store(const Args &a, const TileHead &th, const MfmaSlices<NS> &m, int MT,
+                                         const f4_t (&acc)[NS][MTX], float *red)
+{
+    constexpr int W = kMfmaShrinkThreads / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+    // D layout: lane holds rows 4*lg + e of the slice, rank column li.
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+#pragma unroll
+        for (int mt = 0; mt < MTX; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[wave * 1024 + mt * 256 + (4 * lg + e) * 16 + li] = acc[q][mt][e];
+        __syncthreads();
+        if (m.sok[q] && m.srank[q] > 0) {
+            const ProjDev &pd = a.p[m.sp[q]];
+            for (int o = tid; o < MT * 256; o += kMfmaShrinkThreads) {
+                const int mt = o >> 8, i = (o >> 4) & 15, j = o & 15;
+                const int rr = 16 * mt + i, col = m.sj0[q] + j;
+                if (rr >= th.nrows || col >= pd.w.r_max) continue;
+                const int row = row_of<false>(a.ts, th.pos0 + rr, a.n_rows);
+                if (row < 0) continue;
+                float s = 0.f;
+#pragma unroll
+                for (int w = 0; w < W; ++w) s += red[w * 1024 + o];
+                pd.v[(int64_t)row * pd.ldv + col] = col < m.srank[q] ? s : 0.f;
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // MFMA shrink for tiles of up to 64 rows: v_mfma_f32_16x16x32_f16 over (16-row
 // slices) x (16-rank slices).  A workgroup takes NS consecutive rank slices of the
 // launch's slice list (projection by projection), so the projections of one launch
@@ -427,18 +486,14 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Ar
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;       // operand row/col, k-group of the lane
     const int MT = min((th.nrows + 15) >> 4, MTX);
-    // this workgroup's rank slices: projection, first rank-row, this lane's A^T rank-row
-    int sp[NS], sj0[NS], srank[NS];
+    // this workgroup's rank slices, and this lane's A^T rank-row in each
+    const MfmaSlices<NS> m = mfma_slices<NS>(a, th.slot, g0);
+    const int *sp = m.sp, *sj0 = m.sj0, *srank = m.srank;
+    const bool *sok = m.sok;
     const uint16_t *arow[NS];
-    bool sok[NS];
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
-        const int sl = g0 + q;
-        sp[q] = proj_of(a, min(sl, a.per_tile - 1));
-        sj0[q] = 16 * (sl - a.off[sp[q]]);
         const WeightsDev &w = a.p[sp[q]].w;
-        sok[q] = sl < a.per_tile && th.slot < w.num_slots && sj0[q] < w.r_max;
-        srank[q] = sok[q] ? slot_rank(w, th.slot) : 0;
         const int jcol = sj0[q] + li;
         arow[q] = (!PAGED && sok[q] && jcol < w.r_max) ? dense_row<false>(w, th.slot, jcol) : nullptr;
     }
@@ -497,30 +552,107 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Ar
                                                                         acc[q][mt], 0, 0, 0);
             }
     }
-    // D layout: lane holds rows 4*lg + e of the slice, rank column li.
+    mfma_shrink_store<MTX, NS>(a, th, m, MT, acc, red);
+}
+
+// The dense MFMA shrink with x and A^T staged through LDS.  Work item, operand values
+// and accumulation order are those of lora_shrink_mfma_kernel (wavefront w owns k-steps
+// w, w + 16, ... and applies them in that order; the sums are added in LDS in wavefront
+// order), so the two give the same bits; only the data movement differs.  Each
+// 512-column chunk (one k-step per wavefront) of the tile's x rows and of the slices'
+// A^T rank-rows is loaded one whole 1 KB row per wavefront load (full cache lines,
+// where the operand layout would fetch 64 bytes from each of 16 rows), written to LDS,
+// and the MFMA operands are read from LDS while the next chunk's loads are in flight.
+constexpr int kStageCols = 512;               // columns per chunk: 16 k-steps of 32
+constexpr int kStageStride = kStageCols + 8;  // halves per staged row; the pad puts the 16
+                                              // rows an operand read touches in distinct banks
+
+__host__ __device__ constexpr int stage_rows(int mtx, int ns) { return 16 * (mtx + ns); }
+
+__host__ __device__ constexpr size_t stage_lds_bytes(int mtx, int ns)
+{
+    return (size_t)stage_rows(mtx, ns) * kStageStride * 2 > (size_t)(kMfmaShrinkThreads / 64) * 1024 * 4
+               ? (size_t)stage_rows(mtx, ns) * kStageStride * 2
+               : (size_t)(kMfmaShrinkThreads / 64) * 1024 * 4;
+}
+
+// Octet k .. k+7 of every staged row this wavefront loads; zero past d_in or for rows
+// without a source.
+template <int RPW>
+__device__ inline void stage_load(const uint16_t *const (&src)[RPW], int k, int d_in, uint4 (&st)[RPW])
+{
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int q = 0; q < NS; ++q) {
+    for (int i = 0; i < RPW; ++i) st[i] = (src[i] && k < d_in) ? load16(src[i] + k) : z4;
+}
+
+template <int MTX, int NS>
+__global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_kernel(Args a)
+{
+    constexpr int W = kMfmaShrinkThreads / 64;
+    constexpr int XR = 16 * MTX, ROWS = stage_rows(MTX, NS);
+    constexpr int RPW = (ROWS + W - 1) / W;  // staged rows per wavefront: rows wave, wave + W, ...
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t *stg = reinterpret_cast<uint16_t *>(smem);  // [ROWS][kStageStride]
+    float *red = reinterpret_cast<float *>(smem);        // reused after the k loop
+    const int wi = work_item(blockIdx.x, a.grid);
+    const int groups = (a.per_tile + NS - 1) / NS;
+    const int tile = wi / groups, g0 = (wi - tile * groups) * NS;
+    if (tile >= a.n_tiles) return;
+    const TileHead th = tile_head<false>(a.ts, a.p[0].w, tile);
+    if (th.slot < 0 || th.nrows <= 0) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, lg = lane >> 4;
+    const int MT = min((th.nrows + 15) >> 4, MTX);
+    const MfmaSlices<NS> m = mfma_slices<NS>(a, th.slot, g0);
+    // staged row r: x row r of the tile (r < XR), else A^T rank-row of slice (r - XR) / 16
+    const uint16_t *src[RPW];
 #pragma unroll
-        for (int mt = 0; mt < MTX; ++mt)
+    for (int i = 0; i < RPW; ++i) {
+        const int r = i * W + wave;
+        src[i] = nullptr;
+        if (r < XR) {
+            const int row = r < th.nrows ? row_of<false>(a.ts, th.pos0 + r, a.n_rows) : -1;
+            if (row >= 0) src[i] = a.x + (int64_t)row * a.ldx;
+        } else if (r < ROWS) {
+            const int q = (r - XR) >> 4, j = m.sj0[q] + ((r - XR) & 15);
+            const WeightsDev &w = a.p[m.sp[q]].w;
+            if (m.sok[q] && j < w.r_max) src[i] = dense_row<false>(w, th.slot, j);
+        }
+    }
+    f4_t acc[NS][MTX];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) red[wave * 1024 + mt * 256 + (4 * lg + e) * 16 + li] = acc[q][mt][e];
+    for (int q = 0; q < NS; ++q)
+#pragma unroll
+        for (int mt = 0; mt < MTX; ++mt) acc[q][mt] = f4_t{0.f, 0.f, 0.f, 0.f};
+    const int d_in = a.p[0].w.d_in;
+    const int chunks = (d_in + kStageCols - 1) / kStageCols;
+    const int kc = 32 * wave + 8 * lg;  // this lane's operand columns within a chunk
+    uint4 st[RPW];
+    stage_load<RPW>(src, 8 * lane, d_in, st);
+    for (int ck = 0; ck < chunks; ++ck) {
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+            const int r = i * W + wave;
+            if (r < ROWS) *reinterpret_cast<uint4 *>(stg + r * kStageStride + 8 * lane) = st[i];
+        }
         __syncthreads();
-        if (sok[q] && srank[q] > 0) {
-            const ProjDev &pd = a.p[sp[q]];
-            for (int o = tid; o < MT * 256; o += kMfmaShrinkThreads) {
-                const int mt = o >> 8, i = (o >> 4) & 15, j = o & 15;
-                const int rr = 16 * mt + i, col = sj0[q] + j;
-                if (rr >= th.nrows || col >= pd.w.r_max) continue;
-                const int row = row_of<false>(a.ts, th.pos0 + rr, a.n_rows);
-                if (row < 0) continue;
-                float s = 0.f;
+        if (ck + 1 < chunks) stage_load<RPW>(src, (ck + 1) * kStageCols + 8 * lane, d_in, st);
+        h8_t bop[NS];
 #pragma unroll
-                for (int w = 0; w < W; ++w) s += red[w * 1024 + o];
-                pd.v[(int64_t)row * pd.ldv + col] = col < srank[q] ? s : 0.f;
+        for (int q = 0; q < NS; ++q) bop[q] = *reinterpret_cast<const h8_t *>(stg + (XR + 16 * q + li) * kStageStride + kc);
+#pragma unroll
+        for (int mt = 0; mt < MTX; ++mt) {
+            if (mt < MT) {
+                const h8_t xop = *reinterpret_cast<const h8_t *>(stg + (16 * mt + li) * kStageStride + kc);
+#pragma unroll
+                for (int q = 0; q < NS; ++q)
+                    acc[q][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, bop[q], acc[q][mt], 0, 0, 0);
             }
         }
         __syncthreads();
     }
+    mfma_shrink_store<MTX, NS>(a, th, m, MT, acc, red);
 }
 
 // ------------------------------------------------------------------------ expand
@@ -1170,23 +1302,37 @@ int shrink_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSr
     const dim3 grid((unsigned)a.grid);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (mfma) {
-        // rank slices per workgroup: all of the tile's (up to 4) share one read of x
-        const int ns = paged ? 1 : (a.per_tile + (a.per_tile + 3) / 4 - 1) / ((a.per_tile + 3) / 4);
+        // rank slices per workgroup: all of the tile's (up to 4, up to 3 with 64-row tiles,
+        // whose staged chunk and prefetch registers leave no room for a fourth) share one
+        // read of x
+        const int mtx = (max_rows + 15) / 16;
+        const int ns_max = mtx > 2 ? 3 : 4;
+        const int ns = paged ? 1 : (a.per_tile + (a.per_tile + ns_max - 1) / ns_max - 1) /
+                                       ((a.per_tile + ns_max - 1) / ns_max);
         a.grid = pad8((int64_t)n_tiles * ((a.per_tile + ns - 1) / ns));
         const dim3 g((unsigned)a.grid);
-        const int mtx = (max_rows + 15) / 16;
-#define LORA_SHRINK_MFMA(MTX)                                                                         \
-    do {                                                                                             \
-        if (paged) launch(lora_shrink_mfma_kernel<true, MTX, 1>, g, kMfmaShrinkThreads, 0, s, a);    \
-        else if (ns == 1) launch(lora_shrink_mfma_kernel<false, MTX, 1>, g, kMfmaShrinkThreads, 0, s, a); \
-        else if (ns == 2) launch(lora_shrink_mfma_kernel<false, MTX, 2>, g, kMfmaShrinkThreads, 0, s, a); \
-        else if (ns == 3) launch(lora_shrink_mfma_kernel<false, MTX, 3>, g, kMfmaShrinkThreads, 0, s, a); \
-        else launch(lora_shrink_mfma_kernel<false, MTX, 4>, g, kMfmaShrinkThreads, 0, s, a);          \
-    } while (0)
-        if (mtx <= 1) LORA_SHRINK_MFMA(1);
-        else if (mtx == 2) LORA_SHRINK_MFMA(2);
-        else LORA_SHRINK_MFMA(4);
-#undef LORA_SHRINK_MFMA
+#define LORA_SHRINK_STAGED(MTX, NS) \
+    launch(lora_shrink_mfma_staged_kernel<MTX, NS>, g, kMfmaShrinkThreads, stage_lds_bytes(MTX, NS), s, a)
+        if (paged) {
+            if (mtx <= 1) launch(lora_shrink_mfma_kernel<true, 1, 1>, g, kMfmaShrinkThreads, 0, s, a);
+            else if (mtx == 2) launch(lora_shrink_mfma_kernel<true, 2, 1>, g, kMfmaShrinkThreads, 0, s, a);
+            else launch(lora_shrink_mfma_kernel<true, 4, 1>, g, kMfmaShrinkThreads, 0, s, a);
+        } else if (mtx <= 1) {
+            if (ns == 1) LORA_SHRINK_STAGED(1, 1);
+            else if (ns == 2) LORA_SHRINK_STAGED(1, 2);
+            else if (ns == 3) LORA_SHRINK_STAGED(1, 3);
+            else LORA_SHRINK_STAGED(1, 4);
+        } else if (mtx == 2) {
+            if (ns == 1) LORA_SHRINK_STAGED(2, 1);
+            else if (ns == 2) LORA_SHRINK_STAGED(2, 2);
+            else if (ns == 3) LORA_SHRINK_STAGED(2, 3);
+            else LORA_SHRINK_STAGED(2, 4);
+        } else {
+            if (ns == 1) LORA_SHRINK_STAGED(4, 1);
+            else if (ns == 2) LORA_SHRINK_STAGED(4, 2);
+            else LORA_SHRINK_STAGED(4, 3);
+        }
+#undef LORA_SHRINK_STAGED
     } else if constexpr (PERROW) {
         shrink_valu_launch<true, 1>(paged, a.jw, grid, s, a);
     } else {

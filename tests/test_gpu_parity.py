@@ -361,3 +361,33 @@ def test_mfma_paths_with_rank_not_multiple_of_16(layout):
     dc = G.DeviceCase(x, y0, 20)
     y, v = G.run_sgmv(w, dc, seg_ptr=seg_ptr, seg_slot=seg_slot, max_tile_rows=16)
     G.check(dc, y, v, y_ref, v_ref, G.active_rows(idx, rank), f"rmax20-{layout}")
+
+
+@pytest.mark.parametrize("max_tile_rows", [16, 32, 64])
+@pytest.mark.parametrize("d_in", [1288, 4096])
+def test_mfma_dense_and_paged_are_bitwise_identical(max_tile_rows, d_in):
+    """Long segments on the MFMA kernels: the dense shrink stages x and A^T through LDS
+    and groups up to 4 rank slices per workgroup, the paged one reads its operands
+    straight from memory one slice at a time; both sum every element in the same order,
+    so v and y agree bit for bit (d_in 1288 leaves a ragged last 512-column chunk)."""
+    lens = [150, 9, 70, 33, 1, 64]
+    seg_ptr = wl.segments_from_lengths(lens)
+    S = len(lens)
+    seg_slot = np.arange(S, dtype=np.int32)[::-1].copy()
+    rank = np.array([64, 16, 33, 8, 1, 48], dtype=np.int32)
+    scale = wl.scale_for_rank(rank)
+    d_out = 1032
+    dense = wl.dense_store(23, 0, S, d_in, d_out, rank, scale, r_max=64)
+    paged = wl.paged_store(23, 0, S, d_in, d_out, rank, scale, 8, spare_pages=5)
+    idx = np.repeat(seg_slot, lens).astype(np.int32)
+    x, y0 = wl.activations(23, 0, len(idx), d_in, d_out)
+    G.say(f"case mfma-dense-vs-paged d_in={d_in} tiles={max_tile_rows}")
+    outs = []
+    for store in (dense, paged):
+        dc = G.DeviceCase(x, y0, 64)
+        outs.append(G.run_sgmv(B.weights_from_store(store), dc, seg_ptr=seg_ptr, seg_slot=seg_slot,
+                               max_tile_rows=max_tile_rows))
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32)), "v"
+    assert np.array_equal(outs[0][0].view(np.uint16), outs[1][0].view(np.uint16)), "y"
+    y_ref, v_ref = _oracle(dense, x, y0, idx)
+    G.check(dc, *outs[1], y_ref, v_ref, G.active_rows(idx, rank), f"mfma-dense-vs-paged-{d_in}-{max_tile_rows}")
