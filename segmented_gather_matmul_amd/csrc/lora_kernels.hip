@@ -350,7 +350,6 @@ __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_oct = pd.w.d_in >> 3;
     const int n_half = 2 * ((n_oct + 2 * kThreads - 1) / (2 * kThreads));  // halves of octet pairs, even
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
     for (int rg = 0; rg < th.nrows; rg += NR) {
         int rows[NR];
 #pragma unroll
