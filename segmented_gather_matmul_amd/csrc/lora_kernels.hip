@@ -661,36 +661,59 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_ke
 // issued unconditionally (page 0, which always exists, stands in for a missing entry)
 // and masked, because a load under a per-lane branch is sunk by the compiler next to
 // its conditional use and waited on alone.
+// Paged part of load_b_octets: the first N of the RU entries (the rest zero).  Every
+// load is issued, in bounds (page 0 stands in for a missing or invalid entry) and
+// without a branch, then masked: all N loads are in flight together.
+template <int N, int RU>
+__device__ inline void load_b_paged(const WeightsDev &w, int slot, int jlim, int wave, int u0, int c, bool cin,
+                                    uint4 *bv)
+{
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
+    const int P = w.page_elems, q = c / P, within = c - q * P;
+    const int64_t ptb = pt_base<true>(w, slot);
+    int pg[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+        const int j = wave + kWaves * (u0 + u);
+        pg[u] = (cin && j < jlim) ? page_entry<true>(w, ptb, j, q) : -1;
+    }
+    uint4 t[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u) t[u] = load16(page_ptr(w, max(page_ok(w, pg[u]), 0), within));
+#pragma unroll
+    for (int u = 0; u < N; ++u) bv[u] = page_ok(w, pg[u]) >= 0 ? t[u] : z4;
+#pragma unroll
+    for (int u = N; u < RU; ++u) bv[u] = z4;
+    // keep the loads here: otherwise each is sunk next to its (conditional) use and waited on alone
+#pragma unroll
+    for (int u = 0; u < RU; ++u) asm volatile("" : "+v"(bv[u].x), "+v"(bv[u].y), "+v"(bv[u].z), "+v"(bv[u].w));
+}
+
+// Rank-rows j = w + 4 u, u0 <= u < u0 + RU, that wavefront w of a 256-lane group loads
+// for its 8 columns at c: B[slot][j][c .. c+7], zero where j >= jlim or the columns
+// are out of range.  Paged weights resolve all page ids first, then issue only as many
+// data loads as the rank needs (a quarter, half or all of RU, picked once per
+// wavefront), unconditionally and masked, because a load under a per-lane branch is
+// sunk by the compiler next to its conditional use and waited on alone.
 template <bool PAGED, int RU>
 __device__ inline void load_b_octets(const WeightsDev &w, int slot, int jlim, int wave, int u0, int c, bool cin,
                                      uint4 *bv)
 {
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
     if (!PAGED) {
+        const uint4 z4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
             const int j = wave + kWaves * (u0 + u);
             bv[u] = (cin && j < jlim) ? load16(dense_row<true>(w, slot, j) + c) : z4;
         }
+    } else if constexpr (RU >= 8) {
+        // entries this wavefront needs: rank-rows wave + 4 u below jlim, from u0 on
+        const int need = (jlim - wave + kWaves - 1) / kWaves - u0;
+        if (need <= RU / 4) load_b_paged<RU / 4, RU>(w, slot, jlim, wave, u0, c, cin, bv);
+        else if (need <= RU / 2) load_b_paged<RU / 2, RU>(w, slot, jlim, wave, u0, c, cin, bv);
+        else load_b_paged<RU, RU>(w, slot, jlim, wave, u0, c, cin, bv);
     } else {
-        const int P = w.page_elems, q = c / P, within = c - q * P;
-        const int64_t ptb = pt_base<true>(w, slot);
-        int pg[RU];
-#pragma unroll
-        for (int u = 0; u < RU; ++u) {
-            const int j = wave + kWaves * (u0 + u);
-            pg[u] = (cin && j < jlim) ? page_entry<true>(w, ptb, j, q) : -1;
-        }
-        // every load is issued, in bounds (page 0 stands in for a missing or invalid entry)
-        // and without a branch, then masked: all RU loads are in flight together
-        uint4 t[RU];
-#pragma unroll
-        for (int u = 0; u < RU; ++u) t[u] = load16(page_ptr(w, max(page_ok(w, pg[u]), 0), within));
-#pragma unroll
-        for (int u = 0; u < RU; ++u) bv[u] = page_ok(w, pg[u]) >= 0 ? t[u] : z4;
-        // keep the loads here: otherwise each is sunk next to its (conditional) use and waited on alone
-#pragma unroll
-        for (int u = 0; u < RU; ++u) asm volatile("" : "+v"(bv[u].x), "+v"(bv[u].y), "+v"(bv[u].z), "+v"(bv[u].w));
+        load_b_paged<RU, RU>(w, slot, jlim, wave, u0, c, cin, bv);
     }
 }
 
