@@ -64,7 +64,7 @@ def workload_spec(name, rows=None):
         b = wl.batch_paged_zipf(256, 2000)
         tp8 = name.endswith("tp8")
         return dict(cfg_id=5, shapes=wl.LLAMA2_70B_TP8 if tp8 else wl.LLAMA2_70B, layers=2, num_slots=2000,
-                    rank=rank, scale=wl.scale_for_rank(rank), batch=b, form="sgmv", layout="paged",
+                    rank=rank, scale=wl.scale_for_rank(rank), batch=b, form="mixed", layout="paged",
                     page_elems=128 if tp8 else 1024, model="Llama-2-70B, one GPU of 8-way TP" if tp8 else "Llama-2-70B",
                     popularity="zipf1.2")
     raise SystemExit(f"unknown workload {name}")
@@ -87,8 +87,8 @@ def make_ops(spec, layers, device, tile_rows=None):
     r_max = int(rank.max())
     idx_d = torch.from_numpy(b.idx.astype(np.int32)).to(device)
     segs = None
-    if spec["form"].startswith("sgmv"):
-        if spec["form"] == "sgmv":
+    if spec["form"].startswith("sgmv") or spec["form"] == "mixed":
+        if spec["form"] in ("sgmv", "mixed"):
             row_map, seg_ptr, seg_slot, n_act = B.lora_build_segments(b.idx, S)
             tiles = B.lora_build_tiles(seg_ptr, seg_slot, tile_rows)
             segs = B.segments_to_device(tiles, row_map, n_act, device)
@@ -139,6 +139,7 @@ def make_ops(spec, layers, device, tile_rows=None):
                                      b_pt_off=torch.from_numpy(b_off).to(device))
                 op.v = torch.zeros((n, ldv), dtype=torch.float32, device=device)
                 op.idx, op.segs = idx_d, segs
+                op.expand_per_row = spec["form"] == "mixed"
                 ops.append(op)
             groups.append(ops)
     return groups
@@ -158,11 +159,12 @@ def launch_unit(kind, ops, fused_chunks):
             B.lora_bgmv_shrink_multi(op0.x, op0.idx, items)
         else:
             B.lora_bgmv_expand_multi(op0.idx, items, n)
+    elif kind == "shrink":
+        B.lora_sgmv_shrink_multi(op0.x, op0.segs, items)
+    elif op0.expand_per_row:
+        B.lora_bgmv_expand_multi(op0.idx, items, n)
     else:
-        if kind == "shrink":
-            B.lora_sgmv_shrink_multi(op0.x, op0.segs, items)
-        else:
-            B.lora_sgmv_expand_multi(op0.segs, items, n)
+        B.lora_sgmv_expand_multi(op0.segs, items, n)
 
 
 def launches(groups, grouped, fused_chunks):
@@ -684,8 +686,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile-rows", type=int, default=None,
                     help="tile height for the segment form (default: lora_pick_tile_rows)")
-    ap.add_argument("--form", choices=["bgmv", "sgmv"], default=None,
-                    help="per-row slots (bgmv) or rows grouped by adapter (sgmv); default: the workload's own")
+    ap.add_argument("--form", choices=["bgmv", "sgmv", "mixed"], default=None,
+                    help="per-row slots (bgmv), rows grouped by adapter (sgmv), or the segment-form shrink with "
+                         "the per-row expand (mixed); default: the workload's own")
     ap.add_argument("--fused-chunks", type=int, default=-1,
                     help="per-row form: -1 = separate shrink and expand launches (the library's choice); c >= 1 = "
                          "one launch per unit, each workgroup covering c 512-column chunks")

@@ -74,6 +74,18 @@ def run_bgmv(w: B.Weights, dc: DeviceCase, idx, split_calls=False):
     return dc.results()
 
 
+def run_mixed(w: B.Weights, dc: DeviceCase, idx):
+    """Segment-form shrink (rows grouped by the library's builder) followed by the
+    per-row expand: v is indexed by row in both forms, so the two compose."""
+    t = torch()
+    row_map, seg_ptr, seg_slot, n_act = B.lora_build_segments(idx, w.num_slots)
+    tiles = B.lora_build_tiles(seg_ptr, seg_slot)
+    segs = B.segments_to_device(tiles, row_map, n_act)
+    B.lora_sgmv_shrink(dc.v, dc.x, w, segs)
+    B.lora_bgmv_expand(dc.y, dc.v, t.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda(), w)
+    return dc.results()
+
+
 def run_sgmv(w: B.Weights, dc: DeviceCase, idx=None, seg_ptr=None, seg_slot=None, max_tile_rows=None):
     """Segment form.  With idx: rows are grouped by the library's builder (row_map);
     with seg_ptr/seg_slot: contiguous segments, no row map."""

@@ -40,6 +40,8 @@ def _run(form, w, dc, idx, seg_ptr=None, seg_slot=None):
         return G.run_sgmv(w, dc, idx=idx)
     if form == "sgmv":
         return G.run_sgmv(w, dc, seg_ptr=seg_ptr, seg_slot=seg_slot)
+    if form == "mixed":
+        return G.run_mixed(w, dc, idx)
     raise ValueError(form)
 
 
@@ -86,7 +88,7 @@ def test_prefill_7b(shape):
 
 
 @pytest.mark.parametrize("d_out", [1024, 8192, 28672])
-@pytest.mark.parametrize("form", ["bgmv", "sgmv_rowmap"])
+@pytest.mark.parametrize("form", ["bgmv", "sgmv_rowmap", "mixed"])
 def test_paged_mixed_rank_70b(d_out, form):
     import torch
     d_in, P, S = 8192, 1024, 2000
@@ -147,7 +149,7 @@ def _mixed_rank_store(cfg, d_in, d_out, S=7, paged_P=None):
 
 
 @pytest.mark.parametrize("layout", ["dense", "paged8", "paged56"])
-@pytest.mark.parametrize("form", ["bgmv", "sgmv_rowmap"])
+@pytest.mark.parametrize("form", ["bgmv", "sgmv_rowmap", "mixed"])
 def test_ragged_widths_mixed_ranks(layout, form):
     d_in, d_out = 1288, 1064        # neither is a multiple of the 256-wide k-block or 512-wide column chunk
     P = {"dense": None, "paged8": 8, "paged56": 56}[layout]
