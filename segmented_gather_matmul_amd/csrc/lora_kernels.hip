@@ -840,18 +840,24 @@ __global__ __launch_bounds__(kThreads) void lora_expand_valu_kernel(Args a)
 // bits kept) and the accumulator starts from y.  MFMAs go in pairs whose output
 // columns are interleaved so that each lane ends up with 8 consecutive columns of one
 // row: y is read and written with 16-byte accesses.  The next slice's y and v are
-// requested before the current slice's products.
+// requested before the current slice's products.  With SY (dense weights) the slice's
+// y passes through LDS: each wavefront loads and stores whole 1 KB rows (full cache
+// lines, where the operand layout touches 64 bytes of each of 16 rows), and the lanes
+// read and write their operand layout in LDS; the arithmetic is the same, so SY
+// changes no bits.
 constexpr int kBtPad = 4;  // halves of padding per column of the transposed B chunk
+constexpr int kYStride = kCols + 8;  // halves per row of the staged y slice (the pad spreads rows over banks)
 
 __host__ __device__ constexpr int bt_stride(int rq) { return 16 * rq + kBtPad; }
 
-template <bool PAGED, int RQ>
+template <bool PAGED, int RQ, bool SY>
 __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args a)
 {
     constexpr int kStage = RQ * 16 * (kCols / 8) / kThreads;  // 16-byte loads per lane to stage B
     constexpr int KS = bt_stride(RQ);
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t *bt = reinterpret_cast<uint16_t *>(smem);  // bt[col * KS + k] = B[k][c0 + col]
+    uint16_t *ys = bt + kCols * KS;                      // SY: y of the slice, [16][kYStride]
     const Item it = work(a);
     if (!it.ok) return;
     const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
@@ -874,7 +880,8 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args a)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int col = cw + 32 * p + 8 * lg;
-            yq[p] = (row >= 0 && col < pd.w.d_out) ? load16(pd.y + (int64_t)row * pd.ldy + col) : make_uint4(0, 0, 0, 0);
+            yq[p] = (!SY && row >= 0 && col < pd.w.d_out) ? load16(pd.y + (int64_t)row * pd.ldy + col)
+                                                           : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int kq = 0; kq < RQ; ++kq) {
@@ -883,6 +890,28 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args a)
             if (row >= 0 && j < pd.w.r_max) vq[kq] = *reinterpret_cast<const float4 *>(pd.v + (int64_t)row * pd.ldv + j);
         }
     };
+    // SY: wavefront w moves rows 4 w .. 4 w + 3 of a slice between memory and LDS, one
+    // whole 1 KB row per load or store (lane l: columns c0 + 8 l .. + 7)
+    const int ycol = c0 + 8 * lane;
+    const bool ycin = ycol < pd.w.d_out;
+    auto stage_rows = [&](int mt, int (&lrow)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = 16 * mt + 4 * wave + i;
+            lrow[i] = (mt < MT && rr < th.nrows) ? row_of<false>(a.ts, th.pos0 + rr, a.n_rows) : -1;
+        }
+    };
+    auto stage_load = [&](const int (&lrow)[4], uint4 (&yr)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            yr[i] = (lrow[i] >= 0 && ycin) ? load16(pd.y + (int64_t)lrow[i] * pd.ldy + ycol) : make_uint4(0, 0, 0, 0);
+    };
+    int lrow[4] = {-1, -1, -1, -1};
+    uint4 yr[4];
+    if (SY) {
+        stage_rows(0, lrow);
+        stage_load(lrow, yr);
+    }
     int row = slice_row(0);
     uint4 yq[4];
     float4 vq[RQ];
@@ -930,11 +959,26 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args a)
         if (rank <= 0) return;
     }
     for (int mt = 0; mt < MT; ++mt) {
+        if (SY) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(ys + (4 * wave + i) * kYStride + 8 * lane) = yr[i];
+            __syncthreads();
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                yq[p] = *reinterpret_cast<const uint4 *>(ys + li * kYStride + 128 * wave + 32 * p + 8 * lg);
+        }
         // the next slice's loads go out before this slice's products
         const int row_n = slice_row(mt + 1);
         uint4 yn[4];
         float4 vn[RQ];
-        if (mt + 1 < MT) load_yv(row_n, yn, vn);
+        int lrow_n[4] = {-1, -1, -1, -1};
+        if (mt + 1 < MT) {
+            load_yv(row_n, yn, vn);
+            if (SY) {
+                stage_rows(mt + 1, lrow_n);
+                stage_load(lrow_n, yr);
+            }
+        }
         f4_t acc[4][2];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -971,19 +1015,32 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args a)
                     acc[p][h] += lo * (1.f / 2048.f);
                 }
         }
-        if (row >= 0) {
+        if (SY || row >= 0) {
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const int col = cw + 32 * p + 8 * lg;
-                if (col >= pd.w.d_out) continue;
+                if (!SY && col >= pd.w.d_out) continue;
                 uint32_t o[4];
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int e2 = 0; e2 < 2; ++e2)
                         o[2 * h + e2] = (uint32_t)f2h(acc[p][h][2 * e2]) | ((uint32_t)f2h(acc[p][h][2 * e2 + 1]) << 16);
-                *reinterpret_cast<uint4 *>(pd.y + (int64_t)row * pd.ldy + col) = make_uint4(o[0], o[1], o[2], o[3]);
+                const uint4 ov = make_uint4(o[0], o[1], o[2], o[3]);
+                if (SY) *reinterpret_cast<uint4 *>(ys + li * kYStride + 128 * wave + 32 * p + 8 * lg) = ov;
+                else *reinterpret_cast<uint4 *>(pd.y + (int64_t)row * pd.ldy + col) = ov;
             }
+        }
+        if (SY) {
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (lrow[i] >= 0 && ycin)
+                    *reinterpret_cast<uint4 *>(pd.y + (int64_t)lrow[i] * pd.ldy + ycol) =
+                        *reinterpret_cast<const uint4 *>(ys + (4 * wave + i) * kYStride + 8 * lane);
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lrow[i] = lrow_n[i];
         }
         if (mt + 1 < MT) {
             row = row_n;
@@ -1389,9 +1446,10 @@ int expand_impl(void *stream, int32_t n_rows, TileSrc ts, int32_t n_tiles, int32
     if (mfma) {
         const int rq = (r_max + 15) / 16;
         const size_t lds = (size_t)kCols * bt_stride(rq) * sizeof(uint16_t);
-#define LORA_EXPAND_MFMA(RQ)                                                        \
-    (paged ? launch(lora_expand_mfma_kernel<true, RQ>, grid, kThreads, lds, s, a)   \
-           : launch(lora_expand_mfma_kernel<false, RQ>, grid, kThreads, lds, s, a))
+        const size_t lds_sy = lds + (size_t)16 * kYStride * sizeof(uint16_t);  // dense: plus the staged y slice
+#define LORA_EXPAND_MFMA(RQ)                                                                 \
+    (paged ? launch(lora_expand_mfma_kernel<true, RQ, false>, grid, kThreads, lds, s, a)     \
+           : launch(lora_expand_mfma_kernel<false, RQ, true>, grid, kThreads, lds_sy, s, a))
         if (rq == 1) LORA_EXPAND_MFMA(1);
         else if (rq == 2) LORA_EXPAND_MFMA(2);
         else if (rq == 3) LORA_EXPAND_MFMA(3);
