@@ -59,14 +59,23 @@ def workload_spec(name, rows=None):
         return dict(cfg_id=4, shapes=wl.LLAMA2_7B, layers=4, num_slots=16, rank=np.full(16, 16, np.int32),
                     scale=np.full(16, 2.0, np.float32), batch=b, form="sgmv_contiguous", layout="dense",
                     model="Llama-2-7B", popularity="distinct")
-    if name in ("paged_70b", "paged_70b_tp8"):
+    if name in ("paged_70b", "paged_70b_tp8", "paged_70b_tp8_slora"):
         rank = wl.paged_ranks(2000)
         b = wl.batch_paged_zipf(256, 2000)
-        tp8 = name.endswith("tp8")
-        return dict(cfg_id=5, shapes=wl.LLAMA2_70B_TP8 if tp8 else wl.LLAMA2_70B, layers=2, num_slots=2000,
+        tp8 = "tp8" in name
+        slora = name.endswith("slora")
+        spec = dict(cfg_id=5, shapes=wl.LLAMA2_70B_TP8 if tp8 else wl.LLAMA2_70B, layers=2, num_slots=2000,
                     rank=rank, scale=wl.scale_for_rank(rank), batch=b, form="mixed", layout="paged",
                     page_elems=128 if tp8 else 1024, model="Llama-2-70B, one GPU of 8-way TP" if tp8 else "Llama-2-70B",
                     popularity="zipf1.2")
+        if slora:
+            # A of the column-parallel projections split by rank columns over the 8 GPUs
+            # (S-LoRA's partition): this GPU's shrink covers ceil(r / 8) rank-rows of the
+            # full-width input; the expand still reads all r (after the all-gather of v,
+            # which one GPU leaves out) into its d_out / 8 columns
+            spec["shrink_rank"] = {p: (rank + 7) // 8 for p in ("q", "k", "v", "gate", "up")}
+            spec["model"] = "Llama-2-70B, one GPU of 8-way TP, A split by rank columns"
+        return spec
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -137,6 +146,22 @@ def make_ops(spec, layers, device, tile_rows=None):
                                      page_table=torch.from_numpy(pt).to(device),
                                      a_pt_off=torch.from_numpy(a_off).to(device),
                                      b_pt_off=torch.from_numpy(b_off).to(device))
+                op.ws, op.shrink_rank = op.w, None
+                if pname in spec.get("shrink_rank", {}):
+                    # this GPU's rank-column shard of A: its own pages (each shard rank-row
+                    # carries one page of B that no kernel reads, as the descriptor wants both)
+                    from segmented_gather_matmul_amd import workloads as wl
+                    P = spec["page_elems"]
+                    rs = spec["shrink_rank"][pname]
+                    pt, a_off, b_off, num_pages = wl.page_placement(spec["cfg_id"], 100 + layer * 7 + pid, rs, d_in,
+                                                                    P, P)
+                    pool_s = rnd(num_pages, P)
+                    op.ws = B.Weights(num_slots=S, d_in=d_in, d_out=P, r_max=int(rs.max()),
+                                      rank=torch.from_numpy(rs.astype(np.int32)).to(device), scale=scale_d,
+                                      pool=pool_s, page_elems=P, page_table=torch.from_numpy(pt).to(device),
+                                      a_pt_off=torch.from_numpy(a_off).to(device),
+                                      b_pt_off=torch.from_numpy(b_off).to(device))
+                    op.shrink_rank = rs
                 op.v = torch.zeros((n, ldv), dtype=torch.float32, device=device)
                 op.idx, op.segs = idx_d, segs
                 op.expand_per_row = spec["form"] == "mixed"
@@ -150,7 +175,7 @@ def launch_unit(kind, ops, fused_chunks):
     "fused" (both steps of the per-row form in one launch)."""
     from segmented_gather_matmul_amd import binding as B
     op0 = ops[0]
-    items = [(op.w, op.v, op.y) for op in ops]
+    items = [(op.ws if kind == "shrink" else op.w, op.v, op.y) for op in ops]
     n = op0.x.shape[0]
     if kind == "fused":
         B.lora_bgmv_multi(op0.x, op0.idx, items, chunks=fused_chunks)
@@ -174,6 +199,8 @@ def launches(groups, grouped, fused_chunks):
     for ops in groups:
         units = [ops] if grouped else [[op] for op in ops]
         for u in units:
+            if fused_chunks >= 1 and any(op.shrink_rank is not None for op in u):
+                raise SystemExit("the one-launch form reads one weight descriptor; this workload's shrink has its own")
             if u[0].segs is None and fused_chunks >= 1:
                 out.append(("fused", u))
             else:
@@ -277,9 +304,10 @@ def unit_counts(spec, ops):
     idx, rank, r_max = spec["batch"].idx, spec["rank"], int(spec["rank"].max())
     n_act = int(cm.active_rows(idx, rank))
     x_bytes = 2 * n_act * ops[0].d_in
-    sb = x_bytes + sum(cm.shrink_bytes(idx, rank, o.d_in, r_max) - x_bytes for o in ops)
+    srank = [rank if getattr(o, "shrink_rank", None) is None else o.shrink_rank for o in ops]
+    sb = x_bytes + sum(cm.shrink_bytes(idx, sr, o.d_in, int(sr.max())) - x_bytes for o, sr in zip(ops, srank))
     eb = sum(cm.expand_bytes(idx, rank, o.d_out, r_max) for o in ops)
-    sf = sum(cm.shrink_flops(idx, rank, o.d_in) for o in ops)
+    sf = sum(cm.shrink_flops(idx, sr, o.d_in) for o, sr in zip(ops, srank))
     ef = sum(cm.expand_flops(idx, rank, o.d_out) for o in ops)
     return dict(shrink_bytes=sb, expand_bytes=eb, shrink_flops=sf, expand_flops=ef,
                 fused_bytes=sb + eb, fused_flops=sf + ef)

@@ -139,6 +139,32 @@ def test_paged_70b_tp8_shard_shapes(proj):
         G.check(dc, y, v, y_ref, v_ref, G.active_rows(b.idx, rank), f"paged-70b-tp8-{proj}-{form}")
 
 
+
+@pytest.mark.parametrize("proj", ["q", "gate"])
+def test_paged_70b_tp8_rank_column_shard(proj):
+    """One GPU's share when A of a column-parallel projection is split by rank columns
+    over 8 GPUs: the shrink over ceil(r / 8) rank-rows of the full 8192-wide input
+    (ranks 1, 2, 4, 8 from the pool's 8..64) into the d_out / 8 shard, 128-element
+    pages; the segment-form shrink with the per-row expand, as the bench runs it."""
+    import torch
+    d_in, d_out = wl.LLAMA2_70B_TP8[proj]
+    P, S = 128, 2000
+    rank = (wl.paged_ranks(S) + 7) // 8
+    scale = wl.scale_for_rank(rank)
+    b = wl.batch_paged_zipf(256, S)
+    pid = wl.PROJ_IDS[proj] + 20
+    G.say(f"case paged-70b-tp8-rank-shard {proj} {d_in}->{d_out}")
+    pool, pt, a_off, b_off, rows, compact_pt = G.paged_device_pool(5, pid, rank, d_in, d_out, P, b.idx)
+    ostore = wl.PagedStore(S, d_in, d_out, 8, P, rank, scale, rows, compact_pt, a_off, b_off)
+    x, y0 = wl.activations(5, pid, 256, d_in, d_out)
+    y_ref, v_ref = _oracle(ostore, x, y0, b.idx)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    w = B.Weights(num_slots=S, d_in=d_in, d_out=d_out, r_max=8, rank=dev(rank), scale=dev(scale), pool=pool,
+                  page_elems=P, page_table=dev(pt), a_pt_off=dev(a_off), b_pt_off=dev(b_off))
+    dc = G.DeviceCase(x, y0, 8)
+    y, v = _run("mixed", w, dc, b.idx)
+    G.check(dc, y, v, y_ref, v_ref, G.active_rows(b.idx, rank), f"paged-70b-tp8-rank-shard-{proj}")
+
 # ------------------------------------------------------------------ edge cases
 def _mixed_rank_store(cfg, d_in, d_out, S=7, paged_P=None):
     rank = np.array([1, 64, 0, 17, 8, 33, 64], dtype=np.int32)[:S]
