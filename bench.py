@@ -171,13 +171,16 @@ def make_ops(spec, layers, device, tile_rows=None):
 
 
 def launch_unit(kind, ops, fused_chunks):
-    """One launch over `ops` (projections sharing x): kind is "shrink", "expand" or
-    "fused" (both steps of the per-row form in one launch)."""
+    """One launch over `ops` (projections sharing x): kind is "shrink", "expand",
+    "handoff" (both steps of the per-row form in one launch, v handed off) or "fused"
+    (both steps in one launch, v recomputed per workgroup)."""
     from segmented_gather_matmul_amd import binding as B
     op0 = ops[0]
     items = [(op.ws if kind == "shrink" else op.w, op.v, op.y) for op in ops]
     n = op0.x.shape[0]
-    if kind == "fused":
+    if kind == "handoff":
+        B.lora_bgmv_multi_handoff(op0.x, op0.idx, items, op0.work)
+    elif kind == "fused":
         B.lora_bgmv_multi(op0.x, op0.idx, items, chunks=fused_chunks)
     elif op0.segs is None:
         if kind == "shrink":
@@ -192,17 +195,18 @@ def launch_unit(kind, ops, fused_chunks):
         B.lora_sgmv_expand_multi(op0.segs, items, n)
 
 
-def launches(groups, grouped, fused_chunks):
-    """(kind, ops) of every launch of one step, in order.  With fused_chunks >= 1 the
-    per-row form runs each unit as one fused launch."""
+def launches(groups, grouped, fused_chunks, handoff=False):
+    """(kind, ops) of every launch of one step, in order.  In the per-row form, with
+    handoff each unit is one hand-off launch, and with fused_chunks >= 1 one fused launch."""
     out = []
     for ops in groups:
         units = [ops] if grouped else [[op] for op in ops]
         for u in units:
-            if fused_chunks >= 1 and any(op.shrink_rank is not None for op in u):
-                raise SystemExit("the one-launch form reads one weight descriptor; this workload's shrink has its own")
-            if u[0].segs is None and fused_chunks >= 1:
-                out.append(("fused", u))
+            one = fused_chunks >= 1 or handoff
+            if one and any(op.shrink_rank is not None for op in u):
+                raise SystemExit("the one-launch forms read one weight descriptor; this workload's shrink has its own")
+            if u[0].segs is None and one:
+                out.append(("handoff" if handoff else "fused", u))
             else:
                 out += [("shrink", u), ("expand", u)]
     return out
@@ -310,7 +314,7 @@ def unit_counts(spec, ops):
     sf = sum(cm.shrink_flops(idx, sr, o.d_in) for o, sr in zip(ops, srank))
     ef = sum(cm.expand_flops(idx, rank, o.d_out) for o in ops)
     return dict(shrink_bytes=sb, expand_bytes=eb, shrink_flops=sf, expand_flops=ef,
-                fused_bytes=sb + eb, fused_flops=sf + ef)
+                fused_bytes=sb + eb, fused_flops=sf + ef, handoff_bytes=sb + eb, handoff_flops=sf + ef)
 
 
 def kernel_source_sha():
@@ -717,6 +721,9 @@ def main():
     ap.add_argument("--form", choices=["bgmv", "sgmv", "mixed"], default=None,
                     help="per-row slots (bgmv), rows grouped by adapter (sgmv), or the segment-form shrink with "
                          "the per-row expand (mixed); default: the workload's own")
+    ap.add_argument("--handoff", choices=["auto", "on", "off"], default="auto",
+                    help="per-row form: one launch per unit with v handed from the shrink's workgroups to the "
+                         "expand's (auto: with dense weights, where it measures faster than two launches)")
     ap.add_argument("--fused-chunks", type=int, default=-1,
                     help="per-row form: -1 = separate shrink and expand launches (the library's choice); c >= 1 = "
                          "one launch per unit, each workgroup covering c 512-column chunks")
@@ -789,7 +796,20 @@ def main():
     counts = [unit_counts(spec, ops) for ops in groups]
     step_bytes = sum(c["shrink_bytes"] + c["expand_bytes"] for c in counts)
     step_flops = sum(c["shrink_flops"] + c["expand_flops"] for c in counts)
-    plan = launches(groups, grouped, args.fused_chunks)
+    per_row = spec["form"] == "bgmv"
+    if args.handoff == "on" and not per_row:
+        raise SystemExit("--handoff on needs the per-row form (--form bgmv)")
+    if args.handoff == "on" and args.fused_chunks >= 1:
+        raise SystemExit("--handoff on and --fused-chunks >= 1 are two different one-launch forms")
+    # the library's hand-off form where it measures faster: dense weights, per-row form
+    handoff = args.handoff == "on" or (args.handoff == "auto" and per_row and spec["layout"] == "dense"
+                                       and args.fused_chunks < 1)
+    if handoff:
+        work = B.handoff_workspace(spec["batch"].n, device)
+        for ops in groups:
+            for op in ops:
+                op.work = work
+    plan = launches(groups, grouped, args.fused_chunks, handoff)
     n_launch = len(plan)
 
     log(f"[bench] {n_launch} launches/step, {step_bytes / 1e6:.1f} MB algorithmic per step; warmup {args.warmup}")
@@ -842,7 +862,8 @@ def main():
                 for key, (n, t, nb) in by_shape.items()}
     dom = max(per_kernel, key=lambda k: totals[k])
     pk = per_kernel[dom]
-    kernel_name = {"shrink": "lora_shrink_kernel", "expand": "lora_expand_kernel", "fused": "lora_fused_row_kernel"}[dom]
+    kernel_name = {"shrink": "lora_shrink_kernel", "expand": "lora_expand_kernel", "fused": "lora_fused_row_kernel",
+                   "handoff": "lora_bgmv_handoff_kernel"}[dom]
     traffic = None if args.rows is not None else traffic_from_profile(args.workload, dom)
     roofline = dict(bound="hbm", achieved=pk["gbs"], peak=cm.HBM_PEAK_GBS, unit="GB/s",
                     frac=round(pk["gbs"] / cm.HBM_PEAK_GBS, 4), traffic=traffic, kernel=kernel_name,
@@ -878,7 +899,8 @@ def main():
                    "num_slots": spec["num_slots"], "rank": sorted(set(int(r) for r in spec["rank"])),
                    "popularity": spec["popularity"], "form": spec["form"], "layout": spec["layout"],
                    "grouped": grouped, "launches_per_step": n_launch, "tile_rows": args.tile_rows,
-                   "fused_chunks": args.fused_chunks if spec["form"] == "bgmv" else None, "plan": args.plan,
+                   "fused_chunks": args.fused_chunks if spec["form"] == "bgmv" else None, "handoff": handoff,
+                   "plan": args.plan,
                    "graph": not args.no_graph,
                    "parallelism": "none"},
         "us_per_layer": round(1e3 * ms / layers, 3),

@@ -277,6 +277,29 @@ int lora_bgmv_expand_multi(void *stream, const int32_t *idx, int32_t n_rows, int
 int lora_bgmv_multi(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows,
                     int32_t n_proj, const lora_proj *proj, int32_t chunks);
 
+/*
+ * The same result as lora_bgmv_multi (bit for bit, v included) in ONE launch without
+ * recomputation (Punica digest, section 5.5, BGMV; the kernel launches per layer are
+ * what bounds a small decode batch): the launch's first workgroups run the shrink's
+ * work items and hand each row's v to the workgroups running the expand's through
+ * `work`, which poll for it while their loads of B and y are in flight.  An expand
+ * workgroup that has not seen its v after a bounded number of polls computes it
+ * itself, so the result does not depend on how the workgroups are scheduled.
+ *   work:  caller-owned device memory of at least lora_handoff_bytes(n_rows) bytes,
+ *          256-byte aligned, all zero before its first use (e.g. one hipMemset);
+ *          every call leaves it all zero again when it completes.  Calls ordered on
+ *          one stream (graph replays included) may share a workspace; calls that may
+ *          run at the same time need their own.
+ * Other arguments as for lora_bgmv_multi.  LORA_E_NULL for a NULL workspace,
+ * LORA_E_ALIGN for a misaligned one, LORA_E_SHAPE when it is too small or a
+ * projection's d_out exceeds 65535 * 512.  The per-row v contract is that of
+ * lora_bgmv_shrink_multi; the one NaN bit pattern 0xFFFFFFFF is handed to the expand
+ * as the canonical NaN (y is NaN either way).
+ */
+size_t lora_handoff_bytes(int32_t n_rows);   /* 0 for n_rows <= 0 */
+int lora_bgmv_multi_handoff(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows,
+                            int32_t n_proj, const lora_proj *proj, void *work, size_t work_bytes);
+
 /* ---------------------------------------------------------------- adapter pool */
 /*
  * Loading adapters into the paged layout (S-LoRA summary, "Unified Paging" and
@@ -360,6 +383,14 @@ int lora_set_launch_events(void *start_event, void *stop_event);
  * state, like the event pair.
  */
 int lora_set_plan(int32_t shrink_rank_rows, int32_t rows_per_pass);
+
+/*
+ * Test hook: the number of polls an expand workgroup of lora_bgmv_multi_handoff makes
+ * for its v before computing v itself, for the calling thread's later calls (0: every
+ * expand workgroup computes its v; a negative value restores the default, about 30 ms
+ * of polling).  Results are the same bits whatever the value.  Returns LORA_OK.
+ */
+int lora_set_handoff_polls(int32_t polls);
 
 const char *lora_last_error(void);   /* message of this thread's last failed call */
 const char *lora_status_str(int status);

@@ -33,7 +33,8 @@ EXPORTS = ["lora_build_segments", "lora_tiles_bound", "lora_build_tiles", "lora_
            "lora_abi_version", "lora_set_launch_events", "lora_sgmv_shrink_multi", "lora_sgmv_expand_multi",
            "lora_bgmv_shrink_multi", "lora_bgmv_expand_multi", "lora_pick_tile_rows", "lora_bgmv_multi",
            "lora_set_plan", "lora_pool_state_bytes", "lora_pool_init", "lora_pool_alloc", "lora_pool_release",
-           "lora_pool_free_count", "lora_pool_pages_for", "lora_pool_load_header_bytes", "lora_pool_load"]
+           "lora_pool_free_count", "lora_pool_pages_for", "lora_pool_load_header_bytes", "lora_pool_load",
+           "lora_handoff_bytes", "lora_bgmv_multi_handoff", "lora_set_handoff_polls"]
 MAX_PROJ = 4
 
 
@@ -102,6 +103,8 @@ def lib() -> ctypes.CDLL:
             "lora_pick_tile_rows": [P, I32],
             "lora_bgmv_multi": [P, P, I64, P, I32, I32, P, I32],
             "lora_set_plan": [I32, I32],
+            "lora_bgmv_multi_handoff": [P, P, I64, P, I32, I32, P, P, ctypes.c_size_t],
+            "lora_set_handoff_polls": [I32],
             "lora_pool_init": [P, ctypes.c_size_t, I64],
             "lora_pool_alloc": [P, I32, P],
             "lora_pool_release": [P, I32, P],
@@ -115,7 +118,8 @@ def lib() -> ctypes.CDLL:
         for name, args, res in (("lora_pool_state_bytes", [I64], ctypes.c_size_t),
                                 ("lora_pool_free_count", [P], I64),
                                 ("lora_pool_pages_for", [I32, I32, I32, I32], I64),
-                                ("lora_pool_load_header_bytes", [I32], ctypes.c_size_t)):
+                                ("lora_pool_load_header_bytes", [I32], ctypes.c_size_t),
+                                ("lora_handoff_bytes", [I32], ctypes.c_size_t)):
             fn = getattr(L, name)
             fn.argtypes, fn.restype = args, res
         L.lora_pick_tile_rows.restype = ctypes.c_int32
@@ -312,6 +316,13 @@ def lora_set_plan(shrink_rank_rows=0, rows_per_pass=0):
     _check(lib().lora_set_plan(int(shrink_rank_rows), int(rows_per_pass)))
 
 
+def lora_set_handoff_polls(polls=-1):
+    """Polls an expand workgroup of the hand-off form makes before computing its v itself
+    (0: always computes it; negative: the library's default), for this thread's later
+    calls; results are bit-identical either way."""
+    _check(lib().lora_set_handoff_polls(int(polls)))
+
+
 def lora_set_launch_events(start_event, stop_event):
     """Attach raw hipEvent_t handles (ints) to this thread's next kernel launch."""
     _check(lib().lora_set_launch_events(start_event, stop_event))
@@ -347,6 +358,23 @@ def lora_bgmv_shrink_multi(x, idx, items, stream=None):
 def lora_bgmv_expand_multi(idx, items, n_rows, stream=None):
     arr = proj_list(items)
     _check(lib().lora_bgmv_expand_multi(_stream(stream), _ptr(idx), int(n_rows), len(items), arr))
+
+
+def handoff_workspace(n_rows, device="cuda"):
+    """A zeroed workspace for lora_bgmv_multi_handoff calls of up to n_rows rows (the
+    library leaves it zeroed after every call)."""
+    import torch
+    nbytes = int(lib().lora_handoff_bytes(int(n_rows)))
+    return torch.zeros(max(nbytes, 256) // 4, dtype=torch.int32, device=device)
+
+
+def lora_bgmv_multi_handoff(x, idx, items, work, stream=None):
+    """Shrink and expand of the decode form in one launch, v handed from the shrink's
+    workgroups to the expand's through `work` (handoff_workspace); the bits of the
+    two-launch path."""
+    arr = proj_list(items)
+    _check(lib().lora_bgmv_multi_handoff(_stream(stream), _ptr(x), _ld(x), _ptr(idx), int(x.shape[0]), len(items),
+                                         arr, _ptr(work), int(work.numel() * work.element_size())))
 
 
 def lora_bgmv_multi(x, idx, items, chunks=0, stream=None):

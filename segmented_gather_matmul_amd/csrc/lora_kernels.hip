@@ -76,6 +76,18 @@ struct TileSrc {
     const int32_t *idx;       // per-row form
 };
 
+// The one-launch per-row form that hands v from the shrink's workgroups to the expand's
+// (lora_bgmv_handoff_kernel): the grid holds the shrink's work items (laid out as in a
+// shrink launch: per_tile, off, p[].slices) and then the expand's.
+struct HandoffDev {
+    uint32_t *work;                    // caller's workspace: kHandoffWords per (row, projection)
+    int32_t n_shrink;                  // workgroups of the shrink part
+    int32_t e_per_tile;                // expand items per row
+    int32_t e_off[LORA_MAX_PROJ];      // first expand item of projection p within a row's items
+    int32_t e_slices[LORA_MAX_PROJ];   // 512-column chunks of projection p
+    int32_t polls;                     // polls before an expand workgroup computes v itself
+};
+
 struct Args {
     const uint16_t *x;  // shrink input
     int64_t ldx;
@@ -85,6 +97,7 @@ struct Args {
     int32_t off[LORA_MAX_PROJ];  // first slice of projection p within a tile's items
     TileSrc ts;
     ProjDev p[LORA_MAX_PROJ];
+    HandoffDev ho;
 };
 
 constexpr int kThreads = 256;
@@ -318,6 +331,12 @@ __device__ inline ShrinkHalf<NR, RJ> load_half(const ShrinkSrc &s, const int (&r
     return h;
 }
 
+__device__ inline uint32_t *handoff_row(const HandoffDev &ho, int row, int p);
+
+// Where a VALU shrink puts v: the v buffer; a workgroup's own LDS row (indexed by
+// rank-row, per-row form); or the v buffer and the launch's hand-off row.
+enum class VSink { Global, Lds, Handoff };
+
 // VALU shrink.  Workgroup = one tile x rank-rows [j0, j0 + jw); NR rows and RJ
 // rank-rows per pass; d_in striped over the 256 lanes, 16 bytes per lane per load.
 // Lane l sums octets l, l + 256, l + 512, ... of d_in in that order, the octets taken
@@ -325,20 +344,20 @@ __device__ inline ShrinkHalf<NR, RJ> load_half(const ShrinkSrc &s, const int (&r
 // wavefront's lanes are added by wave_sum and the 4 wavefronts in order.  The
 // loads of several halves of pairs (256 octets each, about 16 loads per lane) are
 // issued together before any is summed, so a long d_in costs few round trips.
-template <bool PAGED, bool PERROW, int RJ, int NR>
-__global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
+// shrink_valu_item runs one work item.  It returns true when it stored v (a valid
+// tile whose slot has a non-zero rank), the same for every thread of the workgroup.
+// DH: halves of octet pairs in flight together (0: about 16 loads per lane); it changes
+// the batching of the loads, not the order of any sum.
+template <bool PAGED, bool PERROW, int RJ, int NR, VSink SINK, int DH = 0>
+__device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *red, int *pcache, float *vlds)
 {
     // halves in flight together: about 16 loads per lane, an even count (whole pairs)
-    constexpr int D = (16 / (NR + RJ)) & ~1 ? (16 / (NR + RJ)) & ~1 : 2;
-    __shared__ float red[kWaves * NR * RJ];
-    __shared__ int pcache[PAGED ? kPageCache : 1];
-    const Item it = work(a);
-    if (!it.ok) return;
+    constexpr int D = DH > 0 ? DH : (16 / (NR + RJ)) & ~1 ? (16 / (NR + RJ)) & ~1 : 2;
     const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
     const int j0 = it.slice * a.jw;
     const int jend = min(j0 + a.jw, pd.w.r_max);
     const TileHead th = tile_head<PERROW>(a.ts, pd.w, it.tile);
-    if (!th.valid || j0 >= jend) return;
+    if (!th.valid || j0 >= jend) return false;
     const int rank = slot_rank(pd.w, th.slot);
     const int jload = PAGED ? min(jend, rank) : jend;
     bool cached = false;
@@ -395,11 +414,33 @@ __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
                 for (int qq = 1; qq < NR; ++qq) row = q == qq ? rows[qq] : row;
                 // wavefront order: the same sum for every launch of this shape
                 const float s = red[tid] + red[NR * RJ + tid] + red[2 * NR * RJ + tid] + red[3 * NR * RJ + tid];
-                if (row >= 0 && j < jend) pd.v[(int64_t)row * pd.ldv + j] = j < rank ? s : 0.f;
+                if (row >= 0 && j < jend) {
+                    const float vj = j < rank ? s : 0.f;
+                    float *dst = pd.v + (int64_t)row * pd.ldv + j;
+                    if constexpr (SINK == VSink::Lds) vlds[j] = vj;
+                    else *dst = vj;
+                    if constexpr (SINK == VSink::Handoff) {
+                        uint32_t hv = ~__builtin_bit_cast(uint32_t, vj);
+                        if (hv == 0) hv = ~0x7FC00000u;  // zero stays "not yet"
+                        __hip_atomic_store(handoff_row(a.ho, row, it.p) + j, hv, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
             }
             __syncthreads();
         }
     }
+    return rank > 0;
+}
+
+template <bool PAGED, bool PERROW, int RJ, int NR>
+__global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
+{
+    __shared__ float red[kWaves * NR * RJ];
+    __shared__ int pcache[PAGED ? kPageCache : 1];
+    const Item it = work(a);
+    if (!it.ok) return;
+    shrink_valu_item<PAGED, PERROW, RJ, NR, VSink::Global>(a, it, red, pcache, nullptr);
 }
 
 // Rank slices of an MFMA shrink workgroup: slices g0 .. g0 + NS - 1 of the launch's
@@ -831,6 +872,133 @@ __global__ __launch_bounds__(kThreads) void lora_expand_valu_kernel(Args a)
         }
         expand_pass<PERROW, NR, RU>(pd, ps, sc, rank, bv, yv, c, cin, red);
     }
+}
+
+// ------------------------------------------------------------------------ one launch, v handed off
+// Shrink and expand of the per-row form in one launch, v passed from the shrink's
+// workgroups to the expand's through a caller-owned workspace.  Workgroups [0,
+// n_shrink) run the shrink's work items and the rest the expand's.  The hardware hands
+// out workgroup ids in increasing order, so every shrink workgroup has a CU before any
+// expand workgroup that could wait for it, and shrink workgroups never wait; the waits
+// are bounded all the same, and correctness does not rest on that order.
+//   shrink workgroup: lora_shrink_valu_kernel's work item (same bits); besides v it
+//     stores its entries into the (row, projection) hand-off row, device-coherently and
+//     bit-inverted, so that the zero of a cleared row means "not yet";
+//   expand workgroup: requests y and its rank-rows of B, then polls the hand-off row
+//     (one device-coherent load per lane, at most `polls` times) until every entry is
+//     set, and runs lora_expand_valu_kernel's arithmetic on it (same bits).  When the
+//     poll limit runs out it computes the row's v itself with the shrink's arithmetic
+//     (same bits again), so the result never depends on scheduling;
+//   a counter per (row, projection) takes every count of the launch: shrink items add
+//     1 (bits 0-7) once their hand-off stores have completed, expand workgroups add
+//     1 << 8 when done; whichever count completes the fixed total clears the hand-off
+//     row and the counter, so the workspace is zero again when the launch ends, in any
+//     order of events.
+// A v whose bits invert to zero (one NaN pattern) is handed off as the canonical NaN.
+constexpr int kHandoffWords = 128;  // per (row, projection): 64 hand-off entries, the counter on its own line
+
+__device__ inline uint32_t *handoff_row(const HandoffDev &ho, int row, int p)
+{
+    return ho.work + (int64_t)kHandoffWords * (row * LORA_MAX_PROJ + p);
+}
+
+// Wavefront 0 of a workgroup adds `inc` to the (row, projection) counter; when that
+// completes the launch's total (`need` shrink items, `e` expand workgroups) it clears
+// the hand-off row (r_max entries) and the counter.
+__device__ inline void handoff_count(const HandoffDev &ho, int row, int p, uint32_t inc, uint32_t need, uint32_t e,
+                                     int r_max)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t *h = handoff_row(ho, row, p), *cnt = h + kHandoffWords / 2;
+    uint32_t now = 0;
+    if (lane == 0) now = __hip_atomic_fetch_add(cnt, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
+    now = __builtin_amdgcn_readfirstlane(now);
+    if ((now & 0xFF) == need && ((now >> 8) & 0xFFFF) == e) {
+        if (lane < r_max) __hip_atomic_store(h + lane, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Work item `wi` of a list with `per_row` items per row, projection p's from off[p].
+__device__ inline Item row_item(int wi, int per_row, const int32_t *off, int n_proj, int n_rows)
+{
+    Item it;
+    it.tile = wi / per_row;
+    const int sl = wi - it.tile * per_row;
+    int p = 0;
+#pragma unroll
+    for (int q = 1; q < LORA_MAX_PROJ; ++q) p += (q < n_proj && sl >= off[q]) ? 1 : 0;
+    it.p = p;
+    it.slice = sl - off[p];
+    it.ok = it.tile < n_rows;
+    return it;
+}
+
+template <bool PAGED, int RJ, int RU>
+__global__ __launch_bounds__(kThreads) void lora_bgmv_handoff_kernel(Args a)
+{
+    constexpr int kDH = RJ == 1 ? 4 : 0;    // the shrink items' halves in flight (registers)
+    __shared__ float red[kWaves * 8 * 64];  // the shrink's kWaves * RJ sums or the expand's
+    __shared__ int pcache[PAGED ? kPageCache : 1];
+    __shared__ float vrow[LORA_MAX_RANK];
+    __shared__ int s_ok;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.x;
+    if (b < a.ho.n_shrink) {
+        const Item it = row_item(b, a.per_tile, a.off, a.n_proj, a.n_rows);
+        if (!it.ok) return;
+        const bool stored = shrink_valu_item<PAGED, true, RJ, 1, VSink::Handoff, kDH>(a, it, red, pcache, nullptr);
+        // wavefront 0 made every v store of this workgroup
+        if (stored && wave == 0) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the hand-off stores have completed
+            handoff_count(a.ho, it.tile, it.p, 1u, a.p[it.p].slices, a.ho.e_slices[it.p], a.p[it.p].w.r_max);
+        }
+        return;
+    }
+    const Item it = row_item(b - a.ho.n_shrink, a.ho.e_per_tile, a.ho.e_off, a.n_proj, a.n_rows);
+    if (!it.ok) return;
+    const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
+    const TileHead th = tile_head<true>(a.ts, pd.w, it.tile);
+    if (!th.valid) return;
+    const int rank = slot_rank(pd.w, th.slot);
+    if (rank == 0) return;  // the row's shrink items store nothing
+    const int row = it.tile;
+    const int jlim = PAGED ? rank : pd.w.r_max;
+    const float sc = pd.w.scale[th.slot];
+    const int c = it.slice * kCols + 8 * lane;
+    const bool cin = c < pd.w.d_out;
+    ExpandPass<true, 1> ps;
+    ps.rows[0] = row;
+    ps.my_row = wave == 0 ? row : -1;
+    const uint4 yv = ps.load_y(pd, c, cin);
+    uint4 bv[RU];
+    load_b_octets<PAGED, RU>(pd.w, th.slot, jlim, wave, 0, c, cin, bv);
+    if (wave == 0) {
+        const uint32_t *h = handoff_row(a.ho, row, it.p) + lane;
+        const bool mine = lane < pd.w.r_max;
+        uint32_t hv = 0;
+        bool ok = false;
+        for (int n = 0;; ++n) {
+            hv = mine ? __hip_atomic_load(h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
+            ok = __ballot(hv == 0) == 0;
+            if (ok || n >= a.ho.polls) break;
+            __builtin_amdgcn_s_sleep(8);
+        }
+        if (ok && mine) vrow[lane] = __builtin_bit_cast(float, ~hv);
+        if (lane == 0) s_ok = ok;
+    }
+    __syncthreads();
+    if (!s_ok) {
+        for (int sl = 0; sl < a.p[it.p].slices; ++sl) {
+            const Item si{row, it.p, sl, true};
+            // one rank-row and one pair of halves at a time: few registers on a path
+            // that only runs when the poll limit runs out
+            shrink_valu_item<PAGED, true, 1, 1, VSink::Lds, 2>(a, si, red, pcache, vrow);
+        }
+    }
+    ps.sv[0] = lane < pd.w.r_max ? vrow[lane] : 0.f;
+    expand_pass<true, 1, RU>(pd, ps, sc, rank, bv, yv, c, cin, red);
+    if (wave == 0) handoff_count(a.ho, row, it.p, 1u << 8, a.p[it.p].slices, a.ho.e_slices[it.p], pd.w.r_max);
 }
 
 // MFMA expand for tiles of up to 64 rows.  B[0:r][512 columns] is staged in LDS
@@ -1517,6 +1685,70 @@ int fused_row_impl(void *stream, const void *x, int64_t ldx, const int32_t *idx,
     return launch_status("fused bgmv");
 }
 
+constexpr int32_t kHandoffPolls = 1 << 15;  // ~30 ms of polling before computing v locally
+thread_local int32_t t_handoff_polls = kHandoffPolls;
+constexpr int64_t kResidentGroups = 2048;   // 256 CUs x 8 workgroups of 4 wavefronts (<= 64 VGPRs)
+
+// Per-row form in one launch with v handed off (lora_bgmv_handoff_kernel).  Arguments
+// other than the workspace are checked by the caller.
+int handoff_row_impl(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows, int32_t n_proj,
+                     const lora_proj *proj, Args &a, bool paged, void *work, size_t work_bytes)
+{
+    if (!work) return fail(LORA_E_NULL, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(work) & 255) return fail(LORA_E_ALIGN, "workspace must be 256-byte aligned");
+    if (work_bytes < lora_handoff_bytes(n_rows))
+        return fail(LORA_E_SHAPE, "workspace of %zu bytes < %zu for %d rows", work_bytes, lora_handoff_bytes(n_rows),
+                    n_rows);
+    int32_t r_max = 0, e_per_tile = 0;
+    for (int32_t p = 0; p < n_proj; ++p) r_max = std::max(r_max, proj[p].w->r_max);
+    for (int32_t p = 0; p < LORA_MAX_PROJ; ++p) {
+        a.ho.e_off[p] = e_per_tile;
+        a.ho.e_slices[p] = p < n_proj ? (proj[p].w->d_out + kCols - 1) / kCols : 0;
+        if (a.ho.e_slices[p] > 0xFFFF)
+            return fail(LORA_E_SHAPE, "d_out = %d is too wide for one launch", proj[p].w->d_out);
+        e_per_tile += a.ho.e_slices[p];
+    }
+    a.ho.e_per_tile = e_per_tile;
+    // rank-rows per shrink item: the narrowest that keeps both parts within what the
+    // CUs hold at once, else 4
+    a.jw = 1;
+    for (;; a.jw *= 2) {
+        int64_t s_per_row = 0;
+        for (int32_t p = 0; p < n_proj; ++p) s_per_row += (proj[p].w->r_max + a.jw - 1) / a.jw;
+        if (a.jw == 4 || n_rows * (s_per_row + e_per_tile) <= kResidentGroups) break;
+    }
+    if (t_plan_jw > 0) a.jw = t_plan_jw;
+    for (int32_t p = 0; p < n_proj; ++p) a.p[p].slices = (proj[p].w->r_max + a.jw - 1) / a.jw;
+    int st = finish_layout(a, n_rows);
+    if (st) return st;
+    const int64_t groups = (int64_t)n_rows * (a.per_tile + e_per_tile);
+    if (groups > ((int64_t)1 << 30)) return fail(LORA_E_SHAPE, "launch of %lld workgroups is too large", (long long)groups);
+    a.ho.work = static_cast<uint32_t *>(work);
+    a.ho.n_shrink = n_rows * a.per_tile;
+    a.ho.polls = t_handoff_polls;
+    a.grid = (int32_t)groups;
+    a.x = static_cast<const uint16_t *>(x);
+    a.ldx = ldx;
+    a.n_rows = n_rows;
+    a.n_tiles = n_rows;
+    a.ts = row_src(idx);
+    const dim3 grid((unsigned)a.grid);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+#define LORA_HANDOFF(RJ, RU)                                                                 \
+    (paged ? launch(lora_bgmv_handoff_kernel<true, RJ, RU>, grid, kThreads, 0, s, a)         \
+           : launch(lora_bgmv_handoff_kernel<false, RJ, RU>, grid, kThreads, 0, s, a))
+#define LORA_HANDOFF_RU(RJ)                     \
+    if (r_max <= 16) LORA_HANDOFF(RJ, 4);       \
+    else if (r_max <= 32) LORA_HANDOFF(RJ, 8);  \
+    else LORA_HANDOFF(RJ, 16)
+    if (a.jw == 1) { LORA_HANDOFF_RU(1); }
+    else if (a.jw == 2) { LORA_HANDOFF_RU(2); }
+    else { LORA_HANDOFF_RU(4); }
+#undef LORA_HANDOFF_RU
+#undef LORA_HANDOFF
+    return launch_status("bgmv with v handed off");
+}
+
 inline int32_t seg_max_rows(const lora_segments *seg) { return seg->max_rows > 0 ? seg->max_rows : LORA_MAX_TILE_ROWS; }
 
 lora_proj one_proj(const lora_weights *w, float *v, int64_t ldv, void *y, int64_t ldy)
@@ -1643,29 +1875,60 @@ int lora_bgmv_expand(void *stream, void *y, int64_t ldy, const float *v, int64_t
     return lora_bgmv_expand_multi(stream, idx, n_rows, 1, &p);
 }
 
-int lora_bgmv_multi(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows, int32_t n_proj,
-                    const lora_proj *proj, int32_t chunks)
+// Checks shared by the one-launch and two-launch decode entry points.
+static int check_bgmv_multi(const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows, int32_t n_proj,
+                            const lora_proj *proj, Args &a, bool &paged)
 {
-    clear_error();
     if (n_rows > 0 && !idx) return fail(LORA_E_NULL, "idx is NULL");
-    // Check everything both steps need before launching either.
-    Args a{};
-    bool paged = false;
     int st = check_projs(n_proj, proj, true, a, paged);
     if (st) return st;
     for (int32_t p = 1; p < n_proj; ++p)
         if (proj[p].w->d_in != proj[0].w->d_in)
             return fail(LORA_E_SHAPE, "projections of one launch share x: d_in %d != %d", proj[p].w->d_in,
                         proj[0].w->d_in);
-    if (chunks < -1) return fail(LORA_E_SHAPE, "chunks = %d (-1, 0 or a chunk count)", chunks);
     if (n_rows < 0) return fail(LORA_E_SHAPE, "n_rows = %d", n_rows);
     if (n_rows == 0) return LORA_OK;
-    if ((st = check_rows_arg(x, ldx, proj[0].w->d_in, 8, "x"))) return st;
+    return check_rows_arg(x, ldx, proj[0].w->d_in, 8, "x");
+}
+
+int lora_bgmv_multi(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows, int32_t n_proj,
+                    const lora_proj *proj, int32_t chunks)
+{
+    clear_error();
+    // Check everything both steps need before launching either.
+    Args a{};
+    bool paged = false;
+    if (chunks < -1) return fail(LORA_E_SHAPE, "chunks = %d (-1, 0 or a chunk count)", chunks);
+    int st = check_bgmv_multi(x, ldx, idx, n_rows, n_proj, proj, a, paged);
+    if (st || n_rows == 0) return st;
     const int32_t gc = chunks == 0 ? plan_fused_chunks(n_rows, n_proj, proj) : chunks;
     if (gc > 0) return fused_row_impl(stream, x, ldx, idx, n_rows, n_proj, proj, gc, a, paged);
     st = shrink_impl<true>(stream, x, ldx, n_rows, row_src(idx), n_rows, 1, n_proj, proj);
     if (st) return st;
     return expand_impl<true>(stream, n_rows, row_src(idx), n_rows, 1, n_proj, proj);
+}
+
+size_t lora_handoff_bytes(int32_t n_rows)
+{
+    return n_rows > 0 ? (size_t)n_rows * LORA_MAX_PROJ * kHandoffWords * sizeof(uint32_t) : 0;
+}
+
+int lora_bgmv_multi_handoff(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows,
+                            int32_t n_proj, const lora_proj *proj, void *work, size_t work_bytes)
+{
+    clear_error();
+    Args a{};
+    bool paged = false;
+    int st = check_bgmv_multi(x, ldx, idx, n_rows, n_proj, proj, a, paged);
+    if (st || n_rows == 0) return st;
+    return handoff_row_impl(stream, x, ldx, idx, n_rows, n_proj, proj, a, paged, work, work_bytes);
+}
+
+int lora_set_handoff_polls(int32_t polls)
+{
+    clear_error();
+    t_handoff_polls = polls < 0 ? kHandoffPolls : polls;
+    return LORA_OK;
 }
 
 int lora_bgmv(void *stream, void *y, int64_t ldy, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows,

@@ -11,9 +11,9 @@ work-list and row map of the segment form built once on the host from those ids
 q/k/v come from one backbone GEMM against a [h, 3h] weight and gate/up from one against
 [h, 2f]; their add-ons land in column slices of that output through the row-stride
 argument (ldy = 3h or 2f).  q/k/v share one call over three projections (same x), and
-gate/up another, so a layer makes four add-on calls.  Optionally each shrink runs on a
-second stream while the backbone GEMM of the same input runs, so only the expands stay
-on the layer's critical path.
+gate/up another, so a layer makes four add-on calls; in the per-row form each is one
+launch.  Optionally each shrink runs on a second stream while the backbone GEMM of the
+same input runs, so only the expands stay on the layer's critical path.
 
 Left out of the step on purpose: rotary position embedding (elementwise on q and k) and
 sampling.  The current token's k and v are written into the last position of the cache,
@@ -104,18 +104,21 @@ class LoraDecoderLayer:
     w_d [f, h] (all applied as x @ W), norm1 [h], norm2 [h].
     adapters: proj -> (a_t [S, r_max, d_in], b [S, r_max, d_out]) fp16 device tensors.
     rank (int32 [S]) and scale (fp32 [S]) are the slots' ranks and scales, shared by the
-    seven projections.  max_rows bounds the batch (it sizes the v buffers).  chunks is passed
-    to the per-row form's calls (0: the library's choice of one or two launches).  overlap:
+    seven projections.  max_rows bounds the batch (it sizes the v buffers).  In the per-row
+    form each add-on call is one launch that hands v from the shrink's workgroups to the
+    expand's (handoff, through a workspace the layer owns); with handoff False, chunks is
+    passed to lora_bgmv_multi (0: the library's choice of one or two launches).  overlap:
     each shrink runs on a second stream (default priority) concurrently with the backbone
-    GEMM of its projections, the expand after that GEMM; the results are the same bits as
-    without overlap (the same two launches, in the same data order)."""
+    GEMM of its projections, the expand after that GEMM.  The results are the same bits
+    in every case."""
 
     def __init__(self, shape: LlamaShape, backbone: dict, adapters: dict, rank, scale, max_rows, chunks=0,
-                 overlap=False):
+                 overlap=False, handoff=True):
         import torch
         self.shape = shape
         self.chunks = int(chunks)
         self.side = torch.cuda.Stream(device=rank.device) if overlap else None
+        self.work = B.handoff_workspace(max_rows, rank.device) if handoff and not overlap else None
         self.bb = backbone
         num_slots, r_max = adapters["q"][0].shape[:2]
         self.num_slots, self.r_max = int(num_slots), int(r_max)
@@ -171,7 +174,9 @@ class LoraDecoderLayer:
             self._expand(meta, names, outs, n)
         elif meta is not None:
             items = self._items(names, outs, n)
-            if meta.form == "bgmv":
+            if meta.form == "bgmv" and self.work is not None:
+                B.lora_bgmv_multi_handoff(x, meta.idx, items, self.work)
+            elif meta.form == "bgmv":
                 B.lora_bgmv_multi(x, meta.idx, items, chunks=self.chunks)
             else:
                 B.lora_sgmv_shrink_multi(x, meta.segs, items)
@@ -211,7 +216,7 @@ class LoraDecoderLayer:
         return h1 + d
 
 
-def random_layer(shape: LlamaShape, num_slots, rank, max_rows, gen, device="cuda", overlap=False):
+def random_layer(shape: LlamaShape, num_slots, rank, max_rows, gen, device="cuda", overlap=False, handoff=True):
     """A layer with N(0, 0.02) fp16 backbone and adapter weights drawn on the device, every
     slot of rank `rank` with scale 32 / rank."""
     import torch
@@ -226,4 +231,4 @@ def random_layer(shape: LlamaShape, num_slots, rank, max_rows, gen, device="cuda
     ads = {p: (rnd(num_slots, rank, di), rnd(num_slots, rank, do)) for p, (di, do) in proj_dims(shape).items()}
     rank_t = torch.full((num_slots,), rank, dtype=torch.int32, device=device)
     scale_t = torch.full((num_slots,), 32.0 / rank, dtype=torch.float32, device=device)
-    return LoraDecoderLayer(shape, bb, ads, rank_t, scale_t, max_rows, overlap=overlap)
+    return LoraDecoderLayer(shape, bb, ads, rank_t, scale_t, max_rows, overlap=overlap, handoff=handoff)

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 29 and set(names) == set(B.EXPORTS)
+    assert len(names) == 32 and set(names) == set(B.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", build_mod.LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (lora_\w+)", out))
@@ -306,6 +306,33 @@ def test_one_launch_decode_errors():
     assert call() == B.LORA_E_SHAPE and "share x" in B.last_error()
     arr[1].w = ctypes.addressof(c1)
     assert call(n=0) == B.LORA_OK and call(n=0, chunks=-1) == B.LORA_OK and call(n=0, chunks=3) == B.LORA_OK
+
+
+def test_handoff_decode_errors():
+    """lora_bgmv_multi_handoff checks lora_bgmv_multi's arguments, then the workspace,
+    before launching anything."""
+    L = B.lib()
+    assert L.lora_handoff_bytes(0) == 0 and L.lora_handoff_bytes(-3) == 0
+    assert L.lora_handoff_bytes(1) == 4 * 128 * 4 and L.lora_handoff_bytes(1000) == 1000 * 2048
+    c1 = _desc()
+    arr = (B.CProj * 2)()
+    for i in range(2):
+        arr[i].w, arr[i].v, arr[i].ldv, arr[i].y, arr[i].ldy = ctypes.addressof(c1), FAKE, 16, FAKE, 1024
+    need = L.lora_handoff_bytes(8)
+    call = lambda x=FAKE, idx=FAKE, n=8, n_proj=2, a=arr, work=FAKE, nbytes=need: \
+        L.lora_bgmv_multi_handoff(None, x, 1024, idx, n, n_proj, a, work, nbytes)
+    assert call(idx=None) == B.LORA_E_NULL
+    assert call(n_proj=5) == B.LORA_E_SHAPE
+    assert call(x=FAKE + 8) == B.LORA_E_ALIGN
+    assert call(n=-1) == B.LORA_E_SHAPE
+    assert call(work=None) == B.LORA_E_NULL and "workspace" in B.last_error()
+    assert call(work=FAKE + 16) == B.LORA_E_ALIGN and "workspace" in B.last_error()
+    assert call(nbytes=need - 1) == B.LORA_E_SHAPE and "workspace" in B.last_error()
+    wide = _desc(d_out=65536 * 512)
+    arr[1].w, arr[1].ldy = ctypes.addressof(wide), 65536 * 512
+    assert call() == B.LORA_E_SHAPE and "too wide" in B.last_error()
+    assert call(n=0, work=None, nbytes=0) == B.LORA_OK                 # no rows: nothing is read or launched
+    assert L.lora_set_handoff_polls(0) == B.LORA_OK and L.lora_set_handoff_polls(-1) == B.LORA_OK
 
 
 def test_set_plan_ranges():
