@@ -108,6 +108,46 @@ constexpr int kMfmaShrinkThreads = 1024;  // 16 wavefronts split d_in in the MFM
 constexpr int kFusedGroups = 4;            // 256-lane groups of a fused workgroup
 constexpr int kFusedThreads = kFusedGroups * kThreads;
 
+// The kernel arguments, read through a pointer that comes out of one scalar load per
+// 64-byte line of them, all issued before a single wait: every argument read that
+// follows hits the scalar cache.  Without it the reads miss one line after another at
+// the start of a launch, each a round trip to L2 or memory, and the compiler hoists
+// them ahead of any load of its own that does not feed their address.
+__device__ inline const Args &touched_args()
+{
+    static_assert(sizeof(Args) > 11 * 64 && sizeof(Args) <= 12 * 64, "12 lines of kernel arguments");
+    auto ka = __builtin_amdgcn_kernarg_segment_ptr();
+    int t0, t1, t2, t3, t4, t5, t6, t7, t8, t9, t10, t11;
+    asm volatile(
+        "s_load_dword %0, %12, 0x0\n\t"
+        "s_load_dword %1, %12, 0x40\n\t"
+        "s_load_dword %2, %12, 0x80\n\t"
+        "s_load_dword %3, %12, 0xc0\n\t"
+        "s_load_dword %4, %12, 0x100\n\t"
+        "s_load_dword %5, %12, 0x140\n\t"
+        "s_load_dword %6, %12, 0x180\n\t"
+        "s_load_dword %7, %12, 0x1c0\n\t"
+        "s_load_dword %8, %12, 0x200\n\t"
+        "s_load_dword %9, %12, 0x240\n\t"
+        "s_load_dword %10, %12, 0x280\n\t"
+        "s_load_dword %11, %12, 0x2c0\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=s"(t0), "=s"(t1), "=s"(t2), "=s"(t3), "=s"(t4), "=s"(t5), "=s"(t6), "=s"(t7), "=s"(t8), "=s"(t9),
+          "=s"(t10), "=s"(t11), "+s"(ka));
+    typedef const __attribute__((address_space(4))) Args args_t;
+    return *(const Args *)(args_t *)ka;
+}
+
+// The kernel arguments as a kernel reads them: through touched_args with dense weights;
+// with paged weights directly (there the touch measured slower: the kernels' extra
+// registers cost a wavefront per SIMD).
+template <bool TOUCH>
+__device__ inline const Args &kernel_args(const Args &param)
+{
+    if constexpr (TOUCH) return touched_args();
+    else return param;
+}
+
 // Contiguous work ranges per XCD: workgroup b runs on XCD b % 8; grid % 8 == 0.
 __device__ inline int work_item(int b, int grid) { return (b & 7) * (grid >> 3) + (b >> 3); }
 
@@ -434,8 +474,9 @@ __device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *re
 }
 
 template <bool PAGED, bool PERROW, int RJ, int NR>
-__global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args a)
+__global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args args)
 {
+    const Args &a = kernel_args<!PAGED>(args);
     __shared__ float red[kWaves * NR * RJ];
     __shared__ int pcache[PAGED ? kPageCache : 1];
     const Item it = work(a);
@@ -510,8 +551,9 @@ __device__ inline void mfma_shrink_store(const Args &a, const TileHead &th, cons
 // order, one rank slice at a time.  Neither NS nor MTX changes the order in which any
 // element is summed, so every split gives the same bits.
 template <bool PAGED, int MTX, int NS>
-__global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Args a)
+__global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Args args)
 {
+    const Args &a = kernel_args<!PAGED>(args);
     constexpr int W = kMfmaShrinkThreads / 64;
     // k-steps in flight per wavefront: ~16 loads, or one step when the accumulators are large
     constexpr int U = MTX * NS >= 12 ? 1 : 16 / (MTX + NS);
@@ -627,8 +669,9 @@ __device__ inline void stage_load(const uint16_t *const (&src)[RPW], int k, int 
 }
 
 template <int MTX, int NS>
-__global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_kernel(Args a)
+__global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_kernel(Args args)
 {
+    const Args &a = kernel_args<true>(args);
     constexpr int W = kMfmaShrinkThreads / 64;
     constexpr int XR = 16 * MTX, ROWS = stage_rows(MTX, NS);
     constexpr int RPW = (ROWS + W - 1) / W;  // staged rows per wavefront: rows wave, wave + W, ...
@@ -846,8 +889,9 @@ __device__ inline void expand_pass(const ProjDev &pd, const ExpandPass<PERROW, N
 }
 
 template <bool PAGED, bool PERROW, int NR, int RU>
-__global__ __launch_bounds__(kThreads) void lora_expand_valu_kernel(Args a)
+__global__ __launch_bounds__(kThreads) void lora_expand_valu_kernel(Args args)
 {
+    const Args &a = kernel_args<!PAGED>(args);
     __shared__ float red[kWaves * NR * 8 * 64];
     const Item it = work(a);
     if (!it.ok) return;
@@ -935,8 +979,9 @@ __device__ inline Item row_item(int wi, int per_row, const int32_t *off, int n_p
 }
 
 template <bool PAGED, int RJ, int RU>
-__global__ __launch_bounds__(kThreads) void lora_bgmv_handoff_kernel(Args a)
+__global__ __launch_bounds__(kThreads) void lora_bgmv_handoff_kernel(Args args)
 {
+    const Args &a = kernel_args<!PAGED>(args);
     constexpr int kDH = RJ == 1 ? 4 : 0;    // the shrink items' halves in flight (registers)
     __shared__ float red[kWaves * 8 * 64];  // the shrink's kWaves * RJ sums or the expand's
     __shared__ int pcache[PAGED ? kPageCache : 1];
@@ -944,9 +989,16 @@ __global__ __launch_bounds__(kThreads) void lora_bgmv_handoff_kernel(Args a)
     __shared__ int s_ok;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x;
-    if (b < a.ho.n_shrink) {
-        const Item it = row_item(b, a.per_tile, a.off, a.n_proj, a.n_rows);
-        if (!it.ok) return;
+    // The item comes from kernel arguments read before the first branch (both parts'
+    // layouts), so the slot and the projection's descriptor are one round trip later.
+    const bool shrink = b < a.ho.n_shrink;
+    int32_t off[LORA_MAX_PROJ];
+#pragma unroll
+    for (int q = 0; q < LORA_MAX_PROJ; ++q) off[q] = shrink ? a.off[q] : a.ho.e_off[q];
+    const Item it = row_item(shrink ? b : b - a.ho.n_shrink, shrink ? a.per_tile : a.ho.e_per_tile, off, a.n_proj,
+                             a.n_rows);
+    if (!it.ok) return;
+    if (shrink) {
         const bool stored = shrink_valu_item<PAGED, true, RJ, 1, VSink::Handoff, kDH>(a, it, red, pcache, nullptr);
         // wavefront 0 made every v store of this workgroup
         if (stored && wave == 0) {
@@ -955,13 +1007,10 @@ __global__ __launch_bounds__(kThreads) void lora_bgmv_handoff_kernel(Args a)
         }
         return;
     }
-    const Item it = row_item(b - a.ho.n_shrink, a.ho.e_per_tile, a.ho.e_off, a.n_proj, a.n_rows);
-    if (!it.ok) return;
     const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
     const TileHead th = tile_head<true>(a.ts, pd.w, it.tile);
     if (!th.valid) return;
     const int rank = slot_rank(pd.w, th.slot);
-    if (rank == 0) return;  // the row's shrink items store nothing
     const int row = it.tile;
     const int jlim = PAGED ? rank : pd.w.r_max;
     const float sc = pd.w.scale[th.slot];
@@ -973,7 +1022,12 @@ __global__ __launch_bounds__(kThreads) void lora_bgmv_handoff_kernel(Args a)
     const uint4 yv = ps.load_y(pd, c, cin);
     uint4 bv[RU];
     load_b_octets<PAGED, RU>(pd.w, th.slot, jlim, wave, 0, c, cin, bv);
-    if (wave == 0) {
+    // A rank-0 row's shrink items store nothing: such a workgroup neither waits nor
+    // counts, and its expand writes nothing.  Tested as a predicate rather than by an
+    // early return so that the loads above are not held back behind the rank.
+    const bool active = rank > 0;
+    if (wave == 0 && !active && lane == 0) s_ok = 1;
+    if (wave == 0 && active) {
         const uint32_t *h = handoff_row(a.ho, row, it.p) + lane;
         const bool mine = lane < pd.w.r_max;
         uint32_t hv = 0;
@@ -998,7 +1052,7 @@ __global__ __launch_bounds__(kThreads) void lora_bgmv_handoff_kernel(Args a)
     }
     ps.sv[0] = lane < pd.w.r_max ? vrow[lane] : 0.f;
     expand_pass<true, 1, RU>(pd, ps, sc, rank, bv, yv, c, cin, red);
-    if (wave == 0) handoff_count(a.ho, row, it.p, 1u << 8, a.p[it.p].slices, a.ho.e_slices[it.p], pd.w.r_max);
+    if (wave == 0 && active) handoff_count(a.ho, row, it.p, 1u << 8, a.p[it.p].slices, a.ho.e_slices[it.p], pd.w.r_max);
 }
 
 // MFMA expand for tiles of up to 64 rows.  B[0:r][512 columns] is staged in LDS
@@ -1019,8 +1073,9 @@ constexpr int kYStride = kCols + 8;  // halves per row of the staged y slice (th
 __host__ __device__ constexpr int bt_stride(int rq) { return 16 * rq + kBtPad; }
 
 template <bool PAGED, int RQ, bool SY>
-__global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args a)
+__global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args args)
 {
+    const Args &a = kernel_args<!PAGED>(args);
     constexpr int kStage = RQ * 16 * (kCols / 8) / kThreads;  // 16-byte loads per lane to stage B
     constexpr int KS = bt_stride(RQ);
     extern __shared__ __align__(16) unsigned char smem[];
@@ -1234,8 +1289,9 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args a)
 // hit its L2.  For r_max <= 32, B and y of a group's first chunk are requested before
 // the shrink's loads, so they arrive while v is being summed.
 template <bool PAGED, int RU>
-__global__ __launch_bounds__(kFusedThreads) void lora_fused_row_kernel(Args a)
+__global__ __launch_bounds__(kFusedThreads) void lora_fused_row_kernel(Args args)
 {
+    const Args &a = kernel_args<!PAGED>(args);
     constexpr int RJ = 4;  // rank-rows per group per batch
     __shared__ float sred[kFusedGroups][kWaves][RJ];
     __shared__ float vrow[LORA_MAX_RANK];
