@@ -178,8 +178,10 @@ def launch_unit(kind, ops, fused_chunks):
     op0 = ops[0]
     items = [(op.ws if kind == "shrink" else op.w, op.v, op.y) for op in ops]
     n = op0.x.shape[0]
-    if kind == "handoff":
+    if kind == "handoff" and op0.segs is None:
         B.lora_bgmv_multi_handoff(op0.x, op0.idx, items, op0.work)
+    elif kind == "handoff":
+        B.lora_sgmv_multi_handoff(op0.x, op0.segs, items, n, op0.work)
     elif kind == "fused":
         B.lora_bgmv_multi(op0.x, op0.idx, items, chunks=fused_chunks)
     elif op0.segs is None:
@@ -196,8 +198,9 @@ def launch_unit(kind, ops, fused_chunks):
 
 
 def launches(groups, grouped, fused_chunks, handoff=False):
-    """(kind, ops) of every launch of one step, in order.  In the per-row form, with
-    handoff each unit is one hand-off launch, and with fused_chunks >= 1 one fused launch."""
+    """(kind, ops) of every launch of one step, in order.  With handoff each unit of the
+    per-row or segment form is one hand-off launch; with fused_chunks >= 1 each unit of
+    the per-row form is one fused launch."""
     out = []
     for ops in groups:
         units = [ops] if grouped else [[op] for op in ops]
@@ -205,8 +208,10 @@ def launches(groups, grouped, fused_chunks, handoff=False):
             one = fused_chunks >= 1 or handoff
             if one and any(op.shrink_rank is not None for op in u):
                 raise SystemExit("the one-launch forms read one weight descriptor; this workload's shrink has its own")
-            if u[0].segs is None and one:
-                out.append(("handoff" if handoff else "fused", u))
+            if handoff and not u[0].expand_per_row:
+                out.append(("handoff", u))
+            elif u[0].segs is None and fused_chunks >= 1:
+                out.append(("fused", u))
             else:
                 out += [("shrink", u), ("expand", u)]
     return out
@@ -722,8 +727,9 @@ def main():
                     help="per-row slots (bgmv), rows grouped by adapter (sgmv), or the segment-form shrink with "
                          "the per-row expand (mixed); default: the workload's own")
     ap.add_argument("--handoff", choices=["auto", "on", "off"], default="auto",
-                    help="per-row form: one launch per unit with v handed from the shrink's workgroups to the "
-                         "expand's (auto: with dense weights, where it measures faster than two launches)")
+                    help="per-row and segment forms: one launch per unit with v handed from the shrink's "
+                         "workgroups to the expand's (auto: with dense weights, where it measures faster than two "
+                         "launches)")
     ap.add_argument("--fused-chunks", type=int, default=-1,
                     help="per-row form: -1 = separate shrink and expand launches (the library's choice); c >= 1 = "
                          "one launch per unit, each workgroup covering c 512-column chunks")
@@ -796,13 +802,13 @@ def main():
     counts = [unit_counts(spec, ops) for ops in groups]
     step_bytes = sum(c["shrink_bytes"] + c["expand_bytes"] for c in counts)
     step_flops = sum(c["shrink_flops"] + c["expand_flops"] for c in counts)
-    per_row = spec["form"] == "bgmv"
-    if args.handoff == "on" and not per_row:
-        raise SystemExit("--handoff on needs the per-row form (--form bgmv)")
+    decode_form = spec["form"] in ("bgmv", "sgmv")
+    if args.handoff == "on" and not decode_form:
+        raise SystemExit("--handoff on needs the per-row or segment form (--form bgmv or sgmv)")
     if args.handoff == "on" and args.fused_chunks >= 1:
         raise SystemExit("--handoff on and --fused-chunks >= 1 are two different one-launch forms")
-    # the library's hand-off form where it measures faster: dense weights, per-row form
-    handoff = args.handoff == "on" or (args.handoff == "auto" and per_row and spec["layout"] == "dense"
+    # the library's hand-off form where it measures faster: dense weights
+    handoff = args.handoff == "on" or (args.handoff == "auto" and decode_form and spec["layout"] == "dense"
                                        and args.fused_chunks < 1)
     if handoff:
         work = B.handoff_workspace(spec["batch"].n, device)

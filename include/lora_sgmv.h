@@ -300,6 +300,19 @@ size_t lora_handoff_bytes(int32_t n_rows);   /* 0 for n_rows <= 0 */
 int lora_bgmv_multi_handoff(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows,
                             int32_t n_proj, const lora_proj *proj, void *work, size_t work_bytes);
 
+/*
+ * The segment form's counterpart (Punica summary, "The SGMV Operator"): the result of
+ * lora_sgmv_shrink_multi followed by lora_sgmv_expand_multi, bit for bit, v included.
+ * With dense weights and tiles of fewer than 8 rows (seg->max_rows, the tile heights
+ * of decode batches) it is one launch that hands v over through `work` as above; with
+ * taller tiles (the MFMA kernels) or paged weights it makes those two launches and
+ * leaves `work` untouched.  `work` is checked (as above, for n_rows rows) either way.
+ * Every row may appear in at most one tile, as lora_build_tiles makes them.  Other
+ * arguments as for the two calls.
+ */
+int lora_sgmv_multi_handoff(void *stream, const void *x, int64_t ldx, int32_t n_rows, const lora_segments *seg,
+                            int32_t n_proj, const lora_proj *proj, void *work, size_t work_bytes);
+
 /* ---------------------------------------------------------------- adapter pool */
 /*
  * Loading adapters into the paged layout (S-LoRA summary, "Unified Paging" and

@@ -34,7 +34,7 @@ EXPORTS = ["lora_build_segments", "lora_tiles_bound", "lora_build_tiles", "lora_
            "lora_bgmv_shrink_multi", "lora_bgmv_expand_multi", "lora_pick_tile_rows", "lora_bgmv_multi",
            "lora_set_plan", "lora_pool_state_bytes", "lora_pool_init", "lora_pool_alloc", "lora_pool_release",
            "lora_pool_free_count", "lora_pool_pages_for", "lora_pool_load_header_bytes", "lora_pool_load",
-           "lora_handoff_bytes", "lora_bgmv_multi_handoff", "lora_set_handoff_polls"]
+           "lora_handoff_bytes", "lora_bgmv_multi_handoff", "lora_sgmv_multi_handoff", "lora_set_handoff_polls"]
 MAX_PROJ = 4
 
 
@@ -105,6 +105,7 @@ def lib() -> ctypes.CDLL:
             "lora_set_plan": [I32, I32],
             "lora_bgmv_multi_handoff": [P, P, I64, P, I32, I32, P, P, ctypes.c_size_t],
             "lora_set_handoff_polls": [I32],
+            "lora_sgmv_multi_handoff": [P, P, I64, I32, P, I32, P, P, ctypes.c_size_t],
             "lora_pool_init": [P, ctypes.c_size_t, I64],
             "lora_pool_alloc": [P, I32, P],
             "lora_pool_release": [P, I32, P],
@@ -375,6 +376,15 @@ def lora_bgmv_multi_handoff(x, idx, items, work, stream=None):
     arr = proj_list(items)
     _check(lib().lora_bgmv_multi_handoff(_stream(stream), _ptr(x), _ld(x), _ptr(idx), int(x.shape[0]), len(items),
                                          arr, _ptr(work), int(work.numel() * work.element_size())))
+
+
+def lora_sgmv_multi_handoff(x, segs, items, n_rows, work, stream=None):
+    """Shrink and expand of the segment form, in one launch with v handed off where the
+    tiles are short and the weights dense (otherwise the two launches); the bits of the
+    two calls."""
+    arr = proj_list(items)
+    _check(lib().lora_sgmv_multi_handoff(_stream(stream), _ptr(x), _ld(x), int(n_rows), segs.ref, len(items), arr,
+                                         _ptr(work), int(work.numel() * work.element_size())))
 
 
 def lora_bgmv_multi(x, idx, items, chunks=0, stream=None):

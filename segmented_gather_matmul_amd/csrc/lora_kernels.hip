@@ -76,8 +76,8 @@ struct TileSrc {
     const int32_t *idx;       // per-row form
 };
 
-// The one-launch per-row form that hands v from the shrink's workgroups to the expand's
-// (lora_bgmv_handoff_kernel): the grid holds the shrink's work items (laid out as in a
+// The one-launch form that hands v from the shrink's workgroups to the expand's
+// (lora_handoff_kernel): the grid holds the shrink's work items (laid out as in a
 // shrink launch: per_tile, off, p[].slices) and then the expand's.
 struct HandoffDev {
     uint32_t *work;                    // caller's workspace: kHandoffWords per (row, projection)
@@ -457,7 +457,7 @@ __device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *re
                 if (row >= 0 && j < jend) {
                     const float vj = j < rank ? s : 0.f;
                     float *dst = pd.v + (int64_t)row * pd.ldv + j;
-                    if constexpr (SINK == VSink::Lds) vlds[j] = vj;
+                    if constexpr (SINK == VSink::Lds) vlds[q * LORA_MAX_RANK + j] = vj;
                     else *dst = vj;
                     if constexpr (SINK == VSink::Handoff) {
                         uint32_t hv = ~__builtin_bit_cast(uint32_t, vj);
@@ -919,25 +919,29 @@ __global__ __launch_bounds__(kThreads) void lora_expand_valu_kernel(Args args)
 }
 
 // ------------------------------------------------------------------------ one launch, v handed off
-// Shrink and expand of the per-row form in one launch, v passed from the shrink's
-// workgroups to the expand's through a caller-owned workspace.  Workgroups [0,
-// n_shrink) run the shrink's work items and the rest the expand's.  The hardware hands
-// out workgroup ids in increasing order, so every shrink workgroup has a CU before any
-// expand workgroup that could wait for it, and shrink workgroups never wait; the waits
-// are bounded all the same, and correctness does not rest on that order.
+// Shrink and expand in one launch, v passed from the shrink's workgroups to the
+// expand's through a caller-owned workspace: the per-row form, and the segment form
+// with VALU tiles (up to 4 rows).  Workgroups [0, n_shrink) run the shrink's work items
+// and the rest the expand's.  The hardware hands out workgroup ids in increasing order,
+// so every shrink workgroup has a CU before any expand workgroup that could wait for
+// it, and shrink workgroups never wait; the waits are bounded all the same, and
+// correctness does not rest on that order.
 //   shrink workgroup: lora_shrink_valu_kernel's work item (same bits); besides v it
-//     stores its entries into the (row, projection) hand-off row, device-coherently and
-//     bit-inverted, so that the zero of a cleared row means "not yet";
-//   expand workgroup: requests y and its rank-rows of B, then polls the hand-off row
-//     (one device-coherent load per lane, at most `polls` times) until every entry is
-//     set, and runs lora_expand_valu_kernel's arithmetic on it (same bits).  When the
-//     poll limit runs out it computes the row's v itself with the shrink's arithmetic
-//     (same bits again), so the result never depends on scheduling;
+//     stores its entries into the hand-off row of each (row, projection),
+//     device-coherently and bit-inverted, so that the zero of a cleared row means
+//     "not yet";
+//   expand workgroup: requests y and its rank-rows of B, then polls the hand-off rows
+//     of its tile (wavefront q polls row q: one device-coherent load per lane, at most
+//     `polls` times) until every entry is set, and runs lora_expand_valu_kernel's
+//     arithmetic on them (same bits).  When the poll limit runs out it computes the
+//     tile's v itself with the shrink's arithmetic (same bits again), so the result
+//     never depends on scheduling;
 //   a counter per (row, projection) takes every count of the launch: shrink items add
 //     1 (bits 0-7) once their hand-off stores have completed, expand workgroups add
 //     1 << 8 when done; whichever count completes the fixed total clears the hand-off
 //     row and the counter, so the workspace is zero again when the launch ends, in any
-//     order of events.
+//     order of events.  This needs every row in at most one tile, as the tile builder
+//     makes them.
 // A v whose bits invert to zero (one NaN pattern) is handed off as the canonical NaN.
 constexpr int kHandoffWords = 128;  // per (row, projection): 64 hand-off entries, the counter on its own line
 
@@ -946,47 +950,67 @@ __device__ inline uint32_t *handoff_row(const HandoffDev &ho, int row, int p)
     return ho.work + (int64_t)kHandoffWords * (row * LORA_MAX_PROJ + p);
 }
 
-// Wavefront 0 of a workgroup adds `inc` to the (row, projection) counter; when that
-// completes the launch's total (`need` shrink items, `e` expand workgroups) it clears
-// the hand-off row (r_max entries) and the counter.
-__device__ inline void handoff_count(const HandoffDev &ho, int row, int p, uint32_t inc, uint32_t need, uint32_t e,
-                                     int r_max)
+// Wavefront 0 of a workgroup adds `inc` to the (row, projection) counters of the rows
+// it was given (lane q takes rows[q]; rows < 0 are skipped); a row whose count
+// completes the launch's total (`need` shrink items, `e` expand workgroups) gets its
+// hand-off row (r_max entries) and counter cleared.
+template <int NR>
+__device__ inline void handoff_count(const HandoffDev &ho, const int (&rows)[NR], int p, uint32_t inc, uint32_t need,
+                                     uint32_t e, int r_max)
 {
     const int lane = threadIdx.x & 63;
-    uint32_t *h = handoff_row(ho, row, p), *cnt = h + kHandoffWords / 2;
-    uint32_t now = 0;
-    if (lane == 0) now = __hip_atomic_fetch_add(cnt, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
-    now = __builtin_amdgcn_readfirstlane(now);
-    if ((now & 0xFF) == need && ((now >> 8) & 0xFFFF) == e) {
+    int my = -1;
+#pragma unroll
+    for (int q = 0; q < NR; ++q) my = lane == q ? rows[q] : my;
+    bool done = false;
+    if (my >= 0) {
+        uint32_t *cnt = handoff_row(ho, my, p) + kHandoffWords / 2;
+        const uint32_t now = __hip_atomic_fetch_add(cnt, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
+        done = (now & 0xFF) == need && ((now >> 8) & 0xFFFF) == e;
+    }
+    uint64_t m = __ballot(done);
+    while (m) {
+        const int q = __builtin_ctzll(m);
+        m &= m - 1;
+        const int row = __builtin_amdgcn_readlane(my, q);
+        uint32_t *h = handoff_row(ho, row, p);
         if (lane < r_max) __hip_atomic_store(h + lane, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) __hip_atomic_store(h + kHandoffWords / 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-// Work item `wi` of a list with `per_row` items per row, projection p's from off[p].
-__device__ inline Item row_item(int wi, int per_row, const int32_t *off, int n_proj, int n_rows)
+// Work item `wi` of a list with `per_tile` items per tile, projection p's from off[p].
+__device__ inline Item tile_item(int wi, int per_tile, const int32_t *off, int n_proj, int n_tiles)
 {
     Item it;
-    it.tile = wi / per_row;
-    const int sl = wi - it.tile * per_row;
+    it.tile = wi / per_tile;
+    const int sl = wi - it.tile * per_tile;
     int p = 0;
 #pragma unroll
     for (int q = 1; q < LORA_MAX_PROJ; ++q) p += (q < n_proj && sl >= off[q]) ? 1 : 0;
     it.p = p;
     it.slice = sl - off[p];
-    it.ok = it.tile < n_rows;
+    it.ok = it.tile < n_tiles;
     return it;
 }
 
-template <bool PAGED, int RJ, int RU>
-__global__ __launch_bounds__(kThreads) void lora_bgmv_handoff_kernel(Args args)
+// Rows of a tile with at most NR rows (-1 past its end or outside the row range).
+template <bool PERROW, int NR>
+__device__ inline void tile_rows(const Args &a, const TileHead &th, int (&rows)[NR])
+{
+#pragma unroll
+    for (int q = 0; q < NR; ++q) rows[q] = q < th.nrows ? row_of<PERROW>(a.ts, th.pos0 + q, a.n_rows) : -1;
+}
+
+template <bool PAGED, bool PERROW, int RJ, int NR, int RU>
+__global__ __launch_bounds__(kThreads) void lora_handoff_kernel(Args args)
 {
     const Args &a = kernel_args<!PAGED>(args);
-    constexpr int kDH = RJ == 1 ? 4 : 0;    // the shrink items' halves in flight (registers)
-    __shared__ float red[kWaves * 8 * 64];  // the shrink's kWaves * RJ sums or the expand's
+    constexpr int kDH = RJ + NR == 2 ? 4 : 0;    // the shrink items' halves in flight (registers)
+    __shared__ float red[kWaves * NR * 8 * 64];  // the shrink's kWaves * NR * RJ sums or the expand's
     __shared__ int pcache[PAGED ? kPageCache : 1];
-    __shared__ float vrow[LORA_MAX_RANK];
-    __shared__ int s_ok;
+    __shared__ float vrow[NR][LORA_MAX_RANK];
+    __shared__ int s_ok[NR];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x;
     // The item comes from kernel arguments read before the first branch (both parts'
@@ -995,30 +1019,35 @@ __global__ __launch_bounds__(kThreads) void lora_bgmv_handoff_kernel(Args args)
     int32_t off[LORA_MAX_PROJ];
 #pragma unroll
     for (int q = 0; q < LORA_MAX_PROJ; ++q) off[q] = shrink ? a.off[q] : a.ho.e_off[q];
-    const Item it = row_item(shrink ? b : b - a.ho.n_shrink, shrink ? a.per_tile : a.ho.e_per_tile, off, a.n_proj,
-                             a.n_rows);
+    const Item it = tile_item(shrink ? b : b - a.ho.n_shrink, shrink ? a.per_tile : a.ho.e_per_tile, off, a.n_proj,
+                              a.n_tiles);
     if (!it.ok) return;
     if (shrink) {
-        const bool stored = shrink_valu_item<PAGED, true, RJ, 1, VSink::Handoff, kDH>(a, it, red, pcache, nullptr);
+        const bool stored = shrink_valu_item<PAGED, PERROW, RJ, NR, VSink::Handoff, kDH>(a, it, red, pcache, nullptr);
         // wavefront 0 made every v store of this workgroup
         if (stored && wave == 0) {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the hand-off stores have completed
-            handoff_count(a.ho, it.tile, it.p, 1u, a.p[it.p].slices, a.ho.e_slices[it.p], a.p[it.p].w.r_max);
+            const ProjDev &pd = a.p[it.p];
+            int rows[NR];
+            tile_rows<PERROW, NR>(a, tile_head<PERROW>(a.ts, pd.w, it.tile), rows);
+            handoff_count<NR>(a.ho, rows, it.p, 1u, pd.slices, a.ho.e_slices[it.p], pd.w.r_max);
         }
         return;
     }
     const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
-    const TileHead th = tile_head<true>(a.ts, pd.w, it.tile);
+    const TileHead th = tile_head<PERROW>(a.ts, pd.w, it.tile);
     if (!th.valid) return;
     const int rank = slot_rank(pd.w, th.slot);
-    const int row = it.tile;
     const int jlim = PAGED ? rank : pd.w.r_max;
     const float sc = pd.w.scale[th.slot];
     const int c = it.slice * kCols + 8 * lane;
     const bool cin = c < pd.w.d_out;
-    ExpandPass<true, 1> ps;
-    ps.rows[0] = row;
-    ps.my_row = wave == 0 ? row : -1;
+    ExpandPass<PERROW, NR> ps;
+    tile_rows<PERROW, NR>(a, th, ps.rows);
+    ps.my_row = ps.rows[0];  // rows[wave] without a dynamically indexed register array
+#pragma unroll
+    for (int q = 1; q < NR; ++q) ps.my_row = wave == q ? ps.rows[q] : ps.my_row;
+    if (wave >= NR) ps.my_row = -1;
     const uint4 yv = ps.load_y(pd, c, cin);
     uint4 bv[RU];
     load_b_octets<PAGED, RU>(pd.w, th.slot, jlim, wave, 0, c, cin, bv);
@@ -1026,33 +1055,38 @@ __global__ __launch_bounds__(kThreads) void lora_bgmv_handoff_kernel(Args args)
     // counts, and its expand writes nothing.  Tested as a predicate rather than by an
     // early return so that the loads above are not held back behind the rank.
     const bool active = rank > 0;
-    if (wave == 0 && !active && lane == 0) s_ok = 1;
-    if (wave == 0 && active) {
-        const uint32_t *h = handoff_row(a.ho, row, it.p) + lane;
-        const bool mine = lane < pd.w.r_max;
-        uint32_t hv = 0;
-        bool ok = false;
-        for (int n = 0;; ++n) {
-            hv = mine ? __hip_atomic_load(h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
-            ok = __ballot(hv == 0) == 0;
-            if (ok || n >= a.ho.polls) break;
-            __builtin_amdgcn_s_sleep(8);
+    if (wave < NR) {
+        bool ok = true;
+        if (active && ps.my_row >= 0) {
+            const uint32_t *h = handoff_row(a.ho, ps.my_row, it.p) + lane;
+            const bool mine = lane < pd.w.r_max;
+            uint32_t hv = 0;
+            for (int n = 0;; ++n) {
+                hv = mine ? __hip_atomic_load(h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
+                ok = __ballot(hv == 0) == 0;
+                if (ok || n >= a.ho.polls) break;
+                __builtin_amdgcn_s_sleep(8);
+            }
+            if (ok && mine) vrow[wave][lane] = __builtin_bit_cast(float, ~hv);
         }
-        if (ok && mine) vrow[lane] = __builtin_bit_cast(float, ~hv);
-        if (lane == 0) s_ok = ok;
+        if (lane == 0) s_ok[wave] = ok;
     }
     __syncthreads();
-    if (!s_ok) {
+    bool all_ok = true;
+#pragma unroll
+    for (int q = 0; q < NR; ++q) all_ok = all_ok && s_ok[q];
+    if (!all_ok) {
         for (int sl = 0; sl < a.p[it.p].slices; ++sl) {
-            const Item si{row, it.p, sl, true};
+            const Item si{it.tile, it.p, sl, true};
             // one rank-row and one pair of halves at a time: few registers on a path
             // that only runs when the poll limit runs out
-            shrink_valu_item<PAGED, true, 1, 1, VSink::Lds, 2>(a, si, red, pcache, vrow);
+            shrink_valu_item<PAGED, PERROW, 1, NR, VSink::Lds, 2>(a, si, red, pcache, &vrow[0][0]);
         }
     }
-    ps.sv[0] = lane < pd.w.r_max ? vrow[lane] : 0.f;
-    expand_pass<true, 1, RU>(pd, ps, sc, rank, bv, yv, c, cin, red);
-    if (wave == 0 && active) handoff_count(a.ho, row, it.p, 1u << 8, a.p[it.p].slices, a.ho.e_slices[it.p], pd.w.r_max);
+#pragma unroll
+    for (int q = 0; q < NR; ++q) ps.sv[q] = lane < pd.w.r_max ? vrow[q][lane] : 0.f;
+    expand_pass<PERROW, NR, RU>(pd, ps, sc, rank, bv, yv, c, cin, red);
+    if (wave == 0 && active) handoff_count<NR>(a.ho, ps.rows, it.p, 1u << 8, pd.slices, a.ho.e_slices[it.p], pd.w.r_max);
 }
 
 // MFMA expand for tiles of up to 64 rows.  B[0:r][512 columns] is staged in LDS
@@ -1745,16 +1779,27 @@ constexpr int32_t kHandoffPolls = 1 << 15;  // ~30 ms of polling before computin
 thread_local int32_t t_handoff_polls = kHandoffPolls;
 constexpr int64_t kResidentGroups = 2048;   // 256 CUs x 8 workgroups of 4 wavefronts (<= 64 VGPRs)
 
-// Per-row form in one launch with v handed off (lora_bgmv_handoff_kernel).  Arguments
-// other than the workspace are checked by the caller.
-int handoff_row_impl(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows, int32_t n_proj,
-                     const lora_proj *proj, Args &a, bool paged, void *work, size_t work_bytes)
+int check_workspace(const void *work, size_t work_bytes, int32_t n_rows)
 {
     if (!work) return fail(LORA_E_NULL, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(work) & 255) return fail(LORA_E_ALIGN, "workspace must be 256-byte aligned");
     if (work_bytes < lora_handoff_bytes(n_rows))
         return fail(LORA_E_SHAPE, "workspace of %zu bytes < %zu for %d rows", work_bytes, lora_handoff_bytes(n_rows),
                     n_rows);
+    return LORA_OK;
+}
+
+// One launch with v handed off (lora_handoff_kernel) over n_tiles tiles of at most
+// max_rows rows (the per-row form: one row per tile).  Arguments other than the
+// workspace are checked by the caller; the segment form comes here with dense weights
+// and tiles of fewer than kMfmaMinRows rows only.
+template <bool PERROW>
+int handoff_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSrc ts, int32_t n_tiles,
+                 int32_t max_rows, int32_t n_proj, const lora_proj *proj, Args &a, bool paged, void *work,
+                 size_t work_bytes)
+{
+    int st = check_workspace(work, work_bytes, n_rows);
+    if (st) return st;
     int32_t r_max = 0, e_per_tile = 0;
     for (int32_t p = 0; p < n_proj; ++p) r_max = std::max(r_max, proj[p].w->r_max);
     for (int32_t p = 0; p < LORA_MAX_PROJ; ++p) {
@@ -1765,44 +1810,51 @@ int handoff_row_impl(void *stream, const void *x, int64_t ldx, const int32_t *id
         e_per_tile += a.ho.e_slices[p];
     }
     a.ho.e_per_tile = e_per_tile;
-    // rank-rows per shrink item: the narrowest that keeps both parts within what the
-    // CUs hold at once, else 4
-    a.jw = 1;
+    // rank-rows per shrink item: at least the separate shrink's choice, and the narrowest
+    // that keeps both parts within what the CUs hold at once, else 4
+    a.jw = plan_shrink_jw(n_tiles * n_proj, r_max);
     for (;; a.jw *= 2) {
-        int64_t s_per_row = 0;
-        for (int32_t p = 0; p < n_proj; ++p) s_per_row += (proj[p].w->r_max + a.jw - 1) / a.jw;
-        if (a.jw == 4 || n_rows * (s_per_row + e_per_tile) <= kResidentGroups) break;
+        int64_t s_per_tile = 0;
+        for (int32_t p = 0; p < n_proj; ++p) s_per_tile += (proj[p].w->r_max + a.jw - 1) / a.jw;
+        if (a.jw >= 4 || n_tiles * (s_per_tile + e_per_tile) <= kResidentGroups) break;
     }
     if (t_plan_jw > 0) a.jw = t_plan_jw;
     for (int32_t p = 0; p < n_proj; ++p) a.p[p].slices = (proj[p].w->r_max + a.jw - 1) / a.jw;
-    int st = finish_layout(a, n_rows);
-    if (st) return st;
-    const int64_t groups = (int64_t)n_rows * (a.per_tile + e_per_tile);
+    if ((st = finish_layout(a, n_tiles))) return st;
+    const int64_t groups = (int64_t)n_tiles * (a.per_tile + e_per_tile);
     if (groups > ((int64_t)1 << 30)) return fail(LORA_E_SHAPE, "launch of %lld workgroups is too large", (long long)groups);
     a.ho.work = static_cast<uint32_t *>(work);
-    a.ho.n_shrink = n_rows * a.per_tile;
+    a.ho.n_shrink = n_tiles * a.per_tile;
     a.ho.polls = t_handoff_polls;
     a.grid = (int32_t)groups;
     a.x = static_cast<const uint16_t *>(x);
     a.ldx = ldx;
     a.n_rows = n_rows;
-    a.n_tiles = n_rows;
-    a.ts = row_src(idx);
+    a.n_tiles = n_tiles;
+    a.ts = ts;
     const dim3 grid((unsigned)a.grid);
     hipStream_t s = static_cast<hipStream_t>(stream);
-#define LORA_HANDOFF(RJ, RU)                                                                 \
-    (paged ? launch(lora_bgmv_handoff_kernel<true, RJ, RU>, grid, kThreads, 0, s, a)         \
-           : launch(lora_bgmv_handoff_kernel<false, RJ, RU>, grid, kThreads, 0, s, a))
-#define LORA_HANDOFF_RU(RJ)                     \
-    if (r_max <= 16) LORA_HANDOFF(RJ, 4);       \
-    else if (r_max <= 32) LORA_HANDOFF(RJ, 8);  \
-    else LORA_HANDOFF(RJ, 16)
-    if (a.jw == 1) { LORA_HANDOFF_RU(1); }
-    else if (a.jw == 2) { LORA_HANDOFF_RU(2); }
-    else { LORA_HANDOFF_RU(4); }
+#define LORA_HANDOFF_RU(PG, RJ, NR)                                                           \
+    if (r_max <= 16) launch(lora_handoff_kernel<PG, PERROW, RJ, NR, 4>, grid, kThreads, 0, s, a); \
+    else if (r_max <= 32) launch(lora_handoff_kernel<PG, PERROW, RJ, NR, 8>, grid, kThreads, 0, s, a); \
+    else launch(lora_handoff_kernel<PG, PERROW, RJ, NR, 16>, grid, kThreads, 0, s, a)
+#define LORA_HANDOFF_JW(PG, NR)                      \
+    if (a.jw == 1) { LORA_HANDOFF_RU(PG, 1, NR); }    \
+    else if (a.jw == 2) { LORA_HANDOFF_RU(PG, 2, NR); } \
+    else { LORA_HANDOFF_RU(PG, 4, NR); }
+    if constexpr (PERROW) {
+        (void)max_rows;
+        if (paged) { LORA_HANDOFF_JW(true, 1) }
+        else { LORA_HANDOFF_JW(false, 1) }
+    } else {
+        const int nr = rows_per_pass(max_rows);
+        if (nr == 1) { LORA_HANDOFF_JW(false, 1) }
+        else if (nr == 2) { LORA_HANDOFF_JW(false, 2) }
+        else { LORA_HANDOFF_JW(false, 4) }
+    }
+#undef LORA_HANDOFF_JW
 #undef LORA_HANDOFF_RU
-#undef LORA_HANDOFF
-    return launch_status("bgmv with v handed off");
+    return launch_status("shrink and expand with v handed off");
 }
 
 inline int32_t seg_max_rows(const lora_segments *seg) { return seg->max_rows > 0 ? seg->max_rows : LORA_MAX_TILE_ROWS; }
@@ -1977,7 +2029,36 @@ int lora_bgmv_multi_handoff(void *stream, const void *x, int64_t ldx, const int3
     bool paged = false;
     int st = check_bgmv_multi(x, ldx, idx, n_rows, n_proj, proj, a, paged);
     if (st || n_rows == 0) return st;
-    return handoff_row_impl(stream, x, ldx, idx, n_rows, n_proj, proj, a, paged, work, work_bytes);
+    return handoff_impl<true>(stream, x, ldx, n_rows, row_src(idx), n_rows, 1, n_proj, proj, a, paged, work,
+                              work_bytes);
+}
+
+int lora_sgmv_multi_handoff(void *stream, const void *x, int64_t ldx, int32_t n_rows, const lora_segments *seg,
+                            int32_t n_proj, const lora_proj *proj, void *work, size_t work_bytes)
+{
+    clear_error();
+    Args a{};
+    bool paged = false;
+    int st = check_segments(seg);
+    if (st) return st;
+    if ((st = check_projs(n_proj, proj, true, a, paged))) return st;
+    for (int32_t p = 1; p < n_proj; ++p)
+        if (proj[p].w->d_in != proj[0].w->d_in)
+            return fail(LORA_E_SHAPE, "projections of one launch share x: d_in %d != %d", proj[p].w->d_in,
+                        proj[0].w->d_in);
+    if (n_rows < 0) return fail(LORA_E_SHAPE, "n_rows = %d", n_rows);
+    if (n_rows == 0 || seg->n_tiles == 0) return LORA_OK;
+    if ((st = check_rows_arg(x, ldx, proj[0].w->d_in, 8, "x"))) return st;
+    const int32_t max_rows = seg_max_rows(seg);
+    if (paged || max_rows >= kMfmaMinRows) {
+        // the two launches: the MFMA kernels' tiles and paged weights hand nothing off
+        if ((st = check_workspace(work, work_bytes, n_rows))) return st;
+        st = shrink_impl<false>(stream, x, ldx, n_rows, seg_src(seg), seg->n_tiles, max_rows, n_proj, proj);
+        if (st) return st;
+        return expand_impl<false>(stream, n_rows, seg_src(seg), seg->n_tiles, max_rows, n_proj, proj);
+    }
+    return handoff_impl<false>(stream, x, ldx, n_rows, seg_src(seg), seg->n_tiles, max_rows, n_proj, proj, a, paged,
+                               work, work_bytes);
 }
 
 int lora_set_handoff_polls(int32_t polls)

@@ -11,9 +11,10 @@ work-list and row map of the segment form built once on the host from those ids
 q/k/v come from one backbone GEMM against a [h, 3h] weight and gate/up from one against
 [h, 2f]; their add-ons land in column slices of that output through the row-stride
 argument (ldy = 3h or 2f).  q/k/v share one call over three projections (same x), and
-gate/up another, so a layer makes four add-on calls; in the per-row form each is one
-launch.  Optionally each shrink runs on a second stream while the backbone GEMM of the
-same input runs, so only the expands stay on the layer's critical path.
+gate/up another, so a layer makes four add-on calls, each one launch (in the segment
+form, for tiles of fewer than 8 rows).  Optionally each shrink runs on a second stream
+while the backbone GEMM of the same input runs, so only the expands stay on the layer's
+critical path.
 
 Left out of the step on purpose: rotary position embedding (elementwise on q and k) and
 sampling.  The current token's k and v are written into the last position of the cache,
@@ -104,10 +105,11 @@ class LoraDecoderLayer:
     w_d [f, h] (all applied as x @ W), norm1 [h], norm2 [h].
     adapters: proj -> (a_t [S, r_max, d_in], b [S, r_max, d_out]) fp16 device tensors.
     rank (int32 [S]) and scale (fp32 [S]) are the slots' ranks and scales, shared by the
-    seven projections.  max_rows bounds the batch (it sizes the v buffers).  In the per-row
-    form each add-on call is one launch that hands v from the shrink's workgroups to the
-    expand's (handoff, through a workspace the layer owns); with handoff False, chunks is
-    passed to lora_bgmv_multi (0: the library's choice of one or two launches).  overlap:
+    seven projections.  max_rows bounds the batch (it sizes the v buffers).  Each add-on call
+    hands v from the shrink's workgroups to the expand's in one launch (handoff, through a
+    workspace the layer owns; the segment form does so for tiles of fewer than 8 rows);
+    with handoff False, chunks is passed to the per-row form's lora_bgmv_multi (0: the
+    library's choice of one or two launches).  overlap:
     each shrink runs on a second stream (default priority) concurrently with the backbone
     GEMM of its projections, the expand after that GEMM.  The results are the same bits
     in every case."""
@@ -178,6 +180,8 @@ class LoraDecoderLayer:
                 B.lora_bgmv_multi_handoff(x, meta.idx, items, self.work)
             elif meta.form == "bgmv":
                 B.lora_bgmv_multi(x, meta.idx, items, chunks=self.chunks)
+            elif self.work is not None:
+                B.lora_sgmv_multi_handoff(x, meta.segs, items, n, self.work)
             else:
                 B.lora_sgmv_shrink_multi(x, meta.segs, items)
                 B.lora_sgmv_expand_multi(meta.segs, items, n)

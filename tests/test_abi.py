@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 32 and set(names) == set(B.EXPORTS)
+    assert len(names) == 33 and set(names) == set(B.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", build_mod.LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (lora_\w+)", out))
@@ -333,6 +333,23 @@ def test_handoff_decode_errors():
     assert call() == B.LORA_E_SHAPE and "too wide" in B.last_error()
     assert call(n=0, work=None, nbytes=0) == B.LORA_OK                 # no rows: nothing is read or launched
     assert L.lora_set_handoff_polls(0) == B.LORA_OK and L.lora_set_handoff_polls(-1) == B.LORA_OK
+    # the segment form: its own segment checks, then the same workspace checks
+    arr[1].w, arr[1].ldy = ctypes.addressof(c1), 1024
+    seg = B.CSegments()
+    seg.n_tiles, seg.tiles, seg.row_map, seg.n_pos, seg.max_rows = 4, FAKE, FAKE, 8, 2
+    scall = lambda s_=seg, n=8, work=FAKE, nbytes=need: \
+        L.lora_sgmv_multi_handoff(None, FAKE, 1024, n, ctypes.byref(s_) if s_ is not None else None, 2, arr, work,
+                                  nbytes)
+    assert scall(s_=None) == B.LORA_E_NULL
+    assert scall(work=None) == B.LORA_E_NULL and "workspace" in B.last_error()
+    assert scall(work=FAKE + 64) == B.LORA_E_ALIGN
+    assert scall(nbytes=need - 4) == B.LORA_E_SHAPE
+    seg.max_rows = 16                                                   # MFMA tiles: two launches, same checks
+    assert scall(work=None) == B.LORA_E_NULL
+    seg.max_rows = 65
+    assert scall() == B.LORA_E_SHAPE
+    seg.max_rows = 2
+    assert scall(n=0, work=None) == B.LORA_OK
 
 
 def test_set_plan_ranges():

@@ -1,7 +1,10 @@
-"""GPU: the decode form in one launch with v handed from the shrink's workgroups to the
-expand's (lora_bgmv_multi_handoff) against the two-launch path (lora_bgmv_multi with
-chunks = -1), bit for bit on whole buffers (guard rows and padding included), and the
-two-launch path against the fp64 oracle.
+"""GPU: shrink and expand in one launch with v handed from the shrink's workgroups to the
+expand's, against the two-launch path bit for bit on whole buffers (guard rows and
+padding included), and the two-launch path against the fp64 oracle: the per-row form
+(lora_bgmv_multi_handoff vs lora_bgmv_multi with chunks = -1) and the segment form
+(lora_sgmv_multi_handoff vs lora_sgmv_shrink_multi + lora_sgmv_expand_multi, over tiles
+of 1, 2 and 4 rows, and over taller tiles and paged weights, where it makes the two
+launches itself).
 
 Every case runs the hand-off form twice: with the default poll limit, and with the limit
 at zero, where every expand workgroup computes its row's v itself (the path taken when
@@ -144,6 +147,80 @@ def test_paged_70b_shapes(work):
     base = _compare("paged-70b", dc.x, dev(b.idx), [w], [dc], work)
     y_ref, v_ref = oracle.bgmv(ostore, x, y0, b.idx, nthreads=16)
     G.check(dc, *base[0], y_ref, v_ref, G.active_rows(b.idx, rank), "handoff-paged-70b")
+
+
+def _segs(idx, num_slots, tile_rows):
+    row_map, seg_ptr, seg_slot, n_act = B.lora_build_segments(idx, num_slots)
+    tiles = B.lora_build_tiles(seg_ptr, seg_slot, tile_rows)
+    return B.segments_to_device(tiles, row_map, n_act)
+
+
+def _compare_sgmv(label, x_d, segs, n, ws, dcs, work, expect_clear=True):
+    """Two launches, then the segment-form hand-off at the default and at a zero poll
+    limit; returns the two-launch results."""
+    results = {}
+    for mode in ("two", "handoff", "local"):
+        for dc in dcs:
+            dc.reset()
+        items = [(w, dc.v, dc.y) for w, dc in zip(ws, dcs)]
+        if mode == "two":
+            B.lora_sgmv_shrink_multi(x_d, segs, items, n)
+            B.lora_sgmv_expand_multi(segs, items, n)
+        else:
+            B.lora_set_handoff_polls(0 if mode == "local" else -1)
+            try:
+                B.lora_sgmv_multi_handoff(x_d, segs, items, n, work)
+            finally:
+                B.lora_set_handoff_polls(-1)
+        results[mode] = [dc.results() for dc in dcs]
+        _assert_clear(work, f"{label} {mode}")
+    base = results["two"]
+    for mode in ("handoff", "local"):
+        for p, ((yb, vb), (yg, vg)) in enumerate(zip(base, results[mode])):
+            assert np.array_equal(yb.view(np.uint16), yg.view(np.uint16)), f"{label}: {mode} proj {p}: y"
+            assert np.array_equal(vb.view(np.uint32), vg.view(np.uint32)), f"{label}: {mode} proj {p}: v"
+    return base
+
+
+def _case_sgmv(work, label, cfg, layout, d_in, outs, rank, idx, tile_rows, r_max=64):
+    G.say(f"case handoff-sgmv-{label} layout={layout} n={len(idx)} {d_in}->{outs} r_max={r_max} tiles={tile_rows}")
+    stores = _stores(cfg, layout, d_in, outs, np.asarray(rank, dtype=np.int32), r_max)
+    x, _ = wl.activations(cfg, 0, len(idx), d_in, 8)
+    y0s = [wl.activations(cfg, 20 + p, len(idx), 8, d_out)[1] for p, d_out in enumerate(outs)]
+    ws = [B.weights_from_store(st) for st in stores]
+    dcs = [G.DeviceCase(x, y0, st.r_max) for y0, st in zip(y0s, stores)]
+    segs = _segs(idx, len(rank), tile_rows)
+    base = _compare_sgmv(label, dcs[0].x, segs, len(idx), ws, dcs, work)
+    for p, (st, dc) in enumerate(zip(stores, dcs)):
+        y_ref, v_ref = oracle.bgmv(st, x, y0s[p], idx, nthreads=16)
+        yb, vb = base[p]
+        G.check(dc, yb, vb, y_ref, v_ref, G.active_rows(idx, st.rank), f"handoff-sgmv-{label}-p{p}")
+
+
+@pytest.mark.parametrize("pop", ["uniform", "skewed", "identical"])
+def test_sgmv_decode_13b_mixes(work, pop):
+    """The 13B decode mixes (64 rows, 16 slots of rank 64, 10 % of rows without
+    adapter) at their own tile heights, q/k/v in one call."""
+    b = wl.batch_decode_mix(pop)
+    seg_ptr = B.lora_build_segments(b.idx, 16)[1]
+    _case_sgmv(work, f"13b-{pop}", 3, "dense", 5120, (5120, 5120, 5120), [64] * 16, b.idx,
+               B.lora_pick_tile_rows(seg_ptr))
+
+
+@pytest.mark.parametrize("tile_rows", [1, 2, 4])
+def test_sgmv_ragged_mixed_ranks(work, tile_rows):
+    """Rows in shuffled order (row map), ranks 0..64, widths off the 512-column and
+    256-octet grids, tiles of 1, 2 and 4 rows."""
+    idx = np.random.default_rng(17).integers(-1, 7, size=150).astype(np.int32)
+    _case_sgmv(work, f"ragged-t{tile_rows}", 11, "dense", 1288, (1064, 56, 2632), [1, 64, 0, 17, 8, 33, 64], idx,
+               tile_rows)
+
+
+@pytest.mark.parametrize("layout,tile_rows", [("dense", 16), ("dense", 64), ("paged8", 4)])
+def test_sgmv_two_launch_cases(work, layout, tile_rows):
+    """Taller tiles (MFMA kernels) and paged weights: the call makes the two launches."""
+    idx = np.random.default_rng(19).integers(-1, 5, size=96).astype(np.int32)
+    _case_sgmv(work, f"{layout}-t{tile_rows}", 12, layout, 2048, (2048, 1024), [16, 8, 64, 0, 32], idx, tile_rows)
 
 
 def test_graph_replays_share_the_workspace_with_eager_calls(work):
