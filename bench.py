@@ -869,7 +869,7 @@ def main():
     dom = max(per_kernel, key=lambda k: totals[k])
     pk = per_kernel[dom]
     kernel_name = {"shrink": "lora_shrink_kernel", "expand": "lora_expand_kernel", "fused": "lora_fused_row_kernel",
-                   "handoff": "lora_bgmv_handoff_kernel"}[dom]
+                   "handoff": "lora_handoff_kernel"}[dom]
     traffic = None if args.rows is not None else traffic_from_profile(args.workload, dom)
     roofline = dict(bound="hbm", achieved=pk["gbs"], peak=cm.HBM_PEAK_GBS, unit="GB/s",
                     frac=round(pk["gbs"] / cm.HBM_PEAK_GBS, 4), traffic=traffic, kernel=kernel_name,
