@@ -408,11 +408,11 @@ def sweep_assign(pop, n, seed):
 
 
 def operator_sweep(args):
-    """One LoRA operator (shrink + expand, h -> r -> h) per configuration, timed for four
+    """One LoRA operator (shrink + expand, h -> r -> h) per configuration, timed for six
     implementations on the same inputs: this library's segment form (one shrink and one
-    expand launch over contiguous segments) and per-row form, a loop over adapters (two
-    fp16 GEMMs and an add per segment) and Gather-BMM (per-row copies of A and B, then two
-    batched products).  Each implementation's L layers (distinct weights, so the adapters
+    expand launch over contiguous segments) and per-row form, each also in its one-launch
+    hand-off form, a loop over adapters (two fp16 GEMMs and an add per segment) and
+    Gather-BMM (per-row copies of A and B, then two batched products).  Each implementation's L layers (distinct weights, so the adapters
     stream from HBM) are captured in one graph and replayed; the result is us per operator.
     The last two are plain PyTorch, timing context only."""
     import torch
@@ -457,6 +457,14 @@ def operator_sweep(args):
                 def ours_bgmv(lay, y):
                     B.lora_bgmv(y, lay["x"], idx_d, lay["w"], lay["v"])
 
+                work = B.handoff_workspace(n, dev)
+
+                def ours_sgmv_handoff(lay, y):
+                    B.lora_sgmv_multi_handoff(lay["x"], segs, [(lay["w"], lay["v"], y)], n, work)
+
+                def ours_bgmv_handoff(lay, y):
+                    B.lora_bgmv_multi_handoff(lay["x"], idx_d, [(lay["w"], lay["v"], y)], work)
+
                 def loop(lay, y):
                     for g in range(len(seg_slot)):
                         a0, a1, s_ = int(seg_ptr[g]), int(seg_ptr[g + 1]), int(seg_slot[g])
@@ -468,7 +476,8 @@ def operator_sweep(args):
                     vv = torch.bmm(lay["x"].unsqueeze(1), ag)
                     y.add_(torch.bmm(vv, bg).squeeze(1), alpha=scale)
 
-                impls = dict(ours_sgmv=ours_sgmv, ours_bgmv=ours_bgmv, loop=loop, gather_bmm=gather_bmm)
+                impls = dict(ours_sgmv=ours_sgmv, ours_bgmv=ours_bgmv, ours_sgmv_handoff=ours_sgmv_handoff,
+                             ours_bgmv_handoff=ours_bgmv_handoff, loop=loop, gather_bmm=gather_bmm)
                 rec = dict(h=h, r=r, popularity=pop, n=n, adapters=len(seg_slot))
                 # the same result from each, on a fresh copy of layer 0's y
                 outs = {}
