@@ -387,9 +387,11 @@ enum class VSink { Global, Lds, Handoff };
 // shrink_valu_item runs one work item.  It returns true when it stored v (a valid
 // tile whose slot has a non-zero rank), the same for every thread of the workgroup.
 // DH: halves of octet pairs in flight together (0: about 16 loads per lane); it changes
-// the batching of the loads, not the order of any sum.
+// the batching of the loads, not the order of any sum.  only_rg >= 0: only the pass over
+// the tile's rows [only_rg, only_rg + NR).
 template <bool PAGED, bool PERROW, int RJ, int NR, VSink SINK, int DH = 0>
-__device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *red, int *pcache, float *vlds)
+__device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *red, int *pcache, float *vlds,
+                                        int only_rg = -1)
 {
     // halves in flight together: about 16 loads per lane, an even count (whole pairs)
     constexpr int D = DH > 0 ? DH : (16 / (NR + RJ)) & ~1 ? (16 / (NR + RJ)) & ~1 : 2;
@@ -409,7 +411,7 @@ __device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *re
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_oct = pd.w.d_in >> 3;
     const int n_half = 2 * ((n_oct + 2 * kThreads - 1) / (2 * kThreads));  // halves of octet pairs, even
-    for (int rg = 0; rg < th.nrows; rg += NR) {
+    for (int rg = only_rg < 0 ? 0 : only_rg; rg < th.nrows; rg += NR) {
         int rows[NR];
 #pragma unroll
         for (int q = 0; q < NR; ++q)
@@ -469,6 +471,7 @@ __device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *re
             }
             __syncthreads();
         }
+        if (only_rg >= 0) break;
     }
     return rank > 0;
 }
@@ -994,12 +997,13 @@ __device__ inline Item tile_item(int wi, int per_tile, const int32_t *off, int n
     return it;
 }
 
-// Rows of a tile with at most NR rows (-1 past its end or outside the row range).
+// Rows rg .. rg + NR - 1 of a tile (-1 past its end or outside the row range).
 template <bool PERROW, int NR>
-__device__ inline void tile_rows(const Args &a, const TileHead &th, int (&rows)[NR])
+__device__ inline void tile_rows(const Args &a, const TileHead &th, int rg, int (&rows)[NR])
 {
 #pragma unroll
-    for (int q = 0; q < NR; ++q) rows[q] = q < th.nrows ? row_of<PERROW>(a.ts, th.pos0 + q, a.n_rows) : -1;
+    for (int q = 0; q < NR; ++q)
+        rows[q] = rg + q < th.nrows ? row_of<PERROW>(a.ts, th.pos0 + rg + q, a.n_rows) : -1;
 }
 
 template <bool PAGED, bool PERROW, int RJ, int NR, int RU>
@@ -1028,9 +1032,12 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(Args args)
         if (stored && wave == 0) {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the hand-off stores have completed
             const ProjDev &pd = a.p[it.p];
-            int rows[NR];
-            tile_rows<PERROW, NR>(a, tile_head<PERROW>(a.ts, pd.w, it.tile), rows);
-            handoff_count<NR>(a.ho, rows, it.p, 1u, pd.slices, a.ho.e_slices[it.p], pd.w.r_max);
+            const TileHead th = tile_head<PERROW>(a.ts, pd.w, it.tile);
+            for (int rg = 0; rg < th.nrows; rg += NR) {
+                int rows[NR];
+                tile_rows<PERROW, NR>(a, th, rg, rows);
+                handoff_count<NR>(a.ho, rows, it.p, 1u, pd.slices, a.ho.e_slices[it.p], pd.w.r_max);
+            }
         }
         return;
     }
@@ -1042,8 +1049,31 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(Args args)
     const float sc = pd.w.scale[th.slot];
     const int c = it.slice * kCols + 8 * lane;
     const bool cin = c < pd.w.d_out;
+    if (th.nrows > NR) {
+        // A tile taller than the launch was planned for (the row height is only a hint):
+        // each row's v computed here with the shrink's arithmetic, no waiting, one row at
+        // a time (a cold path kept to the registers of the one-row kernels).
+        for (int r = 0; r < th.nrows; ++r) {
+            for (int sl = 0; sl < a.p[it.p].slices; ++sl) {
+                const Item si{it.tile, it.p, sl, true};
+                shrink_valu_item<PAGED, PERROW, 1, 1, VSink::Lds, 2>(a, si, red, pcache, &vrow[0][0], r);
+            }
+            ExpandPass<PERROW, 1> ps;
+            tile_rows<PERROW, 1>(a, th, r, ps.rows);
+            ps.my_row = wave == 0 ? ps.rows[0] : -1;
+            const uint4 yv = ps.load_y(pd, c, cin);
+            uint4 bw[RU];
+            load_b_octets<PAGED, RU>(pd.w, th.slot, jlim, wave, 0, c, cin, bw);
+            ps.sv[0] = lane < pd.w.r_max ? vrow[0][lane] : 0.f;
+            expand_pass<PERROW, 1, RU>(pd, ps, sc, rank, bw, yv, c, cin, red);
+            if (wave == 0 && rank > 0)
+                handoff_count<1>(a.ho, ps.rows, it.p, 1u << 8, pd.slices, a.ho.e_slices[it.p], pd.w.r_max);
+        }
+        return;
+    }
+    // the tile's rows (at most NR): y, then B, then v from the hand-off
     ExpandPass<PERROW, NR> ps;
-    tile_rows<PERROW, NR>(a, th, ps.rows);
+    tile_rows<PERROW, NR>(a, th, 0, ps.rows);
     ps.my_row = ps.rows[0];  // rows[wave] without a dynamically indexed register array
 #pragma unroll
     for (int q = 1; q < NR; ++q) ps.my_row = wave == q ? ps.rows[q] : ps.my_row;
@@ -1055,38 +1085,41 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(Args args)
     // counts, and its expand writes nothing.  Tested as a predicate rather than by an
     // early return so that the loads above are not held back behind the rank.
     const bool active = rank > 0;
-    if (wave < NR) {
-        bool ok = true;
-        if (active && ps.my_row >= 0) {
-            const uint32_t *h = handoff_row(a.ho, ps.my_row, it.p) + lane;
-            const bool mine = lane < pd.w.r_max;
-            uint32_t hv = 0;
-            for (int n = 0;; ++n) {
-                hv = mine ? __hip_atomic_load(h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
-                ok = __ballot(hv == 0) == 0;
-                if (ok || n >= a.ho.polls) break;
-                __builtin_amdgcn_s_sleep(8);
+    {
+        if (wave < NR) {
+            bool ok = true;
+            if (active && ps.my_row >= 0) {
+                const uint32_t *h = handoff_row(a.ho, ps.my_row, it.p) + lane;
+                const bool mine = lane < pd.w.r_max;
+                uint32_t hv = 0;
+                for (int n = 0;; ++n) {
+                    hv = mine ? __hip_atomic_load(h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 1u;
+                    ok = __ballot(hv == 0) == 0;
+                    if (ok || n >= a.ho.polls) break;
+                    __builtin_amdgcn_s_sleep(8);
+                }
+                if (ok && mine) vrow[wave][lane] = __builtin_bit_cast(float, ~hv);
             }
-            if (ok && mine) vrow[wave][lane] = __builtin_bit_cast(float, ~hv);
+            if (lane == 0) s_ok[wave] = ok;
         }
-        if (lane == 0) s_ok[wave] = ok;
-    }
-    __syncthreads();
-    bool all_ok = true;
+        __syncthreads();
+        bool all_ok = true;
 #pragma unroll
-    for (int q = 0; q < NR; ++q) all_ok = all_ok && s_ok[q];
-    if (!all_ok) {
-        for (int sl = 0; sl < a.p[it.p].slices; ++sl) {
-            const Item si{it.tile, it.p, sl, true};
-            // one rank-row and one pair of halves at a time: few registers on a path
-            // that only runs when the poll limit runs out
-            shrink_valu_item<PAGED, PERROW, 1, NR, VSink::Lds, 2>(a, si, red, pcache, &vrow[0][0]);
+        for (int q = 0; q < NR; ++q) all_ok = all_ok && s_ok[q];
+        if (!all_ok) {
+            for (int sl = 0; sl < a.p[it.p].slices; ++sl) {
+                const Item si{it.tile, it.p, sl, true};
+                // one rank-row and one pair of halves at a time: few registers on a path
+                // that only runs when the poll limit runs out
+                shrink_valu_item<PAGED, PERROW, 1, NR, VSink::Lds, 2>(a, si, red, pcache, &vrow[0][0], 0);
+            }
         }
-    }
 #pragma unroll
-    for (int q = 0; q < NR; ++q) ps.sv[q] = lane < pd.w.r_max ? vrow[q][lane] : 0.f;
-    expand_pass<PERROW, NR, RU>(pd, ps, sc, rank, bv, yv, c, cin, red);
-    if (wave == 0 && active) handoff_count<NR>(a.ho, ps.rows, it.p, 1u << 8, pd.slices, a.ho.e_slices[it.p], pd.w.r_max);
+        for (int q = 0; q < NR; ++q) ps.sv[q] = lane < pd.w.r_max ? vrow[q][lane] : 0.f;
+        expand_pass<PERROW, NR, RU>(pd, ps, sc, rank, bv, yv, c, cin, red);
+        if (wave == 0 && active)
+            handoff_count<NR>(a.ho, ps.rows, it.p, 1u << 8, pd.slices, a.ho.e_slices[it.p], pd.w.r_max);
+    }
 }
 
 // MFMA expand for tiles of up to 64 rows.  B[0:r][512 columns] is staged in LDS

@@ -149,10 +149,13 @@ def test_paged_70b_shapes(work):
     G.check(dc, *base[0], y_ref, v_ref, G.active_rows(b.idx, rank), "handoff-paged-70b")
 
 
-def _segs(idx, num_slots, tile_rows):
+def _segs(idx, num_slots, tile_rows, hint=None):
     row_map, seg_ptr, seg_slot, n_act = B.lora_build_segments(idx, num_slots)
     tiles = B.lora_build_tiles(seg_ptr, seg_slot, tile_rows)
-    return B.segments_to_device(tiles, row_map, n_act)
+    segs = B.segments_to_device(tiles, row_map, n_act)
+    if hint is not None:
+        segs.c.max_rows = hint  # a launch-shape hint below the real tile height
+    return segs
 
 
 def _compare_sgmv(label, x_d, segs, n, ws, dcs, work, expect_clear=True):
@@ -182,14 +185,14 @@ def _compare_sgmv(label, x_d, segs, n, ws, dcs, work, expect_clear=True):
     return base
 
 
-def _case_sgmv(work, label, cfg, layout, d_in, outs, rank, idx, tile_rows, r_max=64):
+def _case_sgmv(work, label, cfg, layout, d_in, outs, rank, idx, tile_rows, r_max=64, hint=None):
     G.say(f"case handoff-sgmv-{label} layout={layout} n={len(idx)} {d_in}->{outs} r_max={r_max} tiles={tile_rows}")
     stores = _stores(cfg, layout, d_in, outs, np.asarray(rank, dtype=np.int32), r_max)
     x, _ = wl.activations(cfg, 0, len(idx), d_in, 8)
     y0s = [wl.activations(cfg, 20 + p, len(idx), 8, d_out)[1] for p, d_out in enumerate(outs)]
     ws = [B.weights_from_store(st) for st in stores]
     dcs = [G.DeviceCase(x, y0, st.r_max) for y0, st in zip(y0s, stores)]
-    segs = _segs(idx, len(rank), tile_rows)
+    segs = _segs(idx, len(rank), tile_rows, hint)
     base = _compare_sgmv(label, dcs[0].x, segs, len(idx), ws, dcs, work)
     for p, (st, dc) in enumerate(zip(stores, dcs)):
         y_ref, v_ref = oracle.bgmv(st, x, y0s[p], idx, nthreads=16)
@@ -207,13 +210,14 @@ def test_sgmv_decode_13b_mixes(work, pop):
                B.lora_pick_tile_rows(seg_ptr))
 
 
-@pytest.mark.parametrize("tile_rows", [1, 2, 4])
-def test_sgmv_ragged_mixed_ranks(work, tile_rows):
+@pytest.mark.parametrize("tile_rows,hint", [(1, None), (2, None), (4, None), (6, None), (4, 1), (3, 2)])
+def test_sgmv_ragged_mixed_ranks(work, tile_rows, hint):
     """Rows in shuffled order (row map), ranks 0..64, widths off the 512-column and
-    256-octet grids, tiles of 1, 2 and 4 rows."""
+    256-octet grids, tiles of 1, 2, 4 and 6 rows; and tiles taller than the descriptor's
+    row-height hint says (the hint plans fewer rows per pass than a tile has)."""
     idx = np.random.default_rng(17).integers(-1, 7, size=150).astype(np.int32)
-    _case_sgmv(work, f"ragged-t{tile_rows}", 11, "dense", 1288, (1064, 56, 2632), [1, 64, 0, 17, 8, 33, 64], idx,
-               tile_rows)
+    _case_sgmv(work, f"ragged-t{tile_rows}-h{hint}", 11, "dense", 1288, (1064, 56, 2632), [1, 64, 0, 17, 8, 33, 64],
+               idx, tile_rows, hint=hint)
 
 
 @pytest.mark.parametrize("layout,tile_rows", [("dense", 16), ("dense", 64), ("paged8", 4)])
