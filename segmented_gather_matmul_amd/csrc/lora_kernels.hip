@@ -570,7 +570,6 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Ar
     if (th.slot < 0 || th.nrows <= 0) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;       // operand row/col, k-group of the lane
-    const int MT = min((th.nrows + 15) >> 4, MTX);
     // this workgroup's rank slices, and this lane's A^T rank-row in each
     const MfmaSlices<NS> m = mfma_slices<NS>(a, th.slot, g0);
     const int *sp = m.sp, *sj0 = m.sj0, *srank = m.srank;
@@ -591,11 +590,16 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Ar
         const int j1 = min(sj0[0] + 16, srank[0]);
         if (sok[0] && sj0[0] < j1) cached = cache_a_pages<kMfmaShrinkThreads>(w0, th.slot, sj0[0], j1, pcache);
     }
+    // the tile's rows 16 * MTX at a time (one block for the tile heights the launch was
+    // planned for; the row height is only a hint)
+    for (int m0 = 0; m0 < th.nrows; m0 += 16 * MTX) {
+    const TileHead tb{th.slot, th.pos0 + m0, th.nrows - m0, th.valid};
+    const int MT = min((tb.nrows + 15) >> 4, MTX);
     int xrow[MTX];
 #pragma unroll
     for (int mt = 0; mt < MTX; ++mt) {
         const int rr = 16 * mt + li;
-        xrow[mt] = (mt < MT && rr < th.nrows) ? row_of<false>(a.ts, th.pos0 + rr, a.n_rows) : -1;
+        xrow[mt] = (mt < MT && rr < tb.nrows) ? row_of<false>(a.ts, tb.pos0 + rr, a.n_rows) : -1;
     }
     f4_t acc[NS][MTX];
 #pragma unroll
@@ -637,7 +641,8 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Ar
                                                                         acc[q][mt], 0, 0, 0);
             }
     }
-    mfma_shrink_store<MTX, NS>(a, th, m, MT, acc, red);
+    mfma_shrink_store<MTX, NS>(a, tb, m, MT, acc, red);
+    }
 }
 
 // The dense MFMA shrink with x and A^T staged through LDS.  Work item, operand values
@@ -689,16 +694,20 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_ke
     if (th.slot < 0 || th.nrows <= 0) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    const int MT = min((th.nrows + 15) >> 4, MTX);
     const MfmaSlices<NS> m = mfma_slices<NS>(a, th.slot, g0);
-    // staged row r: x row r of the tile (r < XR), else A^T rank-row of slice (r - XR) / 16
+    // the tile's rows XR at a time (one block for the tile heights the launch was planned
+    // for; the row height is only a hint)
+    for (int m0 = 0; m0 < th.nrows; m0 += XR) {
+    const TileHead tb{th.slot, th.pos0 + m0, th.nrows - m0, th.valid};
+    const int MT = min((tb.nrows + 15) >> 4, MTX);
+    // staged row r: x row r of the block (r < XR), else A^T rank-row of slice (r - XR) / 16
     const uint16_t *src[RPW];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
         const int r = i * W + wave;
         src[i] = nullptr;
         if (r < XR) {
-            const int row = r < th.nrows ? row_of<false>(a.ts, th.pos0 + r, a.n_rows) : -1;
+            const int row = r < tb.nrows ? row_of<false>(a.ts, tb.pos0 + r, a.n_rows) : -1;
             if (row >= 0) src[i] = a.x + (int64_t)row * a.ldx;
         } else if (r < ROWS) {
             const int q = (r - XR) >> 4, j = m.sj0[q] + ((r - XR) & 15);
@@ -738,7 +747,8 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_ke
         }
         __syncthreads();
     }
-    mfma_shrink_store<MTX, NS>(a, th, m, MT, acc, red);
+    mfma_shrink_store<MTX, NS>(a, tb, m, MT, acc, red);
+    }
 }
 
 // ------------------------------------------------------------------------ expand
