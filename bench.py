@@ -65,7 +65,7 @@ def workload_spec(name, rows=None):
         tp8 = "tp8" in name
         slora = name.endswith("slora")
         spec = dict(cfg_id=5, shapes=wl.LLAMA2_70B_TP8 if tp8 else wl.LLAMA2_70B, layers=2, num_slots=2000,
-                    rank=rank, scale=wl.scale_for_rank(rank), batch=b, form="mixed", layout="paged",
+                    rank=rank, scale=wl.scale_for_rank(rank), batch=b, form="sgmv", layout="paged",
                     page_elems=128 if tp8 else 1024, model="Llama-2-70B, one GPU of 8-way TP" if tp8 else "Llama-2-70B",
                     popularity="zipf1.2")
         if slora:

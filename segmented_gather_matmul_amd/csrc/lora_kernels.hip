@@ -916,19 +916,31 @@ __global__ __launch_bounds__(kThreads) void lora_expand_valu_kernel(Args args)
     const float sc = pd.w.scale[th.slot];
     const int c = it.slice * kCols + 8 * (threadIdx.x & 63), wave = threadIdx.x >> 6;
     const bool cin = c < pd.w.d_out;
-    // the first pass's rows, v and y first: their loads are not queued behind B's
+    if (th.nrows > NR) {
+        // A tile taller than the launch was planned for (the row height is only a hint):
+        // one row per pass, B loaded again for each.  Opaque per-pass copies of the
+        // column, wavefront and rank limit keep the address arithmetic inside the loop:
+        // hoisted out of it, it held ~60 VGPRs for the whole kernel and cost the planned
+        // single pass half its resident wavefronts.
+        for (int r = 0; r < th.nrows; ++r) {
+            int cr = c, wr = wave, jr = jlim;
+            asm volatile("" : "+v"(cr), "+v"(wr), "+v"(jr));
+            ExpandPass<PERROW, 1> p1;
+            p1.load(a, pd, th, r);
+            const uint4 y1 = p1.load_y(pd, cr, cin);
+            uint4 b1[RU];
+            load_b_octets<PAGED, RU>(pd.w, th.slot, jr, wr, 0, cr, cin, b1);
+            expand_pass<PERROW, 1, RU>(pd, p1, sc, rank, b1, y1, cr, cin, red);
+        }
+        return;
+    }
+    // the tile's rows, v and y first: their loads are not queued behind B's
     ExpandPass<PERROW, NR> ps;
     ps.load(a, pd, th, 0);
-    uint4 yv = ps.load_y(pd, c, cin);
+    const uint4 yv = ps.load_y(pd, c, cin);
     uint4 bv[RU];
     load_b_octets<PAGED, RU>(pd.w, th.slot, jlim, wave, 0, c, cin, bv);
-    for (int rg = 0; rg < th.nrows; rg += NR) {
-        if (rg > 0) {
-            ps.load(a, pd, th, rg);
-            yv = ps.load_y(pd, c, cin);
-        }
-        expand_pass<PERROW, NR, RU>(pd, ps, sc, rank, bv, yv, c, cin, red);
-    }
+    expand_pass<PERROW, NR, RU>(pd, ps, sc, rank, bv, yv, c, cin, red);
 }
 
 // ------------------------------------------------------------------------ one launch, v handed off
@@ -1759,9 +1771,7 @@ int expand_impl(void *stream, int32_t n_rows, TileSrc ts, int32_t n_tiles, int32
     } else if constexpr (PERROW) {
         expand_valu_launch<true, 1>(paged, r_max, grid, s, a);
     } else {
-        // Paged B at r_max > 32: 16 page-addressed loads per wavefront in flight already
-        // need ~140 registers, and a second row per pass halves the resident wavefronts.
-        const int nr = paged && r_max > 32 && t_plan_nr == 0 ? 1 : rows_per_pass(max_rows);
+        const int nr = rows_per_pass(max_rows);
         if (nr == 1) expand_valu_launch<false, 1>(paged, r_max, grid, s, a);
         else if (nr == 2) expand_valu_launch<false, 2>(paged, r_max, grid, s, a);
         else expand_valu_launch<false, 4>(paged, r_max, grid, s, a);

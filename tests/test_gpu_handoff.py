@@ -221,11 +221,12 @@ def test_sgmv_ragged_mixed_ranks(work, tile_rows, hint):
 
 
 @pytest.mark.parametrize("layout,tile_rows,hint", [("dense", 16, None), ("dense", 64, None), ("paged8", 4, None),
-                                                   ("dense", 64, 16), ("dense", 32, 8), ("paged8", 32, 8)])
+                                                   ("dense", 64, 16), ("dense", 32, 8), ("paged8", 32, 8),
+                                                   ("paged8", 6, None), ("paged8", 3, 1), ("paged8", 4, 2)])
 def test_sgmv_two_launch_cases(work, layout, tile_rows, hint):
     """Taller tiles (MFMA kernels) and paged weights: the call makes the two launches;
     also with a row-height hint below the tiles' height (the MFMA shrinks then take the
-    tile's rows in several blocks)."""
+    tile's rows in several blocks, the VALU expand one row per pass)."""
     idx = np.random.default_rng(19).integers(-1, 5, size=96).astype(np.int32)
     _case_sgmv(work, f"{layout}-t{tile_rows}-h{hint}", 12, layout, 2048, (2048, 1024), [16, 8, 64, 0, 32], idx,
                tile_rows, hint=hint)
