@@ -901,8 +901,15 @@ __device__ inline void expand_pass(const ProjDev &pd, const ExpandPass<PERROW, N
     __syncthreads();
 }
 
+// Wavefronts per SIMD the VALU expand is built for: 4 (at most 128 VGPRs) where that
+// needs no spills.  The 2-row paged kernel at r_max 64 otherwise takes 133 VGPRs and
+// keeps only 3; the 4-row paged kernel at r_max 64 would spill, so it is left alone.
+template <bool PAGED, int NR, int RU>
+constexpr int expand_valu_waves() { return PAGED && NR == 4 && RU == 16 ? 1 : 4; }
+
 template <bool PAGED, bool PERROW, int NR, int RU>
-__global__ __launch_bounds__(kThreads) void lora_expand_valu_kernel(Args args)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(expand_valu_waves<PAGED, NR, RU>())))
+void lora_expand_valu_kernel(Args args)
 {
     const Args &a = kernel_args<!PAGED>(args);
     __shared__ float red[kWaves * NR * 8 * 64];
