@@ -348,7 +348,12 @@ struct ShrinkHalf {
     uint4 x[NR], a[RJ];
 };
 
-template <bool PAGED, int NR, int RJ>
+// CACHED (paged weights only): the page ids come from the workgroup's LDS page cache,
+// else from the page table.  Paged rank-rows first resolve all their page ids, then issue
+// every data load unconditionally (page 0, which always exists, stands in for a rank-row
+// that needs none) and mask the results: loads under per-lane branches were issued one
+// page-id round trip apart.
+template <bool PAGED, bool CACHED, int NR, int RJ>
 __device__ inline ShrinkHalf<NR, RJ> load_half(const ShrinkSrc &s, const int (&rows)[NR], int o)
 {
     ShrinkHalf<NR, RJ> h;
@@ -356,22 +361,63 @@ __device__ inline ShrinkHalf<NR, RJ> load_half(const ShrinkSrc &s, const int (&r
     const bool in = o < s.n_oct;
 #pragma unroll
     for (int q = 0; q < NR; ++q) h.x[q] = (in && rows[q] >= 0) ? load16(s.x + (int64_t)rows[q] * s.ldx + 8 * o) : z4;
+    if constexpr (!PAGED) {
 #pragma unroll
-    for (int jj = 0; jj < RJ; ++jj) {
-        const int j = s.jb + jj;
-        h.a[jj] = z4;
-        if (!in || j >= s.jload) continue;
-        if (!PAGED) {
-            h.a[jj] = load16(dense_row<false>(s.w, s.slot, j) + 8 * o);
-        } else {
-            const uint16_t *p = a_paged(s.w, s.pcache, s.cached, s.ptb, s.j0, j, 8 * o);
-            if (p) h.a[jj] = load16(p);
+        for (int jj = 0; jj < RJ; ++jj) {
+            const int j = s.jb + jj;
+            h.a[jj] = (in && j < s.jload) ? load16(dense_row<false>(s.w, s.slot, j) + 8 * o) : z4;
         }
+    } else {
+        const int P = s.w.page_elems, k = 8 * o, q = k / P, within = k - q * P, npg = s.w.d_in / P;
+        int pg[RJ];
+#pragma unroll
+        for (int jj = 0; jj < RJ; ++jj) {
+            const int j = s.jb + jj;
+            const bool need = in && j < s.jload;
+            if constexpr (CACHED) {
+                // entry 0 exists whenever the cache was filled; read unconditionally, then masked
+                const int e = s.pcache[need ? (j - s.j0) * npg + q : 0];
+                pg[jj] = need ? e : -1;
+            } else {
+                pg[jj] = need ? page_id<false>(s.w, s.ptb, j, q) : -1;
+            }
+        }
+        uint4 t[RJ];
+#pragma unroll
+        for (int jj = 0; jj < RJ; ++jj) t[jj] = load16(page_ptr(s.w, max(pg[jj], 0), within));
+#pragma unroll
+        for (int jj = 0; jj < RJ; ++jj) h.a[jj] = pg[jj] >= 0 ? t[jj] : z4;
     }
     return h;
 }
 
 __device__ inline uint32_t *handoff_row(const HandoffDev &ho, int row, int p);
+
+// The VALU shrink's sums over halves [0, h_end) of octet pairs for NR rows and RJ
+// rank-rows: D halves (whole pairs) are requested together, then summed in order.
+template <bool PAGED, bool CACHED, int NR, int RJ, int D>
+__device__ inline void shrink_halves(const ShrinkSrc &src, const int (&rows)[NR], int n_half, int h_end,
+                                     float (&acc)[NR][RJ])
+{
+    const int tid = threadIdx.x;
+    for (int h0 = 0; h0 < h_end; h0 += D) {
+        ShrinkHalf<NR, RJ> hf[D];
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (d == 0 || h0 + d < n_half) hf[d] = load_half<PAGED, CACHED, NR, RJ>(src, rows, tid + kThreads * (h0 + d));
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            // a pair runs when its first octet exists; its second term may be zero
+            const int h = h0 + d;
+            if (h < n_half && tid + kThreads * (h & ~1) < src.n_oct) {
+#pragma unroll
+                for (int q = 0; q < NR; ++q)
+#pragma unroll
+                    for (int jj = 0; jj < RJ; ++jj) acc[q][jj] = dot8(hf[d].x[q], hf[d].a[jj], acc[q][jj]);
+            }
+        }
+    }
+}
 
 // Where a VALU shrink puts v: the v buffer; a workgroup's own LDS row (indexed by
 // rank-row, per-row form); or the v buffer and the launch's hand-off row.
@@ -423,24 +469,12 @@ __device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *re
 #pragma unroll
                 for (int jj = 0; jj < RJ; ++jj) acc[q][jj] = 0.f;
             const ShrinkSrc src{pd.w, a.x, a.ldx, th.slot, jb, jload, j0, n_oct, ptb, pcache, cached};
-            // D halves (whole pairs) are requested together, then summed in order
-            for (int h0 = 0; h0 < n_half; h0 += D) {
-                ShrinkHalf<NR, RJ> hf[D];
-#pragma unroll
-                for (int d = 0; d < D; ++d)
-                    if (d == 0 || h0 + d < n_half) hf[d] = load_half<PAGED, NR, RJ>(src, rows, tid + kThreads * (h0 + d));
-#pragma unroll
-                for (int d = 0; d < D; ++d) {
-                    // a pair runs when its first octet exists; its second term may be zero
-                    const int h = h0 + d;
-                    if (h < n_half && tid + kThreads * (h & ~1) < n_oct) {
-#pragma unroll
-                        for (int q = 0; q < NR; ++q)
-#pragma unroll
-                            for (int jj = 0; jj < RJ; ++jj) acc[q][jj] = dot8(hf[d].x[q], hf[d].a[jj], acc[q][jj]);
-                    }
-                }
-            }
+            // D halves (whole pairs) are requested together, then summed in order.  Paged
+            // weights: rank-rows at or past the slot's rank (known here) need neither x nor
+            // A; their sums stay zero, as the loop would leave them.
+            const int h_end = (!PAGED || jb < jload) ? n_half : 0;
+            if (!PAGED || cached) shrink_halves<PAGED, true, NR, RJ, D>(src, rows, n_half, h_end, acc);
+            else shrink_halves<PAGED, false, NR, RJ, D>(src, rows, n_half, h_end, acc);
 #pragma unroll
             for (int q = 0; q < NR; ++q)
 #pragma unroll
