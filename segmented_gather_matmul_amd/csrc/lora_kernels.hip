@@ -547,7 +547,7 @@ __device__ inline MfmaSlices<NS> mfma_slices(const Args &a, int slot, int g0)
 
 // The MFMA shrinks' last step: every wavefront's 16x16 accumulators go to LDS and are
 // added in wavefront order, one rank slice at a time; columns at or past the rank are
-// written as 0.  red holds W * 1024 floats.
+// written as 0.  red holds W * MTX * 256 floats.
 template <int MTX, int NS>
 __device__ inline void mfma_shrink_store(const Args &a, const TileHead &th, const MfmaSlices<NS> &m, int MT,
                                          const f4_t (&acc)[NS][MTX], float *red)
@@ -560,7 +560,7 @@ __device__ inline void mfma_shrink_store(const Args &a, const TileHead &th, cons
 #pragma unroll
         for (int mt = 0; mt < MTX; ++mt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) red[wave * 1024 + mt * 256 + (4 * lg + e) * 16 + li] = acc[q][mt][e];
+            for (int e = 0; e < 4; ++e) red[wave * (MTX * 256) + mt * 256 + (4 * lg + e) * 16 + li] = acc[q][mt][e];
         __syncthreads();
         if (m.sok[q] && m.srank[q] > 0) {
             const ProjDev &pd = a.p[m.sp[q]];
@@ -572,7 +572,7 @@ __device__ inline void mfma_shrink_store(const Args &a, const TileHead &th, cons
                 if (row < 0) continue;
                 float s = 0.f;
 #pragma unroll
-                for (int w = 0; w < W; ++w) s += red[w * 1024 + o];
+                for (int w = 0; w < W; ++w) s += red[w * (MTX * 256) + o];
                 pd.v[(int64_t)row * pd.ldv + col] = col < m.srank[q] ? s : 0.f;
             }
         }
@@ -695,9 +695,10 @@ __host__ __device__ constexpr int stage_rows(int mtx, int ns) { return 16 * (mtx
 
 __host__ __device__ constexpr size_t stage_lds_bytes(int mtx, int ns)
 {
-    return (size_t)stage_rows(mtx, ns) * kStageStride * 2 > (size_t)(kMfmaShrinkThreads / 64) * 1024 * 4
+    // the staged chunk, or the wavefronts' accumulators once the k loop is done
+    return (size_t)stage_rows(mtx, ns) * kStageStride * 2 > (size_t)(kMfmaShrinkThreads / 64) * mtx * 256 * 4
                ? (size_t)stage_rows(mtx, ns) * kStageStride * 2
-               : (size_t)(kMfmaShrinkThreads / 64) * 1024 * 4;
+               : (size_t)(kMfmaShrinkThreads / 64) * mtx * 256 * 4;
 }
 
 // Octet k .. k+7 of every staged row this wavefront loads; zero past d_in or for rows
@@ -710,7 +711,7 @@ __device__ inline void stage_load(const uint16_t *const (&src)[RPW], int k, int 
     for (int i = 0; i < RPW; ++i) st[i] = (src[i] && k < d_in) ? load16(src[i] + k) : z4;
 }
 
-template <int MTX, int NS>
+template <int MTX, int NS, int RB>
 __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_kernel(Args args)
 {
     const Args &a = kernel_args<true>(args);
@@ -721,17 +722,20 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_ke
     uint16_t *stg = reinterpret_cast<uint16_t *>(smem);  // [ROWS][kStageStride]
     float *red = reinterpret_cast<float *>(smem);        // reused after the k loop
     const int wi = work_item(blockIdx.x, a.grid);
+    // work item: (tile, row block b of RB, group of NS rank slices)
     const int groups = (a.per_tile + NS - 1) / NS;
-    const int tile = wi / groups, g0 = (wi - tile * groups) * NS;
+    const int tile = wi / (groups * RB), rem = wi - tile * (groups * RB);
+    const int b = RB == 1 ? 0 : rem / groups, g0 = (rem - b * groups) * NS;
     if (tile >= a.n_tiles) return;
     const TileHead th = tile_head<false>(a.ts, a.p[0].w, tile);
     if (th.slot < 0 || th.nrows <= 0) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const MfmaSlices<NS> m = mfma_slices<NS>(a, th.slot, g0);
-    // the tile's rows XR at a time (one block for the tile heights the launch was planned
-    // for; the row height is only a hint)
-    for (int m0 = 0; m0 < th.nrows; m0 += XR) {
+    // The tile's rows XR at a time: block b of every RB (one block per workgroup for the
+    // tile heights the launch was planned for; the row height is only a hint).  RB > 1
+    // spreads one tile's rows over RB workgroups, each reading the slices' A^T itself.
+    for (int m0 = b * XR; m0 < th.nrows; m0 += RB * XR) {
     const TileHead tb{th.slot, th.pos0 + m0, th.nrows - m0, th.valid};
     const int MT = min((tb.nrows + 15) >> 4, MTX);
     // staged row r: x row r of the block (r < XR), else A^T rank-row of slice (r - XR) / 16
@@ -1742,10 +1746,14 @@ int shrink_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSr
         const int ns_max = mtx > 2 ? 3 : 4;
         const int ns = paged ? 1 : (a.per_tile + (a.per_tile + ns_max - 1) / ns_max - 1) /
                                        ((a.per_tile + ns_max - 1) / ns_max);
-        a.grid = pad8((int64_t)n_tiles * ((a.per_tile + ns - 1) / ns));
+        // A single rank slice per tile (one projection of rank <= 16) with 64-row tiles:
+        // the tile's rows go to four workgroups of 16 rows each, as many as the CUs hold at
+        // once (the tiles alone leave CUs idle); each reads the slice's A^T again (from L2).
+        const int rb = !paged && mtx > 2 && ns == 1 && a.per_tile == 1 ? 4 : 1;
+        a.grid = pad8((int64_t)n_tiles * rb * ((a.per_tile + ns - 1) / ns));
         const dim3 g((unsigned)a.grid);
 #define LORA_SHRINK_STAGED(MTX, NS) \
-    launch(lora_shrink_mfma_staged_kernel<MTX, NS>, g, kMfmaShrinkThreads, stage_lds_bytes(MTX, NS), s, a)
+    launch(lora_shrink_mfma_staged_kernel<MTX, NS, 1>, g, kMfmaShrinkThreads, stage_lds_bytes(MTX, NS), s, a)
         if (paged) {
             if (mtx <= 1) launch(lora_shrink_mfma_kernel<true, 1, 1>, g, kMfmaShrinkThreads, 0, s, a);
             else if (mtx == 2) launch(lora_shrink_mfma_kernel<true, 2, 1>, g, kMfmaShrinkThreads, 0, s, a);
@@ -1760,6 +1768,8 @@ int shrink_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSr
             else if (ns == 2) LORA_SHRINK_STAGED(2, 2);
             else if (ns == 3) LORA_SHRINK_STAGED(2, 3);
             else LORA_SHRINK_STAGED(2, 4);
+        } else if (rb == 4) {
+            launch(lora_shrink_mfma_staged_kernel<1, 1, 4>, g, kMfmaShrinkThreads, stage_lds_bytes(1, 1), s, a);
         } else {
             if (ns == 1) LORA_SHRINK_STAGED(4, 1);
             else if (ns == 2) LORA_SHRINK_STAGED(4, 2);

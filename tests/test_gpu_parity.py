@@ -244,6 +244,30 @@ def test_dense_and_paged_are_bitwise_identical():
     assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
 
 
+def test_mfma_shrink_row_blocks_match_paged_bitwise():
+    """64-row tiles of one projection of rank <= 16: the dense MFMA shrink spreads each
+    tile over four 16-row workgroups, the paged one keeps a tile in one; every element is
+    summed in the same order, so y and v must agree bit for bit (and with the oracle)."""
+    lens = [64, 130, 17, 200, 3, 64]
+    seg_ptr = wl.segments_from_lengths(lens)
+    seg_slot = np.array([0, 1, 2, 3, 4, 1], dtype=np.int32)
+    idx = np.repeat(seg_slot, lens).astype(np.int32)
+    rank = np.array([16, 8, 16, 1, 12], dtype=np.int32)
+    scale = wl.scale_for_rank(rank)
+    dense = wl.dense_store(19, 0, 5, 2048, 1536, rank, scale, r_max=16)
+    paged = wl.paged_store(19, 0, 5, 2048, 1536, rank, scale, 512, spare_pages=5)
+    x, y0 = wl.activations(19, 0, len(idx), 2048, 1536)
+    y_ref, v_ref = _oracle(dense, x, y0, idx)
+    outs = []
+    for store in (dense, paged):
+        dc = G.DeviceCase(x, y0, 16)
+        outs.append(G.run_sgmv(B.weights_from_store(store), dc, seg_ptr=seg_ptr, seg_slot=seg_slot,
+                               max_tile_rows=64))
+        G.check(dc, *outs[-1], y_ref, v_ref, G.active_rows(idx, rank), "row-blocks")
+    assert np.array_equal(outs[0][0].view(np.uint16), outs[1][0].view(np.uint16))
+    assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+
+
 def test_run_to_run_determinism():
     b = wl.batch_decode_mix("skewed")
     x, y0, store = G.dense_case(3, 5, b.n, 5120, 13824, 16, 64, 0.5, b.idx)
