@@ -737,8 +737,8 @@ def main():
                          "the per-row expand (mixed); default: the workload's own")
     ap.add_argument("--handoff", choices=["auto", "on", "off"], default="auto",
                     help="per-row and segment forms: one launch per unit with v handed from the shrink's "
-                         "workgroups to the expand's (auto: with dense weights, where it measures faster than two "
-                         "launches)")
+                         "workgroups to the expand's (auto: the per-row form with dense weights, where it measures "
+                         "faster than two launches)")
     ap.add_argument("--fused-chunks", type=int, default=-1,
                     help="per-row form: -1 = separate shrink and expand launches (the library's choice); c >= 1 = "
                          "one launch per unit, each workgroup covering c 512-column chunks")
@@ -816,8 +816,10 @@ def main():
         raise SystemExit("--handoff on needs the per-row or segment form (--form bgmv or sgmv)")
     if args.handoff == "on" and args.fused_chunks >= 1:
         raise SystemExit("--handoff on and --fused-chunks >= 1 are two different one-launch forms")
-    # the library's hand-off form where it measures faster: dense weights
-    handoff = args.handoff == "on" or (args.handoff == "auto" and decode_form and spec["layout"] == "dense"
+    # the library's hand-off form where it measures faster: the per-row form with dense
+    # weights (the segment form's two launches are as fast or faster since its expand runs
+    # the planned tile in one pass)
+    handoff = args.handoff == "on" or (args.handoff == "auto" and spec["form"] == "bgmv" and spec["layout"] == "dense"
                                        and args.fused_chunks < 1)
     if handoff:
         work = B.handoff_workspace(spec["batch"].n, device)
