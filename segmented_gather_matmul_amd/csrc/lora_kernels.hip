@@ -7,10 +7,12 @@
 // 64 consecutive rows of one segment, or one row in the per-row-slot form) instead of
 // binding the adapter to a grid dimension, so segments of 1 to thousands of rows share
 // one launch.  One launch may also serve up to LORA_MAX_PROJ projections that share
-// the batch (q/k/v, gate/up): each work item is (tile, projection, slice) and the items
-// of one tile are consecutive.  A workgroup is 4 wavefronts (256 lanes); workgroup ids
-// are remapped so that each of the 8 XCDs (which take workgroups round-robin) owns a
-// contiguous range of items, so the x row and v row of a tile stay in one L2.
+// the batch (q/k/v, gate/up): each work item is (tile, projection, slice), and the items
+// of one tile are consecutive (tile-major), except in the VALU expand, whose items are
+// slice-major so that the tiles of one adapter reuse each chunk of its B.  A workgroup
+// is 4 wavefronts (256 lanes); workgroup ids are remapped so that each of the 8 XCDs
+// (which take workgroups round-robin) owns a contiguous range of items, so the x row and
+// v row of a tile stay in one L2.
 //
 // Shrink.  The output is only r wide, so parallelism comes from splitting rank-rows
 // over workgroups and d_in over the wavefronts of a workgroup; the partial sums are
