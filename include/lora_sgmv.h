@@ -161,9 +161,8 @@ int32_t lora_tiles_bound(int32_t n_pos, int32_t n_seg, int32_t max_tile_rows);
 
 /*
  * Tile height suited to a batch: 64 (four MFMA slices, fewest re-reads of each
- * adapter) when some segment has at least 128 rows; else 2 when the non-empty
- * segments average fewer than 4 rows (mostly single adapters per row, as in a large
- * mixed pool), else 4 (the VALU kernels spread short segments widest).
+ * adapter) when some segment has at least 128 rows, else 2 (short VALU tiles keep the
+ * most wavefronts resident).
  * seg_ptr: host [n_seg + 1].  Any value in 1..LORA_MAX_TILE_ROWS gives the same
  * results within the stated tolerance; this only picks the faster launch shape.
  */

@@ -121,20 +121,15 @@ int32_t lora_tiles_bound(int32_t n_pos, int32_t n_seg, int32_t max_tile_rows)
 
 int32_t lora_pick_tile_rows(const int32_t *seg_ptr, int32_t n_seg)
 {
-    int32_t longest = 0, nonempty = 0;
-    int64_t rows = 0;
-    for (int32_t g = 0; seg_ptr && g < n_seg; ++g) {
-        const int32_t len = seg_ptr[g + 1] - seg_ptr[g];
-        longest = std::max(longest, len);
-        if (len > 0) ++nonempty, rows += len;
-    }
+    int32_t longest = 0;
+    for (int32_t g = 0; seg_ptr && g < n_seg; ++g) longest = std::max(longest, seg_ptr[g + 1] - seg_ptr[g]);
     // Long segments (prefill) feed the MFMA kernels 64-row tiles, which re-read each
-    // adapter's A and B least; short ones (decode groups) run on the VALU kernels.
-    // Measured on MI355X: 4-row tiles for groups of ~4 or more rows; 2-row tiles when
-    // most adapters serve one to three rows (a 256-row batch over a 2000-adapter pool:
-    // 500 vs 555 us per 70B layer), since shorter passes keep more wavefronts resident.
-    if (longest >= kLongSegment) return LORA_MAX_TILE_ROWS;
-    return nonempty > 0 && rows < 4 * (int64_t)nonempty ? 2 : 4;
+    // adapter's A and B least; short ones (decode groups) run on the VALU kernels in
+    // 2-row tiles.  Measured on MI355X, 2-row tiles are as fast as 4-row ones or faster
+    // for every decode mix once the expand runs a tile in one pass (13B uniform 86 vs 92,
+    // skewed 77 vs 79, identical 69 vs 69 us per layer; a 256-row batch over a
+    // 2000-adapter 70B pool 426 vs 452), since shorter passes keep more wavefronts resident.
+    return longest >= kLongSegment ? LORA_MAX_TILE_ROWS : 2;
 }
 
 int lora_build_tiles(const int32_t *seg_ptr, const int32_t *seg_slot, int32_t n_seg,

@@ -363,10 +363,10 @@ def test_set_plan_ranges():
 
 
 def test_pick_tile_rows():
-    assert B.lora_pick_tile_rows(np.array([0, 1, 4, 6, 8], np.int32)) == 2      # mean 2 rows
-    assert B.lora_pick_tile_rows(np.array([0, 4, 9, 13, 16], np.int32)) == 4    # mean 4 rows
-    assert B.lora_pick_tile_rows(np.array([0, 4, 4, 8], np.int32)) == 4         # empty segment ignored
-    assert B.lora_pick_tile_rows(np.array([0, 3, 3, 6], np.int32)) == 2
-    assert B.lora_pick_tile_rows(np.array([0, 127, 140], np.int32)) == 4
-    assert B.lora_pick_tile_rows(np.array([0, 5, 133], np.int32)) == 64
-    assert B.lora_pick_tile_rows(np.array([0], np.int32)) == 4
+    assert B.lora_pick_tile_rows(np.array([0, 1, 4, 6, 8], np.int32)) == 2      # short segments
+    assert B.lora_pick_tile_rows(np.array([0, 4, 9, 13, 16], np.int32)) == 2
+    assert B.lora_pick_tile_rows(np.array([0, 4, 4, 8], np.int32)) == 2         # empty segment
+    assert B.lora_pick_tile_rows(np.array([0, 127, 140], np.int32)) == 2        # longest 127 rows
+    assert B.lora_pick_tile_rows(np.array([0, 5, 133], np.int32)) == 64         # one of 128 or more
+    assert B.lora_pick_tile_rows(np.array([0, 128], np.int32)) == 64
+    assert B.lora_pick_tile_rows(np.array([0], np.int32)) == 2                  # no segments
