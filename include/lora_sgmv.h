@@ -111,17 +111,57 @@ typedef struct lora_tile {
 } lora_tile;
 
 /*
- * Segment form of a batch, as consumed by the SGMV kernels: a flat work-list of
- * tiles (built once per batch by lora_build_tiles) and the position -> row map.
+ * Segment form of a batch (Punica summary, "The SGMV Operator": offsets
+ * s_0 <= s_1 <= ... <= s_n, segment g = positions s_g .. s_{g+1}-1 sharing adapter
+ * slot seg_slot[g]; Punica digest, section 5.4: the SGMV call takes these offsets and
+ * the adapter index of each segment directly).
+ *
+ * Offsets form (tiles == NULL): the launch cuts every segment into
+ * ceil(len / tile_rows) tiles of near-equal height itself, on the device -- each
+ * workgroup finds its tile by a prefix sum over seg_ptr -- so nothing is built or
+ * copied on the host and a captured graph can be replayed for a new batch written into
+ * the same device arrays.  The cut equals lora_build_tiles' (same results, bit for
+ * bit).  The grid covers n_rows / tile_rows + n_seg tiles, which bounds every valid
+ * batch: segments may be empty, so a descriptor with a fixed capacity n_seg describes
+ * every batch of at most n_seg segments.
+ *   n_seg     number of segments (>= 0)
+ *   seg_ptr   device int32 [n_seg + 1]: 0 <= seg_ptr[0] <= seg_ptr[1] <= ...; with
+ *             row_map NULL the positions are rows, so seg_ptr[n_seg] <= n_rows; with a
+ *             row map, row_map holds seg_ptr[n_seg] entries (distinct rows)
+ *   seg_slot  device int32 [n_seg]: -1 = no adapter
+ *   row_map   device int32 [seg_ptr[n_seg]] or NULL (position p is row p)
+ *   tile_rows 1..LORA_MAX_TILE_ROWS, or 0 for the library's choice from n_rows and
+ *             n_seg (64 when the segments average at least 128 rows, else 2)
+ * The device arrays are read without a host check: an offset outside the positions
+ * is clamped and an out-of-range slot or row makes its rows no-ops.
+ *
+ * Tile-list form (tiles != NULL), the precomputed fast path: the n_tiles tiles of
+ * lora_build_tiles over the same segments (built once per batch on the host and
+ * reused by every projection of every layer); seg_ptr, seg_slot and tile_rows are then
+ * not read.  row_map as above, with n_pos = its length; max_rows = the largest nrows
+ * of any tile (0 = unknown, taken as LORA_MAX_TILE_ROWS), a launch-shape hint only.
  */
 typedef struct lora_segments {
-    int32_t n_tiles;
-    const lora_tile *tiles;  /* device [n_tiles] */
-    const int32_t *row_map;  /* device [n_pos] or NULL (position p is row p) */
-    int32_t n_pos;           /* number of positions (length of row_map) */
-    int32_t max_rows;        /* largest nrows of any tile, 0 = unknown (taken as 64); a launch-shape
-                              * hint only: results do not depend on it */
+    int32_t n_seg;
+    const int32_t *seg_ptr;   /* device [n_seg + 1] */
+    const int32_t *seg_slot;  /* device [n_seg] */
+    const int32_t *row_map;   /* device, or NULL */
+    int32_t tile_rows;        /* offsets form: tile height, 0 = library's choice */
+    int32_t n_tiles;          /* tile-list form: number of tiles */
+    const lora_tile *tiles;   /* tile-list form: device [n_tiles], 16-byte aligned; NULL = offsets form */
+    int32_t n_pos;            /* tile-list form: number of positions (length of row_map) */
+    int32_t max_rows;         /* tile-list form: largest nrows of any tile, 0 = unknown */
 } lora_segments;
+
+/*
+ * Device workspace that the calls on a batch of n_rows rows in n_seg segments need, in
+ * bytes, written to *bytes: the one-launch forms (lora_sgmv_multi_handoff,
+ * lora_bgmv_multi_handoff) need lora_handoff_bytes(n_rows); the separate shrink and
+ * expand launches need none (every split sum is combined inside one workgroup) and
+ * take no workspace argument.  w may be NULL (the size does not depend on the
+ * weights).  LORA_E_SHAPE for n_rows < 0 or n_seg < 0, LORA_E_NULL for bytes NULL.
+ */
+int lora_sgmv_workspace_bytes(const struct lora_weights *w, int32_t n_rows, int32_t n_seg, size_t *bytes);
 
 /*
  * One adapted projection of a launch that serves several projections of the same
@@ -188,9 +228,12 @@ int lora_build_tiles(const int32_t *seg_ptr, const int32_t *seg_slot, int32_t n_
  */
 int lora_validate_weights_host(const lora_weights *w);
 
-/* Host check of a host copy of a segment descriptor against n_rows and num_slots:
- * tiles inside [0, n_pos), 1..LORA_MAX_TILE_ROWS rows, slots in [-1, num_slots),
- * row_map entries in [0, n_rows) and no row used twice. */
+/* Host check of a host copy of a segment descriptor (all its arrays in host memory)
+ * against n_rows and num_slots.  Tile-list form: tiles inside [0, n_pos),
+ * 1..LORA_MAX_TILE_ROWS rows, slots in [-1, num_slots), no position in two tiles.
+ * Offsets form: seg_ptr non-decreasing from seg_ptr[0] >= 0, seg_ptr[n_seg] <= n_rows,
+ * seg_slot in [-1, num_slots), tile_rows in 0..LORA_MAX_TILE_ROWS.  Both forms: row_map
+ * entries in [0, n_rows) and no row used twice. */
 int lora_validate_segments_host(const lora_segments *seg, int32_t n_rows, int32_t num_slots);
 
 /* ---------------------------------------------------------------- SGMV (segments) */
@@ -406,7 +449,7 @@ int lora_set_handoff_polls(int32_t polls);
 
 const char *lora_last_error(void);   /* message of this thread's last failed call */
 const char *lora_status_str(int status);
-int lora_abi_version(void);          /* 1 */
+int lora_abi_version(void);          /* 2 */
 
 #ifdef __cplusplus
 }

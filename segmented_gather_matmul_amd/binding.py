@@ -34,7 +34,8 @@ EXPORTS = ["lora_build_segments", "lora_tiles_bound", "lora_build_tiles", "lora_
            "lora_bgmv_shrink_multi", "lora_bgmv_expand_multi", "lora_pick_tile_rows", "lora_bgmv_multi",
            "lora_set_plan", "lora_pool_state_bytes", "lora_pool_init", "lora_pool_alloc", "lora_pool_release",
            "lora_pool_free_count", "lora_pool_pages_for", "lora_pool_load_header_bytes", "lora_pool_load",
-           "lora_handoff_bytes", "lora_bgmv_multi_handoff", "lora_sgmv_multi_handoff", "lora_set_handoff_polls"]
+           "lora_handoff_bytes", "lora_bgmv_multi_handoff", "lora_sgmv_multi_handoff", "lora_set_handoff_polls",
+           "lora_sgmv_workspace_bytes"]
 MAX_PROJ = 4
 
 
@@ -65,8 +66,9 @@ class CLoadJob(ctypes.Structure):
 
 
 class CSegments(ctypes.Structure):
-    _fields_ = [("n_tiles", ctypes.c_int32), ("tiles", ctypes.c_void_p), ("row_map", ctypes.c_void_p),
-                ("n_pos", ctypes.c_int32), ("max_rows", ctypes.c_int32)]
+    _fields_ = [("n_seg", ctypes.c_int32), ("seg_ptr", ctypes.c_void_p), ("seg_slot", ctypes.c_void_p),
+                ("row_map", ctypes.c_void_p), ("tile_rows", ctypes.c_int32), ("n_tiles", ctypes.c_int32),
+                ("tiles", ctypes.c_void_p), ("n_pos", ctypes.c_int32), ("max_rows", ctypes.c_int32)]
 
 
 _lib = None
@@ -110,6 +112,7 @@ def lib() -> ctypes.CDLL:
             "lora_pool_alloc": [P, I32, P],
             "lora_pool_release": [P, I32, P],
             "lora_pool_load": [P, I32, P, P, ctypes.c_size_t, P, ctypes.c_size_t],
+            "lora_sgmv_workspace_bytes": [P, I32, I32, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -158,12 +161,84 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
+# ------------------------------------------------------------------ argument checks
+# The C ABI receives raw pointers and leading dimensions and cannot tell a host pointer
+# or a too-short tensor from a valid one, so every tensor is checked here before any
+# call: dtype, unit stride along the last dimension, enough rows and columns for what
+# the kernels touch, and residence on the current GPU.  Violations raise ValueError.
+def _torch_dtype(name):
+    import torch
+    return {"f16": torch.float16, "f32": torch.float32, "i32": torch.int32, "i64": torch.int64,
+            "u8": torch.uint8}[name]
+
+
+def _on_gpu(t, what):
+    import torch
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor (got device {t.device})")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{what} is on {t.device}, the current device is cuda:{torch.cuda.current_device()}")
+
+
+def check_matrix(t, what, dtype, rows, cols, gpu=True):
+    """t: 2-D tensor of `dtype` with unit column stride, >= rows rows and >= cols columns."""
+    if t is None:
+        raise ValueError(f"{what} is required")
+    if not hasattr(t, "dtype") or t.dtype != _torch_dtype(dtype):
+        raise ValueError(f"{what} must have dtype {dtype} (got {getattr(t, 'dtype', type(t).__name__)})")
+    if t.dim() != 2:
+        raise ValueError(f"{what} must be 2-D (got {t.dim()}-D)")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{what} needs unit stride along its columns (stride {t.stride(1)})")
+    if t.shape[0] < rows or t.shape[1] < cols:
+        raise ValueError(f"{what} is {tuple(t.shape)}, needs at least ({rows}, {cols})")
+    if t.shape[0] > 1 and t.stride(0) < cols:
+        raise ValueError(f"{what} has row stride {t.stride(0)} < {cols} columns")
+    if gpu:
+        _on_gpu(t, what)
+
+
+def check_vector(t, what, dtype, n, gpu=True):
+    """t: contiguous tensor of `dtype` with at least n elements."""
+    if t is None:
+        raise ValueError(f"{what} is required")
+    if not hasattr(t, "dtype") or t.dtype != _torch_dtype(dtype):
+        raise ValueError(f"{what} must have dtype {dtype} (got {getattr(t, 'dtype', type(t).__name__)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.numel() < n:
+        raise ValueError(f"{what} has {t.numel()} elements, needs at least {n}")
+    if gpu:
+        _on_gpu(t, what)
+
+
+def _rows_arg(n_rows):
+    n_rows = int(n_rows)
+    if n_rows < 0:
+        raise ValueError(f"n_rows = {n_rows}")
+    return n_rows
+
+
 # ------------------------------------------------------------------ descriptors
 class Weights:
     """lora_weights over device tensors (kept alive by this object)."""
 
     def __init__(self, *, num_slots, d_in, d_out, r_max, rank, scale, a_t=None, b=None, pool=None,
                  page_elems=0, page_table=None, a_pt_off=None, b_pt_off=None):
+        # dtypes and sizes here; residence on the current GPU at every launch (on_gpu)
+        S = int(num_slots)
+        check_vector(rank, "rank", "i32", S, gpu=False)
+        check_vector(scale, "scale", "f32", S, gpu=False)
+        if pool is None:
+            for t, what, d in ((a_t, "a_t", d_in), (b, "b", d_out)):
+                check_vector(t, what, "f16", S * int(r_max) * int(d), gpu=False)
+        else:
+            if pool.dim() != 2 or int(pool.shape[1]) != int(page_elems):
+                raise ValueError(f"pool must be [num_pages, page_elems = {page_elems}] (got {tuple(pool.shape)})")
+            check_vector(pool, "pool", "f16", 1, gpu=False)
+            check_vector(page_table, "page_table", "i32", 1, gpu=False)
+            check_vector(a_pt_off, "a_pt_off", "i64", S, gpu=False)
+            check_vector(b_pt_off, "b_pt_off", "i64", S, gpu=False)
         self.tensors = [rank, scale, a_t, b, pool, page_table, a_pt_off, b_pt_off]
         c = CWeights()
         c.layout = LAYOUT_PAGED if pool is not None else LAYOUT_DENSE
@@ -179,8 +254,15 @@ class Weights:
         self.c = c
         self.num_slots, self.d_in, self.d_out, self.r_max = c.num_slots, c.d_in, c.d_out, c.r_max
 
+    def on_gpu(self):
+        for t, what in zip(self.tensors, ("rank", "scale", "a_t", "b", "pool", "page_table", "a_pt_off",
+                                           "b_pt_off")):
+            if t is not None:
+                _on_gpu(t, f"weights.{what}")
+
     @property
     def ref(self):
+        self.on_gpu()
         return ctypes.byref(self.c)
 
 
@@ -201,22 +283,92 @@ def weights_from_store(store, device="cuda"):
 
 
 class Segments:
-    """lora_segments over device tensors: the tile work-list and the row map."""
+    """lora_segments over device tensors, in one of its two forms:
+
+    * tile list (the precomputed fast path): Segments(tiles, row_map, n_pos, max_rows),
+      tiles an int32 [n_tiles, 4] tensor from lora_build_tiles;
+    * offsets (the pages' form): Segments.offsets(seg_ptr, seg_slot, row_map, tile_rows),
+      the launch cuts the segments into tiles on the device."""
 
     def __init__(self, tiles, row_map, n_pos, max_rows=0):
         self.tiles, self.row_map = tiles, row_map
+        self.seg_ptr = self.seg_slot = None
         c = CSegments()
         c.n_tiles = int(tiles.shape[0]) if tiles is not None else 0
         c.tiles = _ptr(tiles) if c.n_tiles else None
+        if c.n_tiles and not c.tiles:
+            raise ValueError("tiles is empty")
         c.row_map = _ptr(row_map)
         c.n_pos = int(n_pos)
         c.max_rows = int(max_rows)
         self.c = c
         self.n_tiles = c.n_tiles
+        self.n_pos = c.n_pos
+
+    @classmethod
+    def offsets(cls, seg_ptr, seg_slot, row_map=None, tile_rows=0):
+        """Offsets form: seg_ptr int32 [n_seg + 1] and seg_slot int32 [n_seg] device tensors
+        (rows grouped by adapter; segments may be empty), row_map int32 device tensor or None,
+        tile_rows 0 (library's choice) or 1..64."""
+        self = cls.__new__(cls)
+        n_seg = int(seg_slot.numel())
+        check_vector(seg_ptr, "seg_ptr", "i32", n_seg + 1, gpu=False)
+        check_vector(seg_slot, "seg_slot", "i32", n_seg, gpu=False)
+        if row_map is not None:
+            check_vector(row_map, "row_map", "i32", 0, gpu=False)
+        self.tiles, self.row_map, self.seg_ptr, self.seg_slot = None, row_map, seg_ptr, seg_slot
+        c = CSegments()
+        c.n_seg, c.seg_ptr, c.seg_slot = n_seg, _ptr(seg_ptr), _ptr(seg_slot)
+        c.row_map, c.tile_rows = _ptr(row_map), int(tile_rows)
+        self.c = c
+        self.n_tiles = 0
+        self.n_pos = 0
+        return self
+
+    @property
+    def is_offsets(self):
+        return self.tiles is None and self.seg_ptr is not None
 
     @property
     def ref(self):
+        if self.is_offsets:
+            _gpu(seg_ptr=self.seg_ptr, seg_slot=self.seg_slot, row_map=self.row_map)
+        else:
+            if self.n_tiles:
+                check_matrix(self.tiles, "tiles", "i32", self.n_tiles, 4)
+            if self.row_map is not None:
+                check_vector(self.row_map, "row_map", "i32", self.n_pos)
         return ctypes.byref(self.c)
+
+
+def segments_from_offsets(seg_ptr, seg_slot, row_map=None, tile_rows=0, device="cuda", n_rows=None,
+                          num_slots=None):
+    """Device copies of host offsets (and row map) as an offsets-form Segments descriptor,
+    after lora_validate_segments_host on the host copies (n_rows and num_slots default to
+    the smallest values the arrays allow)."""
+    import torch
+    sp = np.ascontiguousarray(seg_ptr, dtype=np.int32)
+    ss = np.ascontiguousarray(seg_slot, dtype=np.int32)
+    rm = None if row_map is None else np.ascontiguousarray(row_map, dtype=np.int32)
+    host = CSegments()
+    host.n_seg, host.seg_ptr, host.seg_slot = len(ss), sp.ctypes.data, ss.ctypes.data
+    host.row_map = rm.ctypes.data if rm is not None else None
+    host.tile_rows = int(tile_rows)
+    if n_rows is None:
+        n_rows = max(int(sp[-1]), int(rm.max()) + 1 if rm is not None and len(rm) else 0)
+    if num_slots is None:
+        num_slots = max(int(ss.max()) + 1 if len(ss) else 1, 1)
+    _check(lib().lora_validate_segments_host(ctypes.byref(host), int(n_rows), int(num_slots)))
+    dev = lambda a: torch.from_numpy(a).to(device)
+    return Segments.offsets(dev(sp), dev(ss), None if rm is None else dev(rm), tile_rows)
+
+
+def lora_sgmv_workspace_bytes(n_rows, n_seg=0):
+    """Device workspace bytes the calls on a batch need (the one-launch forms' hand-off
+    buffer; the separate shrink and expand need none)."""
+    out = ctypes.c_size_t()
+    _check(lib().lora_sgmv_workspace_bytes(None, int(n_rows), int(n_seg), ctypes.byref(out)))
+    return int(out.value)
 
 
 # ------------------------------------------------------------------ host metadata
@@ -261,10 +413,28 @@ def lora_build_tiles(seg_ptr, seg_slot, max_tile_rows=None):
     return tiles[:n.value].copy()
 
 
-def segments_to_device(tiles, row_map, n_pos, device="cuda"):
-    """Device copies of a host tile list (and row map) as a Segments descriptor."""
+def segments_to_device(tiles, row_map, n_pos, device="cuda", n_rows=None, num_slots=None):
+    """Device copies of a host tile list (and row map) as a Segments descriptor.
+
+    The host copies are checked first with lora_validate_segments_host: every position
+    in at most one tile and every row at most once in the row map (the one-launch
+    hand-off form counts each row's work items and relies on this), tiles inside the
+    positions, slots inside [-1, num_slots).  n_rows and num_slots default to the
+    smallest values the arrays allow."""
     import torch
     tiles = np.ascontiguousarray(tiles, dtype=np.int32).reshape(-1, 4)
+    rm_h = None if row_map is None else np.ascontiguousarray(row_map, dtype=np.int32)
+    host = CSegments()
+    host.n_tiles = len(tiles)
+    host.tiles = tiles.ctypes.data if len(tiles) else None
+    host.row_map = rm_h.ctypes.data if rm_h is not None else None
+    host.n_pos = int(n_pos)
+    host.max_rows = int(tiles[:, 2].max()) if len(tiles) else 0
+    if n_rows is None:
+        n_rows = (int(rm_h.max()) + 1 if rm_h is not None and len(rm_h) else 0) if rm_h is not None else int(n_pos)
+    if num_slots is None:
+        num_slots = max(int(tiles[:, 0].max()) + 1 if len(tiles) else 1, 1)
+    _check(lib().lora_validate_segments_host(ctypes.byref(host), int(n_rows), int(num_slots)))
     t = torch.from_numpy(tiles).to(device)
     rm = None if row_map is None else torch.from_numpy(np.ascontiguousarray(row_map, dtype=np.int32)).to(device)
     return Segments(t, rm, n_pos, int(tiles[:, 2].max()) if len(tiles) else 0)
@@ -283,30 +453,85 @@ def _ld(t):
     return int(t.stride(0))
 
 
+# Shapes and dtypes of all arguments are checked first, residence on the GPU last
+# (_gpu), so the first message names the first argument that is wrong in kind.
+def _x(x, n_rows, d_in):
+    check_matrix(x, "x", "f16", n_rows, d_in, gpu=False)
+
+
+def _v(v, n_rows, w, what="v"):
+    check_matrix(v, what, "f32", n_rows, w.r_max, gpu=False)
+
+
+def _y(y, n_rows, w, what="y"):
+    check_matrix(y, what, "f16", n_rows, w.d_out, gpu=False)
+
+
+def _idx(idx, n_rows):
+    check_vector(idx, "idx", "i32", n_rows, gpu=False)
+
+
+def _gpu(**tensors):
+    for what, t in tensors.items():
+        if t is not None:
+            _on_gpu(t, what)
+
+
+def _segs(segments, n_rows):
+    if not isinstance(segments, Segments):
+        raise ValueError("segments must be a Segments descriptor")
+    if not segments.is_offsets and segments.row_map is None and segments.n_pos > n_rows:
+        raise ValueError(f"segments cover {segments.n_pos} positions without a row map, n_rows = {n_rows}")
+
+
 def lora_sgmv_shrink(v, x, weights: Weights, segments: Segments, n_rows=None, stream=None):
-    n_rows = x.shape[0] if n_rows is None else n_rows
-    _check(lib().lora_sgmv_shrink(_stream(stream), _ptr(v), _ld(v), _ptr(x), _ld(x), int(n_rows), weights.ref,
+    n_rows = _rows_arg(x.shape[0] if n_rows is None else n_rows)
+    _x(x, n_rows, weights.d_in)
+    _v(v, n_rows, weights)
+    _segs(segments, n_rows)
+    _gpu(v=v, x=x)
+    _check(lib().lora_sgmv_shrink(_stream(stream), _ptr(v), _ld(v), _ptr(x), _ld(x), n_rows, weights.ref,
                                   segments.ref))
 
 
 def lora_sgmv_expand(y, v, weights: Weights, segments: Segments, n_rows=None, stream=None):
-    n_rows = y.shape[0] if n_rows is None else n_rows
-    _check(lib().lora_sgmv_expand(_stream(stream), _ptr(y), _ld(y), _ptr(v), _ld(v), int(n_rows), weights.ref,
+    n_rows = _rows_arg(y.shape[0] if n_rows is None else n_rows)
+    _y(y, n_rows, weights)
+    _v(v, n_rows, weights)
+    _segs(segments, n_rows)
+    _gpu(y=y, v=v)
+    _check(lib().lora_sgmv_expand(_stream(stream), _ptr(y), _ld(y), _ptr(v), _ld(v), n_rows, weights.ref,
                                   segments.ref))
 
 
 def lora_bgmv_shrink(v, x, idx, weights: Weights, stream=None):
-    _check(lib().lora_bgmv_shrink(_stream(stream), _ptr(v), _ld(v), _ptr(x), _ld(x), _ptr(idx), int(x.shape[0]),
+    n_rows = _rows_arg(x.shape[0])
+    _x(x, n_rows, weights.d_in)
+    _v(v, n_rows, weights)
+    _idx(idx, n_rows)
+    _gpu(v=v, x=x, idx=idx)
+    _check(lib().lora_bgmv_shrink(_stream(stream), _ptr(v), _ld(v), _ptr(x), _ld(x), _ptr(idx), n_rows,
                                   weights.ref))
 
 
 def lora_bgmv_expand(y, v, idx, weights: Weights, stream=None):
-    _check(lib().lora_bgmv_expand(_stream(stream), _ptr(y), _ld(y), _ptr(v), _ld(v), _ptr(idx), int(y.shape[0]),
+    n_rows = _rows_arg(y.shape[0])
+    _y(y, n_rows, weights)
+    _v(v, n_rows, weights)
+    _idx(idx, n_rows)
+    _gpu(y=y, v=v, idx=idx)
+    _check(lib().lora_bgmv_expand(_stream(stream), _ptr(y), _ld(y), _ptr(v), _ld(v), _ptr(idx), n_rows,
                                   weights.ref))
 
 
 def lora_bgmv(y, x, idx, weights: Weights, v, stream=None):
-    _check(lib().lora_bgmv(_stream(stream), _ptr(y), _ld(y), _ptr(x), _ld(x), _ptr(idx), int(y.shape[0]),
+    n_rows = _rows_arg(y.shape[0])
+    _x(x, n_rows, weights.d_in)
+    _y(y, n_rows, weights)
+    _v(v, n_rows, weights)
+    _idx(idx, n_rows)
+    _gpu(y=y, x=x, idx=idx, v=v)
+    _check(lib().lora_bgmv(_stream(stream), _ptr(y), _ld(y), _ptr(x), _ld(x), _ptr(idx), n_rows,
                            weights.ref, _ptr(v), _ld(v)))
 
 
@@ -330,10 +555,19 @@ def lora_set_launch_events(start_event, stop_event):
 
 
 # ------------------------------------------------------------------ several projections per launch
-def proj_list(items):
-    """items: sequence of (Weights, v, y_or_None).  Returns a ctypes lora_proj array."""
+def proj_list(items, n_rows=None, expand=False):
+    """items: sequence of (Weights, v, y_or_None).  Returns a ctypes lora_proj array.  With
+    n_rows, each v (and, for an expand, each y) is checked to cover n_rows rows."""
+    if not 1 <= len(items) <= MAX_PROJ:
+        raise ValueError(f"{len(items)} projections (1..{MAX_PROJ} per launch)")
     arr = (CProj * len(items))()
     for i, (w, v, y) in enumerate(items):
+        if n_rows is not None:
+            _v(v, n_rows, w, f"v of projection {i}")
+            if expand:
+                _y(y, n_rows, w, f"y of projection {i}")
+        w.on_gpu()
+        _gpu(**{f"v of projection {i}": v, f"y of projection {i}": y if expand else None})
         arr[i].w = ctypes.addressof(w.c)
         arr[i].v, arr[i].ldv = _ptr(v), _ld(v)
         arr[i].y, arr[i].ldy = (_ptr(y), _ld(y)) if y is not None else (None, 0)
@@ -341,24 +575,36 @@ def proj_list(items):
 
 
 def lora_sgmv_shrink_multi(x, segments: Segments, items, n_rows=None, stream=None):
-    n_rows = x.shape[0] if n_rows is None else n_rows
-    arr = proj_list(items)
-    _check(lib().lora_sgmv_shrink_multi(_stream(stream), _ptr(x), _ld(x), int(n_rows), segments.ref, len(items), arr))
+    n_rows = _rows_arg(x.shape[0] if n_rows is None else n_rows)
+    _x(x, n_rows, items[0][0].d_in)
+    _segs(segments, n_rows)
+    arr = proj_list(items, n_rows)
+    _gpu(x=x)
+    _check(lib().lora_sgmv_shrink_multi(_stream(stream), _ptr(x), _ld(x), n_rows, segments.ref, len(items), arr))
 
 
 def lora_sgmv_expand_multi(segments: Segments, items, n_rows, stream=None):
-    arr = proj_list(items)
-    _check(lib().lora_sgmv_expand_multi(_stream(stream), int(n_rows), segments.ref, len(items), arr))
+    n_rows = _rows_arg(n_rows)
+    _segs(segments, n_rows)
+    arr = proj_list(items, n_rows, expand=True)
+    _check(lib().lora_sgmv_expand_multi(_stream(stream), n_rows, segments.ref, len(items), arr))
 
 
 def lora_bgmv_shrink_multi(x, idx, items, stream=None):
-    arr = proj_list(items)
-    _check(lib().lora_bgmv_shrink_multi(_stream(stream), _ptr(x), _ld(x), _ptr(idx), int(x.shape[0]), len(items), arr))
+    n_rows = _rows_arg(x.shape[0])
+    _x(x, n_rows, items[0][0].d_in)
+    _idx(idx, n_rows)
+    arr = proj_list(items, n_rows)
+    _gpu(x=x, idx=idx)
+    _check(lib().lora_bgmv_shrink_multi(_stream(stream), _ptr(x), _ld(x), _ptr(idx), n_rows, len(items), arr))
 
 
 def lora_bgmv_expand_multi(idx, items, n_rows, stream=None):
-    arr = proj_list(items)
-    _check(lib().lora_bgmv_expand_multi(_stream(stream), _ptr(idx), int(n_rows), len(items), arr))
+    n_rows = _rows_arg(n_rows)
+    _idx(idx, n_rows)
+    arr = proj_list(items, n_rows, expand=True)
+    _gpu(idx=idx)
+    _check(lib().lora_bgmv_expand_multi(_stream(stream), _ptr(idx), n_rows, len(items), arr))
 
 
 def handoff_workspace(n_rows, device="cuda"):
@@ -369,30 +615,47 @@ def handoff_workspace(n_rows, device="cuda"):
     return torch.zeros(max(nbytes, 256) // 4, dtype=torch.int32, device=device)
 
 
+def _work(work):
+    check_vector(work, "work", "i32", 1)
+    return _ptr(work), int(work.numel() * work.element_size())
+
+
 def lora_bgmv_multi_handoff(x, idx, items, work, stream=None):
     """Shrink and expand of the decode form in one launch, v handed from the shrink's
     workgroups to the expand's through `work` (handoff_workspace); the bits of the
     two-launch path."""
-    arr = proj_list(items)
-    _check(lib().lora_bgmv_multi_handoff(_stream(stream), _ptr(x), _ld(x), _ptr(idx), int(x.shape[0]), len(items),
-                                         arr, _ptr(work), int(work.numel() * work.element_size())))
+    n_rows = _rows_arg(x.shape[0])
+    _x(x, n_rows, items[0][0].d_in)
+    _idx(idx, n_rows)
+    arr = proj_list(items, n_rows, expand=True)
+    wp, wb = _work(work)
+    _gpu(x=x, idx=idx)
+    _check(lib().lora_bgmv_multi_handoff(_stream(stream), _ptr(x), _ld(x), _ptr(idx), n_rows, len(items), arr, wp,
+                                         wb))
 
 
 def lora_sgmv_multi_handoff(x, segs, items, n_rows, work, stream=None):
     """Shrink and expand of the segment form, in one launch with v handed off where the
     tiles are short and the weights dense (otherwise the two launches); the bits of the
     two calls."""
-    arr = proj_list(items)
-    _check(lib().lora_sgmv_multi_handoff(_stream(stream), _ptr(x), _ld(x), int(n_rows), segs.ref, len(items), arr,
-                                         _ptr(work), int(work.numel() * work.element_size())))
+    n_rows = _rows_arg(n_rows)
+    _x(x, n_rows, items[0][0].d_in)
+    _segs(segs, n_rows)
+    arr = proj_list(items, n_rows, expand=True)
+    wp, wb = _work(work)
+    _gpu(x=x)
+    _check(lib().lora_sgmv_multi_handoff(_stream(stream), _ptr(x), _ld(x), n_rows, segs.ref, len(items), arr, wp, wb))
 
 
 def lora_bgmv_multi(x, idx, items, chunks=0, stream=None):
     """Shrink and expand of the decode form; chunks: 0 library's choice, -1 two launches,
     c >= 1 one launch with c 512-column chunks per workgroup."""
-    arr = proj_list(items)
-    _check(lib().lora_bgmv_multi(_stream(stream), _ptr(x), _ld(x), _ptr(idx), int(x.shape[0]), len(items), arr,
-                                 int(chunks)))
+    n_rows = _rows_arg(x.shape[0])
+    _x(x, n_rows, items[0][0].d_in)
+    _idx(idx, n_rows)
+    arr = proj_list(items, n_rows, expand=True)
+    _gpu(x=x, idx=idx)
+    _check(lib().lora_bgmv_multi(_stream(stream), _ptr(x), _ld(x), _ptr(idx), n_rows, len(items), arr, int(chunks)))
 
 
 # ------------------------------------------------------------------ adapter pool
@@ -461,5 +724,14 @@ def pack_adapters(adapters, pinned=True):
 
 
 def lora_pool_load(jobs, blob, staging, stream=None):
+    """Place the packed adapters (pack_adapters) into their pools: blob is the host uint8
+    tensor, staging a GPU uint8 tensor of at least blob's size."""
+    check_vector(blob, "blob", "u8", 1, gpu=False)
+    if blob.is_cuda:
+        raise ValueError("blob must be host memory (page-locked for an asynchronous copy)")
+    check_vector(staging, "staging", "u8", int(blob.numel()))
+    for j in jobs:
+        if not j.w:
+            raise ValueError("load job without a target descriptor")
     _check(lib().lora_pool_load(_stream(stream), len(jobs), jobs, _ptr(blob), int(blob.numel()), _ptr(staging),
                                 int(staging.numel())))

@@ -23,6 +23,11 @@ int fail(int code, const char *fmt, ...)
 
 void clear_error() { g_error[0] = '\0'; }
 
+int32_t lora_tile_rows_for(int32_t n_rows, int32_t n_seg)
+{
+    return n_seg > 0 && (int64_t)n_rows >= (int64_t)kLongSegment * n_seg ? LORA_MAX_TILE_ROWS : 2;
+}
+
 int check_weights_desc(const lora_weights *w)
 {
     if (!w) return fail(LORA_E_NULL, "weights descriptor is NULL");
@@ -79,7 +84,7 @@ const char *lora_status_str(int status)
     }
 }
 
-int lora_abi_version(void) { return 1; }
+int lora_abi_version(void) { return 2; }
 
 int lora_build_segments(const int32_t *idx, int32_t n, int32_t num_slots, int32_t *row_map,
                         int32_t *seg_ptr, int32_t *seg_slot, int32_t *n_seg, int32_t *n_act)
@@ -194,14 +199,50 @@ int lora_validate_weights_host(const lora_weights *w)
     return LORA_OK;
 }
 
+// Rows of the row map used by positions [p0, p1): each in [0, n_rows) and at most once.
+static int check_row_map(const int32_t *row_map, int32_t p0, int32_t p1, int32_t n_rows)
+{
+    std::vector<uint8_t> seen((size_t)std::max(n_rows, 0), 0);
+    for (int32_t p = p0; p < p1; ++p) {
+        const int32_t r = row_map[p];
+        if (r < 0 || r >= n_rows) return fail(LORA_E_INDEX, "row_map[%d] = %d outside [0, %d)", p, r, n_rows);
+        if (seen[(size_t)r]) return fail(LORA_E_INDEX, "row %d appears twice in row_map", r);
+        seen[(size_t)r] = 1;
+    }
+    return LORA_OK;
+}
+
 int lora_validate_segments_host(const lora_segments *seg, int32_t n_rows, int32_t num_slots)
 {
     clear_error();
     if (!seg) return fail(LORA_E_NULL, "segments descriptor is NULL");
-    if (seg->n_tiles < 0 || seg->n_pos < 0 || n_rows < 0 || seg->max_rows < 0 || seg->max_rows > LORA_MAX_TILE_ROWS)
+    if (n_rows < 0) return fail(LORA_E_SHAPE, "n_rows = %d", n_rows);
+    if (!seg->tiles) {
+        // offsets form
+        if (seg->n_seg < 0) return fail(LORA_E_SHAPE, "n_seg = %d", seg->n_seg);
+        if (seg->tile_rows < 0 || seg->tile_rows > LORA_MAX_TILE_ROWS)
+            return fail(LORA_E_SHAPE, "tile_rows = %d outside 0..%d", seg->tile_rows, LORA_MAX_TILE_ROWS);
+        if (seg->n_tiles != 0) return fail(LORA_E_NULL, "n_tiles = %d without a tile list", seg->n_tiles);
+        if (seg->n_seg == 0) return LORA_OK;
+        if (!seg->seg_ptr || !seg->seg_slot) return fail(LORA_E_NULL, "seg_ptr and seg_slot are required");
+        if (seg->seg_ptr[0] < 0) return fail(LORA_E_SHAPE, "seg_ptr[0] = %d is negative", seg->seg_ptr[0]);
+        for (int32_t g = 0; g < seg->n_seg; ++g) {
+            if (seg->seg_ptr[g + 1] < seg->seg_ptr[g])
+                return fail(LORA_E_SHAPE, "seg_ptr decreases at segment %d (%d > %d)", g, seg->seg_ptr[g],
+                            seg->seg_ptr[g + 1]);
+            if (seg->seg_slot[g] < -1 || seg->seg_slot[g] >= num_slots)
+                return fail(LORA_E_INDEX, "seg_slot[%d] = %d outside [-1, %d)", g, seg->seg_slot[g], num_slots);
+        }
+        const int32_t end = seg->seg_ptr[seg->n_seg];
+        if (end > n_rows)
+            return fail(LORA_E_INDEX, "seg_ptr[n_seg] = %d exceeds the %d rows (positions are rows or row-map entries)",
+                        end, n_rows);
+        return seg->row_map ? check_row_map(seg->row_map, seg->seg_ptr[0], end, n_rows) : LORA_OK;
+    }
+    // tile-list form
+    if (seg->n_tiles < 0 || seg->n_pos < 0 || seg->max_rows < 0 || seg->max_rows > LORA_MAX_TILE_ROWS)
         return fail(LORA_E_SHAPE, "n_tiles = %d, n_pos = %d, n_rows = %d, max_rows = %d", seg->n_tiles, seg->n_pos,
                     n_rows, seg->max_rows);
-    if (seg->n_tiles > 0 && !seg->tiles) return fail(LORA_E_NULL, "tiles is NULL");
     const int32_t n_pos = seg->row_map ? seg->n_pos : n_rows;
     std::vector<uint8_t> used((size_t)std::max(n_pos, 0), 0);
     for (int32_t t = 0; t < seg->n_tiles; ++t) {
@@ -218,15 +259,17 @@ int lora_validate_segments_host(const lora_segments *seg, int32_t n_rows, int32_
             used[(size_t)p] = 1;
         }
     }
-    if (seg->row_map) {
-        std::vector<uint8_t> seen((size_t)n_rows, 0);
-        for (int32_t p = 0; p < n_pos; ++p) {
-            const int32_t r = seg->row_map[p];
-            if (r < 0 || r >= n_rows) return fail(LORA_E_INDEX, "row_map[%d] = %d outside [0, %d)", p, r, n_rows);
-            if (seen[(size_t)r]) return fail(LORA_E_INDEX, "row %d appears twice in row_map", r);
-            seen[(size_t)r] = 1;
-        }
-    }
+    return seg->row_map ? check_row_map(seg->row_map, 0, n_pos, n_rows) : LORA_OK;
+}
+
+int lora_sgmv_workspace_bytes(const lora_weights *w, int32_t n_rows, int32_t n_seg, size_t *bytes)
+{
+    clear_error();
+    (void)w;
+    if (!bytes) return fail(LORA_E_NULL, "bytes is NULL");
+    *bytes = 0;
+    if (n_rows < 0 || n_seg < 0) return fail(LORA_E_SHAPE, "n_rows = %d, n_seg = %d", n_rows, n_seg);
+    *bytes = lora_handoff_bytes(n_rows);
     return LORA_OK;
 }
 

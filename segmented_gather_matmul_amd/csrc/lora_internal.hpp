@@ -31,6 +31,11 @@ extern thread_local int32_t t_plan_jw, t_plan_nr;
 // launches (shrink, then expand); both give the same bits.
 int32_t plan_fused_chunks(int32_t n_rows, int32_t n_proj, const lora_proj *proj);
 
+// Tile height for a segment batch known only by its size (the offsets form, whose
+// segment lengths are on the device): 64 when the segments average at least
+// kLongSegment rows (n_rows >= kLongSegment * n_seg), else 2.
+int32_t lora_tile_rows_for(int32_t n_rows, int32_t n_seg);
+
 constexpr int32_t kMfmaMinRows = 8;      // launches with a tile this tall run the MFMA kernels
 constexpr int32_t kTargetGroups = 1024;  // shrink workgroups to aim for
 constexpr int32_t kLongSegment = 128;    // segments this long get 64-row (MFMA) tiles

@@ -41,6 +41,13 @@
 
 #include "lora_internal.hpp"
 
+// No floating-point contraction anywhere in the kernels: whether the compiler fused a
+// multiply and an add (or rounded an fp32 product straight to fp16) depended on the
+// template instance, so one projection's result could differ in the last bit between a
+// single-projection launch and a launch serving several.  Every fused operation is an
+// explicit __builtin_fmaf.
+#pragma clang fp contract(off)
+
 namespace lora {
 namespace {
 
@@ -72,10 +79,13 @@ struct ProjDev {
 };
 
 struct TileSrc {
-    const lora_tile *tiles;   // segment form
+    const lora_tile *tiles;   // segment form, tile list (NULL: the offsets below)
     const int32_t *row_map;   // segment form, may be NULL
     int32_t n_pos;
     const int32_t *idx;       // per-row form
+    const int32_t *seg_ptr;   // segment form, offsets: [n_seg + 1]
+    const int32_t *seg_slot;  // [n_seg]
+    int32_t n_seg, tile_rows;
 };
 
 // The one-launch form that hands v from the shrink's workgroups to the expand's
@@ -283,6 +293,82 @@ __device__ inline float wave_sum(float s)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 63));
 }
 
+// ------------------------------------------------------------------------ tiles from offsets
+// The segment form given as offsets (no tile list): each workgroup finds its own tile
+// t of the cut lora_build_tiles makes (segment g of len rows -> ceil(len / T) tiles of
+// near-equal height, in segment order) from seg_ptr and seg_slot, and keeps it in LDS
+// for tile_head.
+
+// This workgroup's tile (offsets form).
+__device__ inline lora_tile &wg_tile()
+{
+    __shared__ lora_tile t;
+    return t;
+}
+
+// Tile t of the offsets form into wg_tile(), or slot -1 when the batch has fewer tiles.
+// The whole workgroup (NT threads) scans NT segments at a time: each lane loads one
+// segment's offsets and slot, counts its tiles, and a prefix sum over the workgroup
+// (shuffles within a wavefront, then the wavefront totals in LDS) gives every segment's
+// first tile; the lane whose range holds t writes the tile.  Offsets are clamped to the
+// positions (the row map's length seg_ptr[n_seg] with a row map, else n_rows), so any
+// device values stay in bounds.  The scan stops at the chunk that holds t.
+template <int NT>
+__device__ void derive_tile(const TileSrc &ts, int n_rows, int t)
+{
+    constexpr int W = NT / 64;
+    __shared__ int wave_total[W];
+    lora_tile &out = wg_tile();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int T = max(ts.tile_rows, 1);
+    const int lim = ts.row_map ? min(n_rows, max(ts.seg_ptr[ts.n_seg], 0)) : n_rows;
+    if (tid == 0) out = lora_tile{-1, 0, 0, -1};
+    int base = 0;  // tiles of the segments before this chunk
+    for (int g0 = 0; g0 < ts.n_seg && base <= t; g0 += NT) {
+        const int g = g0 + tid;
+        int nt = 0, p0 = 0, len = 0, slot = -1;
+        if (g < ts.n_seg) {
+            p0 = min(max(ts.seg_ptr[g], 0), lim);
+            const int p1 = min(max(ts.seg_ptr[g + 1], p0), lim);
+            slot = ts.seg_slot[g];
+            len = p1 - p0;
+            nt = (slot >= 0 && len > 0) ? (len + T - 1) / T : 0;
+        }
+        int inc = nt;  // inclusive prefix sum over the wavefront
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(inc, d);
+            if (lane >= d) inc += u;
+        }
+        if (lane == 63) wave_total[wave] = inc;
+        __syncthreads();
+        int first = base + inc - nt, total = base;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const int s = wave_total[w];
+            first += w < wave ? s : 0;
+            total += s;
+        }
+        if (nt > 0 && t >= first && t < first + nt) {
+            const int q = t - first, rows = len / nt, rem = len - rows * nt;
+            out = lora_tile{slot, p0 + q * rows + min(q, rem), rows + (q < rem ? 1 : 0), g};
+        }
+        base = total;
+        __syncthreads();  // wave_total is rewritten by the next chunk
+    }
+    __syncthreads();
+}
+
+// Every segment-form kernel calls this first (all threads, after uniform early exits):
+// in the offsets form it finds the workgroup's tile; with a tile list it does nothing.
+template <bool PERROW, int NT>
+__device__ inline void prepare_tile(const TileSrc &ts, int n_rows, int t)
+{
+    if constexpr (!PERROW) {
+        if (!ts.tiles) derive_tile<NT>(ts, n_rows, t);
+    }
+}
+
 // ------------------------------------------------------------------------ common head
 // Slot and rows of work tile `t`.  The slot's rank is read separately: the dense
 // layout holds r_max rank-rows per slot, so loads of rank-rows below r_max are in
@@ -302,7 +388,15 @@ __device__ inline TileHead tile_head(const TileSrc &ts, const WeightsDev &w, int
         th.pos0 = t;
         th.nrows = 1;
     } else {
-        const lora_tile tl = ts.tiles[t];
+        lora_tile tl;
+        if (ts.tiles) {
+            tl = ts.tiles[t];
+        } else {
+            // uniform over the workgroup: kept in scalar registers like the tile list's
+            const lora_tile &w = wg_tile();
+            tl = lora_tile{__builtin_amdgcn_readfirstlane(w.slot), __builtin_amdgcn_readfirstlane(w.pos0),
+                           __builtin_amdgcn_readfirstlane(w.nrows), 0};
+        }
         th.slot = tl.slot;
         th.pos0 = tl.pos0;
         th.nrows = min(tl.nrows, LORA_MAX_TILE_ROWS);
@@ -537,6 +631,7 @@ __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args args)
     __shared__ int pcache[PAGED ? kPageCache : 1];
     const Item it = work(a);
     if (!it.ok) return;
+    prepare_tile<PERROW, kThreads>(a.ts, a.n_rows, it.tile);
     shrink_valu_item<PAGED, PERROW, RJ, NR, VSink::Global>(a, it, red, pcache, nullptr);
 }
 
@@ -619,6 +714,7 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Ar
     const int groups = (a.per_tile + NS - 1) / NS;
     const int tile = wi / groups, g0 = (wi - tile * groups) * NS;
     if (tile >= a.n_tiles) return;
+    prepare_tile<false, kMfmaShrinkThreads>(a.ts, a.n_rows, tile);
     const TileHead th = tile_head<false>(a.ts, a.p[0].w, tile);
     if (th.slot < 0 || th.nrows <= 0) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -746,6 +842,7 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_ke
     const int tile = wi / (groups * RB), rem = wi - tile * (groups * RB);
     const int b = RB == 1 ? 0 : rem / groups, g0 = (rem - b * groups) * NS;
     if (tile >= a.n_tiles) return;
+    prepare_tile<false, kMfmaShrinkThreads>(a.ts, a.n_rows, tile);
     const TileHead th = tile_head<false>(a.ts, a.p[0].w, tile);
     if (th.slot < 0 || th.nrows <= 0) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -972,6 +1069,7 @@ void lora_expand_valu_kernel(Args args)
     __shared__ float red[kWaves * NR * 8 * 64];
     const Item it = work_by_slice(a);
     if (!it.ok) return;
+    prepare_tile<PERROW, kThreads>(a.ts, a.n_rows, it.tile);
     const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
     const TileHead th = tile_head<PERROW>(a.ts, pd.w, it.tile);
     if (!th.valid) return;
@@ -1112,6 +1210,7 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(Args args)
     const Item it = tile_item(shrink ? b : b - a.ho.n_shrink, shrink ? a.per_tile : a.ho.e_per_tile, off, a.n_proj,
                               a.n_tiles);
     if (!it.ok) return;
+    prepare_tile<PERROW, kThreads>(a.ts, a.n_rows, it.tile);
     if (shrink) {
         const bool stored = shrink_valu_item<PAGED, PERROW, RJ, NR, VSink::Handoff, kDH>(a, it, red, pcache, nullptr);
         // wavefront 0 made every v store of this workgroup
@@ -1236,6 +1335,7 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args args)
     uint16_t *ys = bt + kCols * KS;                      // SY: y of the slice, [16][kYStride]
     const Item it = work(a);
     if (!it.ok) return;
+    prepare_tile<false, kThreads>(a.ts, a.n_rows, it.tile);
     const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
     const TileHead th = tile_head<false>(a.ts, pd.w, it.tile);
     if (!th.valid) return;
@@ -1355,14 +1455,32 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args args)
                 stage_load(lrow_n, yr);
             }
         }
+        // Row li's power-of-two exponent ex with max_j |s v[row][j]| < 2^ex: the products
+        // run on s v 2^-ex and y 2^-ex, and the result is scaled back by 2^ex, so the fp16
+        // hi/lo parts of s v stay inside fp16's normal range whatever the magnitude of v
+        // (a power-of-two scaling changes no rounding while nothing overflows or
+        // underflows, so in-range values give the same bits as unscaled arithmetic).
+        float mx = 0.f;
+#pragma unroll
+        for (int kq = 0; kq < RQ; ++kq) {
+            const float sv[4] = {vq[kq].x, vq[kq].y, vq[kq].z, vq[kq].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (16 * kq + 4 * lg + e < rank) mx = __builtin_fmaxf(mx, __builtin_fabsf(sc * sv[e]));
+        }
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));  // the row's four k-groups
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+        const int ex = mx > 0.f && mx <= 3.0e38f ? __builtin_amdgcn_frexp_expf(mx) : 0;
         f4_t acc[4][2];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const uint32_t yw[4] = {yq[p].x, yq[p].y, yq[p].z, yq[p].w};
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                acc[p][h] = f4_t{h2f((uint16_t)(yw[2 * h] & 0xffff)), h2f((uint16_t)(yw[2 * h] >> 16)),
-                                 h2f((uint16_t)(yw[2 * h + 1] & 0xffff)), h2f((uint16_t)(yw[2 * h + 1] >> 16))};
+                acc[p][h] = f4_t{__builtin_ldexpf(h2f((uint16_t)(yw[2 * h] & 0xffff)), -ex),
+                                 __builtin_ldexpf(h2f((uint16_t)(yw[2 * h] >> 16)), -ex),
+                                 __builtin_ldexpf(h2f((uint16_t)(yw[2 * h + 1] & 0xffff)), -ex),
+                                 __builtin_ldexpf(h2f((uint16_t)(yw[2 * h + 1] >> 16)), -ex)};
         }
 #pragma unroll
         for (int kq = 0; kq < RQ; ++kq) {
@@ -1372,7 +1490,7 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args args)
             h4_t vhi, vlo;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float m = (j + e < rank) ? sc * sv[e] : 0.f;
+                const float m = (j + e < rank) ? __builtin_ldexpf(sc * sv[e], -ex) : 0.f;
                 const _Float16 hv = (_Float16)m;
                 vhi[e] = hv;
                 vlo[e] = (_Float16)((m - (float)hv) * 2048.f);
@@ -1401,7 +1519,8 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args args)
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int e2 = 0; e2 < 2; ++e2)
-                        o[2 * h + e2] = (uint32_t)f2h(acc[p][h][2 * e2]) | ((uint32_t)f2h(acc[p][h][2 * e2 + 1]) << 16);
+                        o[2 * h + e2] = (uint32_t)f2h(__builtin_ldexpf(acc[p][h][2 * e2], ex)) |
+                                        ((uint32_t)f2h(__builtin_ldexpf(acc[p][h][2 * e2 + 1], ex)) << 16);
                 const uint4 ov = make_uint4(o[0], o[1], o[2], o[3]);
                 if (SY) *reinterpret_cast<uint4 *>(ys + li * kYStride + 128 * wave + 32 * p + 8 * lg) = ov;
                 else *reinterpret_cast<uint4 *>(pd.y + (int64_t)row * pd.ldy + col) = ov;
@@ -1647,11 +1766,52 @@ int check_rows_arg(const void *p, int64_t ld, int32_t need, int32_t mult, const 
 int check_segments(const lora_segments *seg)
 {
     if (!seg) return fail(LORA_E_NULL, "segments descriptor is NULL");
-    if (seg->n_tiles < 0 || seg->n_pos < 0) return fail(LORA_E_SHAPE, "n_tiles = %d, n_pos = %d", seg->n_tiles, seg->n_pos);
-    if (seg->max_rows < 0 || seg->max_rows > LORA_MAX_TILE_ROWS)
-        return fail(LORA_E_SHAPE, "max_rows = %d outside 0..%d", seg->max_rows, LORA_MAX_TILE_ROWS);
-    if (seg->n_tiles > 0 && !seg->tiles) return fail(LORA_E_NULL, "tiles is NULL");
-    if (seg->tiles && !aligned16(seg->tiles)) return fail(LORA_E_ALIGN, "tiles must be 16-byte aligned");
+    if (seg->tiles) {
+        if (seg->n_tiles < 0 || seg->n_pos < 0)
+            return fail(LORA_E_SHAPE, "n_tiles = %d, n_pos = %d", seg->n_tiles, seg->n_pos);
+        if (seg->max_rows < 0 || seg->max_rows > LORA_MAX_TILE_ROWS)
+            return fail(LORA_E_SHAPE, "max_rows = %d outside 0..%d", seg->max_rows, LORA_MAX_TILE_ROWS);
+        if (!aligned16(seg->tiles)) return fail(LORA_E_ALIGN, "tiles must be 16-byte aligned");
+        return LORA_OK;
+    }
+    if (seg->n_tiles != 0) return fail(LORA_E_NULL, "n_tiles = %d without a tile list", seg->n_tiles);
+    if (seg->n_seg < 0) return fail(LORA_E_SHAPE, "n_seg = %d", seg->n_seg);
+    if (seg->tile_rows < 0 || seg->tile_rows > LORA_MAX_TILE_ROWS)
+        return fail(LORA_E_SHAPE, "tile_rows = %d outside 0..%d", seg->tile_rows, LORA_MAX_TILE_ROWS);
+    if (seg->n_seg > 0 && (!seg->seg_ptr || !seg->seg_slot)) return fail(LORA_E_NULL, "seg_ptr and seg_slot are required");
+    return LORA_OK;
+}
+
+// How a checked segment descriptor is launched over n_rows rows: its tile source, the
+// number of tiles the grid covers and the tallest tile.  The offsets form covers
+// n_rows / T + n_seg tiles (an upper bound of sum ceil(len / T) over segments of at
+// most n_rows positions in all); workgroups past the batch's last tile do nothing.
+struct SegLaunch {
+    TileSrc ts;
+    int32_t n_tiles, max_rows;
+};
+
+int seg_launch(const lora_segments *seg, int32_t n_rows, SegLaunch &sl)
+{
+    sl.ts = TileSrc{};
+    sl.ts.row_map = seg->row_map;
+    if (seg->tiles) {
+        sl.ts.tiles = seg->tiles;
+        sl.ts.n_pos = seg->n_pos;
+        sl.n_tiles = seg->n_tiles;
+        sl.max_rows = seg->max_rows > 0 ? seg->max_rows : LORA_MAX_TILE_ROWS;
+        return LORA_OK;
+    }
+    const int32_t T = seg->tile_rows > 0 ? seg->tile_rows : lora_tile_rows_for(n_rows, seg->n_seg);
+    const int64_t bound = seg->n_seg > 0 ? (int64_t)std::max(n_rows, 0) / T + seg->n_seg : 0;
+    if (bound > ((int64_t)1 << 28)) return fail(LORA_E_SHAPE, "%lld tiles are too many for one launch", (long long)bound);
+    sl.ts.seg_ptr = seg->seg_ptr;
+    sl.ts.seg_slot = seg->seg_slot;
+    sl.ts.n_seg = seg->n_seg;
+    sl.ts.tile_rows = T;
+    sl.ts.n_pos = n_rows;
+    sl.n_tiles = (int32_t)bound;
+    sl.max_rows = T;
     return LORA_OK;
 }
 
@@ -1849,15 +2009,6 @@ int expand_impl(void *stream, int32_t n_rows, TileSrc ts, int32_t n_tiles, int32
     return launch_status("expand");
 }
 
-TileSrc seg_src(const lora_segments *seg)
-{
-    TileSrc ts{};
-    ts.tiles = seg->tiles;
-    ts.row_map = seg->row_map;
-    ts.n_pos = seg->n_pos;
-    return ts;
-}
-
 TileSrc row_src(const int32_t *idx)
 {
     TileSrc ts{};
@@ -1980,7 +2131,6 @@ int handoff_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileS
     return launch_status("shrink and expand with v handed off");
 }
 
-inline int32_t seg_max_rows(const lora_segments *seg) { return seg->max_rows > 0 ? seg->max_rows : LORA_MAX_TILE_ROWS; }
 
 lora_proj one_proj(const lora_weights *w, float *v, int64_t ldv, void *y, int64_t ldy)
 {
@@ -2049,18 +2199,20 @@ int lora_sgmv_shrink_multi(void *stream, const void *x, int64_t ldx, int32_t n_r
                            int32_t n_proj, const lora_proj *proj)
 {
     clear_error();
+    SegLaunch sl;
     int st = check_segments(seg);
-    if (st) return st;
-    return shrink_impl<false>(stream, x, ldx, n_rows, seg_src(seg), seg->n_tiles, seg_max_rows(seg), n_proj, proj);
+    if (st || (st = seg_launch(seg, n_rows, sl))) return st;
+    return shrink_impl<false>(stream, x, ldx, n_rows, sl.ts, sl.n_tiles, sl.max_rows, n_proj, proj);
 }
 
 int lora_sgmv_expand_multi(void *stream, int32_t n_rows, const lora_segments *seg, int32_t n_proj,
                            const lora_proj *proj)
 {
     clear_error();
+    SegLaunch sl;
     int st = check_segments(seg);
-    if (st) return st;
-    return expand_impl<false>(stream, n_rows, seg_src(seg), seg->n_tiles, seg_max_rows(seg), n_proj, proj);
+    if (st || (st = seg_launch(seg, n_rows, sl))) return st;
+    return expand_impl<false>(stream, n_rows, sl.ts, sl.n_tiles, sl.max_rows, n_proj, proj);
 }
 
 int lora_bgmv_shrink_multi(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows,
@@ -2170,17 +2322,19 @@ int lora_sgmv_multi_handoff(void *stream, const void *x, int64_t ldx, int32_t n_
             return fail(LORA_E_SHAPE, "projections of one launch share x: d_in %d != %d", proj[p].w->d_in,
                         proj[0].w->d_in);
     if (n_rows < 0) return fail(LORA_E_SHAPE, "n_rows = %d", n_rows);
-    if (n_rows == 0 || seg->n_tiles == 0) return LORA_OK;
+    SegLaunch sl;
+    if ((st = seg_launch(seg, n_rows, sl))) return st;
+    if (n_rows == 0 || sl.n_tiles == 0) return LORA_OK;
     if ((st = check_rows_arg(x, ldx, proj[0].w->d_in, 8, "x"))) return st;
-    const int32_t max_rows = seg_max_rows(seg);
+    const int32_t max_rows = sl.max_rows;
     if (paged || max_rows >= kMfmaMinRows) {
         // the two launches: the MFMA kernels' tiles and paged weights hand nothing off
         if ((st = check_workspace(work, work_bytes, n_rows))) return st;
-        st = shrink_impl<false>(stream, x, ldx, n_rows, seg_src(seg), seg->n_tiles, max_rows, n_proj, proj);
+        st = shrink_impl<false>(stream, x, ldx, n_rows, sl.ts, sl.n_tiles, max_rows, n_proj, proj);
         if (st) return st;
-        return expand_impl<false>(stream, n_rows, seg_src(seg), seg->n_tiles, max_rows, n_proj, proj);
+        return expand_impl<false>(stream, n_rows, sl.ts, sl.n_tiles, max_rows, n_proj, proj);
     }
-    return handoff_impl<false>(stream, x, ldx, n_rows, seg_src(seg), seg->n_tiles, max_rows, n_proj, proj, a, paged,
+    return handoff_impl<false>(stream, x, ldx, n_rows, sl.ts, sl.n_tiles, max_rows, n_proj, proj, a, paged,
                                work, work_bytes);
 }
 

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 33 and set(names) == set(B.EXPORTS)
+    assert len(names) == 34 and set(names) == set(B.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", build_mod.LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (lora_\w+)", out))
@@ -41,7 +41,7 @@ def test_library_exports_every_declared_function():
     assert not missing, missing
     for n in names:
         assert hasattr(B.lib(), n)
-    assert B.lib().lora_abi_version() == 1
+    assert B.lib().lora_abi_version() == 2
 
 
 def test_status_strings():
@@ -370,3 +370,73 @@ def test_pick_tile_rows():
     assert B.lora_pick_tile_rows(np.array([0, 5, 133], np.int32)) == 64         # one of 128 or more
     assert B.lora_pick_tile_rows(np.array([0, 128], np.int32)) == 64
     assert B.lora_pick_tile_rows(np.array([0], np.int32)) == 2                  # no segments
+
+
+# ------------------------------------------------------------------ offsets form of the segment descriptor
+def _offsets(seg_ptr, seg_slot, row_map=None, tile_rows=0):
+    keep = [np.ascontiguousarray(seg_ptr, np.int32), np.ascontiguousarray(seg_slot, np.int32)]
+    s = B.CSegments()
+    s.n_seg, s.seg_ptr, s.seg_slot = len(keep[1]), keep[0].ctypes.data, keep[1].ctypes.data
+    if row_map is not None:
+        keep.append(np.ascontiguousarray(row_map, np.int32))
+        s.row_map = keep[-1].ctypes.data
+    s.tile_rows = tile_rows
+    return s, keep
+
+
+def test_offsets_descriptor_host_checks():
+    """The pages' form (Punica digest, section 5.4: the SGMV call takes the segment offsets
+    s with s[0] = 0 and s[-1] = the batch, and one adapter index per segment)."""
+    L = B.lib()
+    ok, keep = _offsets([0, 1, 4, 6, 8], [0, 1, 2, 3])
+    assert L.lora_validate_segments_host(ctypes.byref(ok), 8, 4) == B.LORA_OK
+    assert L.lora_validate_segments_host(ctypes.byref(ok), 7, 4) == B.LORA_E_INDEX     # s[-1] > rows
+    assert L.lora_validate_segments_host(ctypes.byref(ok), 8, 3) == B.LORA_E_INDEX     # slot 3 >= 3
+    dec, keep2 = _offsets([0, 4, 1, 8], [0, 1, 2])
+    assert L.lora_validate_segments_host(ctypes.byref(dec), 8, 4) == B.LORA_E_SHAPE    # decreasing
+    neg, keep3 = _offsets([-1, 4], [0])
+    assert L.lora_validate_segments_host(ctypes.byref(neg), 8, 4) == B.LORA_E_SHAPE
+    empty, keep4 = _offsets([0, 0, 3, 3, 3], [2, -1, 0, 1])                             # empty and -1 segments
+    assert L.lora_validate_segments_host(ctypes.byref(empty), 3, 4) == B.LORA_OK
+    rm, keep5 = _offsets([0, 2, 3], [1, 0], row_map=[5, 1, 5])
+    assert L.lora_validate_segments_host(ctypes.byref(rm), 6, 2) == B.LORA_E_INDEX     # row 5 twice
+    rm2, keep6 = _offsets([0, 2, 3], [1, 0], row_map=[5, 1, 6])
+    assert L.lora_validate_segments_host(ctypes.byref(rm2), 6, 2) == B.LORA_E_INDEX    # row 6 >= 6
+    assert L.lora_validate_segments_host(ctypes.byref(rm2), 7, 2) == B.LORA_OK
+    tall, keep7 = _offsets([0, 8], [0], tile_rows=65)
+    assert L.lora_validate_segments_host(ctypes.byref(tall), 8, 1) == B.LORA_E_SHAPE
+    # the launching calls check the descriptor before anything else
+    c = _desc()
+    tall.tile_rows = 65
+    assert L.lora_sgmv_shrink(None, FAKE, 16, FAKE, 1024, 8, ctypes.byref(c), ctypes.byref(tall)) == B.LORA_E_SHAPE
+    nul, keep8 = _offsets([0, 8], [0])
+    nul.seg_ptr = None
+    assert L.lora_sgmv_expand(None, FAKE, 1024, FAKE, 16, 8, ctypes.byref(c), ctypes.byref(nul)) == B.LORA_E_NULL
+    neg_seg = B.CSegments()
+    neg_seg.n_seg = -1
+    assert L.lora_sgmv_shrink(None, FAKE, 16, FAKE, 1024, 8, ctypes.byref(c), ctypes.byref(neg_seg)) == B.LORA_E_SHAPE
+    # no segments, or no rows: nothing is read or launched
+    none = B.CSegments()
+    assert L.lora_sgmv_shrink(None, FAKE, 16, FAKE, 1024, 8, ctypes.byref(c), ctypes.byref(none)) == B.LORA_OK
+    assert L.lora_sgmv_expand(None, FAKE, 1024, FAKE, 16, 0, ctypes.byref(c), ctypes.byref(ok)) == B.LORA_OK
+
+
+def test_offsets_host_helper_rejects_bad_offsets():
+    with pytest.raises(B.LoraError):
+        B.segments_from_offsets(np.array([0, 3, 2], np.int32), np.array([0, 1], np.int32), device="cpu")
+    segs = B.segments_from_offsets(np.array([0, 1, 4, 6, 8], np.int32), np.arange(4, dtype=np.int32), device="cpu")
+    assert segs.is_offsets and segs.c.n_seg == 4 and segs.n_tiles == 0
+    with pytest.raises(ValueError, match="GPU tensor"):
+        segs.ref
+
+
+def test_workspace_bytes():
+    L = B.lib()
+    out = ctypes.c_size_t(123)
+    assert L.lora_sgmv_workspace_bytes(None, 32, 32, ctypes.byref(out)) == B.LORA_OK
+    assert out.value == L.lora_handoff_bytes(32) > 0
+    assert L.lora_sgmv_workspace_bytes(None, 0, 0, ctypes.byref(out)) == B.LORA_OK and out.value == 0
+    assert L.lora_sgmv_workspace_bytes(None, -1, 0, ctypes.byref(out)) == B.LORA_E_SHAPE
+    assert L.lora_sgmv_workspace_bytes(None, 1, -1, ctypes.byref(out)) == B.LORA_E_SHAPE
+    assert L.lora_sgmv_workspace_bytes(None, 1, 1, None) == B.LORA_E_NULL
+    assert B.lora_sgmv_workspace_bytes(8, 4) == L.lora_handoff_bytes(8)
