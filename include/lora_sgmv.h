@@ -343,6 +343,24 @@ int lora_bgmv_multi_handoff(void *stream, const void *x, int64_t ldx, const int3
                             int32_t n_proj, const lora_proj *proj, void *work, size_t work_bytes);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): lora_bgmv_multi_handoff with the
+ * hand-off workspace held by the library, a file-scope device array of
+ * LORA_NOALLOC_MAX_ROWS rows (2 MiB) on each GPU, kept until the process ends.  Same
+ * result, bit for bit.  No hipMalloc, hipFree or other allocation happens in the call.
+ * The first call on a device looks up that device's copy of the array and clears it
+ * with a small kernel on `stream` (recorded into the graph when `stream` is being
+ * captured, where it then runs on every replay).  Every call on one GPU shares the array and leaves it all zero when
+ * it completes, so calls ordered on one stream (graph replays included) may share it;
+ * calls that may run at the same time on one GPU race and give wrong results.
+ * LORA_E_SHAPE for n_rows > LORA_NOALLOC_MAX_ROWS (checked before anything else is done
+ * on the GPU); other arguments and errors as for lora_bgmv_multi_handoff.
+ */
+#define LORA_NOALLOC_MAX_ROWS 1024
+int lora_bgmv_multi_handoff_noalloc(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows,
+                                    int32_t n_proj, const lora_proj *proj);
+
+/*
  * The segment form's counterpart (Punica summary, "The SGMV Operator"): the result of
  * lora_sgmv_shrink_multi followed by lora_sgmv_expand_multi, bit for bit, v included.
  * With dense weights and tiles of fewer than 8 rows (seg->max_rows, the tile heights

@@ -35,7 +35,8 @@ EXPORTS = ["lora_build_segments", "lora_tiles_bound", "lora_build_tiles", "lora_
            "lora_set_plan", "lora_pool_state_bytes", "lora_pool_init", "lora_pool_alloc", "lora_pool_release",
            "lora_pool_free_count", "lora_pool_pages_for", "lora_pool_load_header_bytes", "lora_pool_load",
            "lora_handoff_bytes", "lora_bgmv_multi_handoff", "lora_sgmv_multi_handoff", "lora_set_handoff_polls",
-           "lora_sgmv_workspace_bytes"]
+           "lora_sgmv_workspace_bytes", "lora_bgmv_multi_handoff_noalloc"]
+NOALLOC_MAX_ROWS = 1024
 MAX_PROJ = 4
 
 
@@ -113,6 +114,7 @@ def lib() -> ctypes.CDLL:
             "lora_pool_release": [P, I32, P],
             "lora_pool_load": [P, I32, P, P, ctypes.c_size_t, P, ctypes.c_size_t],
             "lora_sgmv_workspace_bytes": [P, I32, I32, P],
+            "lora_bgmv_multi_handoff_noalloc": [P, P, I64, P, I32, I32, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -632,6 +634,19 @@ def lora_bgmv_multi_handoff(x, idx, items, work, stream=None):
     _gpu(x=x, idx=idx)
     _check(lib().lora_bgmv_multi_handoff(_stream(stream), _ptr(x), _ld(x), _ptr(idx), n_rows, len(items), arr, wp,
                                          wb))
+
+
+def lora_bgmv_multi_handoff_noalloc(x, idx, items, stream=None):
+    """lora_bgmv_multi_handoff with the library's own hand-off scratch (at most
+    NOALLOC_MAX_ROWS rows; no allocation in the call; calls that may overlap on one GPU
+    race)."""
+    n_rows = _rows_arg(x.shape[0])
+    _x(x, n_rows, items[0][0].d_in)
+    _idx(idx, n_rows)
+    arr = proj_list(items, n_rows, expand=True)
+    _gpu(x=x, idx=idx)
+    _check(lib().lora_bgmv_multi_handoff_noalloc(_stream(stream), _ptr(x), _ld(x), _ptr(idx), n_rows, len(items),
+                                                 arr))
 
 
 def lora_sgmv_multi_handoff(x, segs, items, n_rows, work, stream=None):

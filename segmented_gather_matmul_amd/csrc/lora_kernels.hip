@@ -38,6 +38,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "lora_internal.hpp"
 
@@ -2169,6 +2170,51 @@ int32_t plan_shrink_jw(int32_t work_tiles, int32_t r_max)
     return t_plan_jw > 0 ? t_plan_jw : jw;
 }
 
+// ------------------------------------------------------------------------ hand-off without allocation
+// lora_bgmv_multi_handoff_noalloc: the hand-off workspace is this file-scope array, one
+// copy per GPU, instead of caller memory.  Host code never passes `scratch` itself (its
+// name is a host-side stand-in, not a device address): each device's address comes
+// from hipGetSymbolAddress, taken once per device with that device current, and only
+// that address reaches a kernel.  Every call on one GPU shares its copy; the hand-off
+// protocol leaves it all zero after each call, so calls ordered on one stream may
+// follow each other, while calls that may overlap on one GPU race.
+constexpr int32_t kNoallocRows = LORA_NOALLOC_MAX_ROWS;
+constexpr size_t kNoallocWords = (size_t)kNoallocRows * LORA_MAX_PROJ * kHandoffWords;
+static __device__ __align__(256) uint32_t scratch[kNoallocWords];  // 2 MiB on every GPU
+
+constexpr int kMaxDevices = 64;
+uint32_t *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null: not set up)
+std::mutex g_scratch_mu;
+
+__global__ __launch_bounds__(kThreads) void lora_clear_words(uint32_t *p, size_t n)
+{
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kThreads) p[i] = 0u;
+}
+
+// This device's scratch address; set up on the first call on the device: the address,
+// then a clear of the whole array on `s` (a kernel, so it may be captured in a graph;
+// the array starts zero anyway).
+int noalloc_scratch(hipStream_t s, uint32_t *&ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(LORA_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(LORA_E_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(LORA_E_HIP, "hipGetSymbolAddress of the hand-off scratch: %s", hipGetErrorString(e));
+        hipLaunchKernelGGL(lora_clear_words, dim3(256), dim3(kThreads), 0, s, static_cast<uint32_t *>(p), kNoallocWords);
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(LORA_E_HIP, "clearing the hand-off scratch: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = static_cast<uint32_t *>(p);
+    }
+    ptr = g_scratch_ptr[dev];
+    return LORA_OK;
+}
+
 }  // namespace lora
 
 using namespace lora;
@@ -2306,6 +2352,24 @@ int lora_bgmv_multi_handoff(void *stream, const void *x, int64_t ldx, const int3
     if (st || n_rows == 0) return st;
     return handoff_impl<true>(stream, x, ldx, n_rows, row_src(idx), n_rows, 1, n_proj, proj, a, paged, work,
                               work_bytes);
+}
+
+int lora_bgmv_multi_handoff_noalloc(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows,
+                                    int32_t n_proj, const lora_proj *proj)
+{
+    clear_error();
+    Args a{};
+    bool paged = false;
+    int st = check_bgmv_multi(x, ldx, idx, n_rows, n_proj, proj, a, paged);
+    if (st || n_rows == 0) return st;
+    if (n_rows > kNoallocRows)
+        return fail(LORA_E_SHAPE, "n_rows = %d exceeds the %d rows of the library's hand-off scratch", n_rows,
+                    kNoallocRows);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t *work = nullptr;
+    if ((st = noalloc_scratch(s, work))) return st;
+    return handoff_impl<true>(stream, x, ldx, n_rows, row_src(idx), n_rows, 1, n_proj, proj, a, paged, work,
+                              kNoallocWords * sizeof(uint32_t));
 }
 
 int lora_sgmv_multi_handoff(void *stream, const void *x, int64_t ldx, int32_t n_rows, const lora_segments *seg,

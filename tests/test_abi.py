@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 34 and set(names) == set(B.EXPORTS)
+    assert len(names) == 35 and set(names) == set(B.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", build_mod.LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (lora_\w+)", out))
@@ -440,3 +440,17 @@ def test_workspace_bytes():
     assert L.lora_sgmv_workspace_bytes(None, 1, -1, ctypes.byref(out)) == B.LORA_E_SHAPE
     assert L.lora_sgmv_workspace_bytes(None, 1, 1, None) == B.LORA_E_NULL
     assert B.lora_sgmv_workspace_bytes(8, 4) == L.lora_handoff_bytes(8)
+
+
+def test_noalloc_handoff_rejects_more_rows_than_its_scratch():
+    """The allocation-free hand-off form holds LORA_NOALLOC_MAX_ROWS rows; larger calls are
+    rejected on the host before anything reaches the GPU."""
+    L = B.lib()
+    c1 = _desc()
+    arr = (B.CProj * 1)()
+    arr[0].w, arr[0].v, arr[0].ldv, arr[0].y, arr[0].ldy = ctypes.addressof(c1), FAKE, 16, FAKE, 1024
+    n = B.NOALLOC_MAX_ROWS + 1
+    assert L.lora_bgmv_multi_handoff_noalloc(None, FAKE, 1024, FAKE, n, 1, arr) == B.LORA_E_SHAPE
+    assert "scratch" in B.last_error() and str(B.NOALLOC_MAX_ROWS) in B.last_error()
+    assert L.lora_bgmv_multi_handoff_noalloc(None, FAKE, 1024, None, 8, 1, arr) == B.LORA_E_NULL
+    assert L.lora_bgmv_multi_handoff_noalloc(None, FAKE, 1024, FAKE, 0, 1, arr) == B.LORA_OK   # nothing to do
