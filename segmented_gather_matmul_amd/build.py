@@ -31,6 +31,9 @@ def flags() -> list[str]:
     return ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
             # Packed FP32 instructions stay off: plain float code is compiled to scalar FP32 ops.
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # Leading scalar kernel arguments (up to four; only the hand-off kernel has any
+            # before its argument block) arrive preloaded in scalar registers.
+            "-mllvm", "-amdgpu-kernarg-preload-count=4",
             "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

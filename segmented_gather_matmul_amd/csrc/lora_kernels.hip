@@ -151,6 +151,36 @@ __device__ inline const Args &touched_args()
     return *(const Args *)(args_t *)ka;
 }
 
+// touched_args for an argument block that starts OFF bytes into the kernel arguments
+// (after leading scalar arguments): one scalar load per 64-byte line it spans.
+template <int OFF>
+__device__ inline const Args &touched_args_at()
+{
+    static_assert(OFF % 8 == 0 && OFF + sizeof(Args) <= 13 * 64, "13 lines of kernel arguments");
+    auto ka = __builtin_amdgcn_kernarg_segment_ptr();
+    int t0, t1, t2, t3, t4, t5, t6, t7, t8, t9, t10, t11, t12;
+    asm volatile(
+        "s_load_dword %0, %13, 0x0\n\t"
+        "s_load_dword %1, %13, 0x40\n\t"
+        "s_load_dword %2, %13, 0x80\n\t"
+        "s_load_dword %3, %13, 0xc0\n\t"
+        "s_load_dword %4, %13, 0x100\n\t"
+        "s_load_dword %5, %13, 0x140\n\t"
+        "s_load_dword %6, %13, 0x180\n\t"
+        "s_load_dword %7, %13, 0x1c0\n\t"
+        "s_load_dword %8, %13, 0x200\n\t"
+        "s_load_dword %9, %13, 0x240\n\t"
+        "s_load_dword %10, %13, 0x280\n\t"
+        "s_load_dword %11, %13, 0x2c0\n\t"
+        "s_load_dword %12, %13, 0x300\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=s"(t0), "=s"(t1), "=s"(t2), "=s"(t3), "=s"(t4), "=s"(t5), "=s"(t6), "=s"(t7), "=s"(t8), "=s"(t9),
+          "=s"(t10), "=s"(t11), "=s"(t12), "+s"(ka));
+    typedef const __attribute__((address_space(4))) Args args_t;
+    typedef const __attribute__((address_space(4))) char bytes_t;
+    return *(const Args *)(args_t *)((bytes_t *)ka + OFF);
+}
+
 // The kernel arguments as a kernel reads them: through touched_args with dense weights;
 // with paged weights directly (there the touch measured slower: the kernels' extra
 // registers cost a wavefront per SIMD).
@@ -380,6 +410,17 @@ struct TileHead {
     bool valid;
 };
 
+// The head of a tile record already read (its slot checked against this projection).
+__device__ inline TileHead head_of(const lora_tile &tl, const WeightsDev &w)
+{
+    TileHead th;
+    th.slot = tl.slot;
+    th.pos0 = tl.pos0;
+    th.nrows = min(tl.nrows, LORA_MAX_TILE_ROWS);
+    th.valid = th.slot >= 0 && th.slot < w.num_slots && th.nrows > 0;
+    return th;
+}
+
 template <bool PERROW>
 __device__ inline TileHead tile_head(const TileSrc &ts, const WeightsDev &w, int t)
 {
@@ -551,14 +592,14 @@ enum class VSink { Global, Lds, Handoff };
 // the tile's rows [only_rg, only_rg + NR).
 template <bool PAGED, bool PERROW, int RJ, int NR, VSink SINK, int DH = 0>
 __device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *red, int *pcache, float *vlds,
-                                        int only_rg = -1)
+                                        int only_rg = -1, bool use_known = false, lora_tile known = lora_tile{})
 {
     // halves in flight together: about 16 loads per lane, an even count (whole pairs)
     constexpr int D = DH > 0 ? DH : (16 / (NR + RJ)) & ~1 ? (16 / (NR + RJ)) & ~1 : 2;
     const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
     const int j0 = it.slice * a.jw;
     const int jend = min(j0 + a.jw, pd.w.r_max);
-    const TileHead th = tile_head<PERROW>(a.ts, pd.w, it.tile);
+    const TileHead th = use_known ? head_of(known, pd.w) : tile_head<PERROW>(a.ts, pd.w, it.tile);
     if (!th.valid || j0 >= jend) return false;
     const int rank = slot_rank(pd.w, th.slot);
     const int jload = PAGED ? min(jend, rank) : jend;
@@ -1191,10 +1232,19 @@ __device__ inline void tile_rows(const Args &a, const TileHead &th, int rg, int 
         rows[q] = rg + q < th.nrows ? row_of<PERROW>(a.ts, th.pos0 + rg + q, a.n_rows) : -1;
 }
 
+// The hand-off kernel takes four scalar arguments ahead of the argument block, which the
+// hardware preloads into scalar registers (the library is built with kernel-argument
+// preloading): the tile source (per-row slots or the tile list; NULL for the offsets
+// form) and the grid layout.  With them each workgroup reads its tile's record at once,
+// in parallel with the argument block instead of after it.
+constexpr int kHandoffArgsOffset = 24;  // byte offset of the argument block after the four
+                                        // leading arguments (8 + 3 * 4 bytes, 8-byte aligned)
+static_assert(alignof(Args) == 8, "argument block alignment");
+
 template <bool PAGED, bool PERROW, int RJ, int NR, int RU>
-__global__ __launch_bounds__(kThreads) void lora_handoff_kernel(Args args)
+__global__ __launch_bounds__(kThreads) void lora_handoff_kernel(const void *__restrict__ pre_src, int32_t pre_n_shrink,
+                                                                int32_t pre_per_tile, int32_t pre_e_per_tile, Args args)
 {
-    const Args &a = kernel_args<!PAGED>(args);
     constexpr int kDH = RJ + NR == 2 ? 4 : 0;    // the shrink items' halves in flight (registers)
     __shared__ float red[kWaves * NR * 8 * 64];  // the shrink's kWaves * NR * RJ sums or the expand's
     __shared__ int pcache[PAGED ? kPageCache : 1];
@@ -1202,6 +1252,17 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(Args args)
     __shared__ int s_ok[NR];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x;
+    // this workgroup's tile record, from the preloaded arguments (the grid holds exactly
+    // n_tiles * (per_tile + e_per_tile) workgroups, so the tile exists)
+    const bool have_early = pre_src != nullptr;
+    lora_tile early{-1, 0, 0, -1};
+    if (have_early) {
+        const bool sh = b < pre_n_shrink;
+        const int t = (sh ? b : b - pre_n_shrink) / (sh ? pre_per_tile : pre_e_per_tile);
+        if constexpr (PERROW) early = lora_tile{static_cast<const int32_t *>(pre_src)[t], t, 1, t};
+        else early = static_cast<const lora_tile *>(pre_src)[t];
+    }
+    const Args &a = PAGED ? args : touched_args_at<kHandoffArgsOffset>();
     // The item comes from kernel arguments read before the first branch (both parts'
     // layouts), so the slot and the projection's descriptor are one round trip later.
     const bool shrink = b < a.ho.n_shrink;
@@ -1213,12 +1274,14 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(Args args)
     if (!it.ok) return;
     prepare_tile<PERROW, kThreads>(a.ts, a.n_rows, it.tile);
     if (shrink) {
-        const bool stored = shrink_valu_item<PAGED, PERROW, RJ, NR, VSink::Handoff, kDH>(a, it, red, pcache, nullptr);
+        const bool stored =
+            shrink_valu_item<PAGED, PERROW, RJ, NR, VSink::Handoff, kDH>(a, it, red, pcache, nullptr, -1, have_early,
+                                                                         early);
         // wavefront 0 made every v store of this workgroup
         if (stored && wave == 0) {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the hand-off stores have completed
             const ProjDev &pd = a.p[it.p];
-            const TileHead th = tile_head<PERROW>(a.ts, pd.w, it.tile);
+            const TileHead th = have_early ? head_of(early, pd.w) : tile_head<PERROW>(a.ts, pd.w, it.tile);
             for (int rg = 0; rg < th.nrows; rg += NR) {
                 int rows[NR];
                 tile_rows<PERROW, NR>(a, th, rg, rows);
@@ -1228,7 +1291,7 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(Args args)
         return;
     }
     const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
-    const TileHead th = tile_head<PERROW>(a.ts, pd.w, it.tile);
+    const TileHead th = have_early ? head_of(early, pd.w) : tile_head<PERROW>(a.ts, pd.w, it.tile);
     if (!th.valid) return;
     const int rank = slot_rank(pd.w, th.slot);
     const int jlim = PAGED ? rank : pd.w.r_max;
@@ -1242,7 +1305,8 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(Args args)
         for (int r = 0; r < th.nrows; ++r) {
             for (int sl = 0; sl < a.p[it.p].slices; ++sl) {
                 const Item si{it.tile, it.p, sl, true};
-                shrink_valu_item<PAGED, PERROW, 1, 1, VSink::Lds, 2>(a, si, red, pcache, &vrow[0][0], r);
+                shrink_valu_item<PAGED, PERROW, 1, 1, VSink::Lds, 2>(a, si, red, pcache, &vrow[0][0], r, have_early,
+                                                                     early);
             }
             ExpandPass<PERROW, 1> ps;
             tile_rows<PERROW, 1>(a, th, r, ps.rows);
@@ -1297,7 +1361,8 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(Args args)
                 const Item si{it.tile, it.p, sl, true};
                 // one rank-row and one pair of halves at a time: few registers on a path
                 // that only runs when the poll limit runs out
-                shrink_valu_item<PAGED, PERROW, 1, NR, VSink::Lds, 2>(a, si, red, pcache, &vrow[0][0], 0);
+                shrink_valu_item<PAGED, PERROW, 1, NR, VSink::Lds, 2>(a, si, red, pcache, &vrow[0][0], 0, have_early,
+                                                                      early);
             }
         }
 #pragma unroll
@@ -1713,6 +1778,21 @@ __global__ __launch_bounds__(kFusedThreads) void lora_fused_row_kernel(Args args
 // Event pair attached to this thread's next kernel launch (lora_set_launch_events).
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
 
+// A launch whose kernel takes leading scalar arguments before the argument block.
+template <typename Kernel>
+void launch_pre(Kernel kernel, dim3 grid, int threads, size_t lds, hipStream_t s, const void *src, int32_t n0,
+                int32_t n1, int32_t n2, const Args &a)
+{
+    const dim3 block(threads);
+    if (t_ev_start || t_ev_stop) {
+        hipEvent_t e0 = t_ev_start, e1 = t_ev_stop;
+        t_ev_start = t_ev_stop = nullptr;
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, s, e0, e1, 0, src, n0, n1, n2, a);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, src, n0, n1, n2, a);
+    }
+}
+
 template <typename Kernel>
 void launch(Kernel kernel, dim3 grid, int threads, size_t lds, hipStream_t s, const Args &a)
 {
@@ -2109,10 +2189,18 @@ int handoff_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileS
     a.ts = ts;
     const dim3 grid((unsigned)a.grid);
     hipStream_t s = static_cast<hipStream_t>(stream);
-#define LORA_HANDOFF_RU(PG, RJ, NR)                                                           \
-    if (r_max <= 16) launch(lora_handoff_kernel<PG, PERROW, RJ, NR, 4>, grid, kThreads, 0, s, a); \
-    else if (r_max <= 32) launch(lora_handoff_kernel<PG, PERROW, RJ, NR, 8>, grid, kThreads, 0, s, a); \
-    else launch(lora_handoff_kernel<PG, PERROW, RJ, NR, 16>, grid, kThreads, 0, s, a)
+    // the preloaded leading arguments: tile source and grid layout
+    const void *pre_src = PERROW ? static_cast<const void *>(ts.idx) : static_cast<const void *>(ts.tiles);
+#define LORA_HANDOFF_RU(PG, RJ, NR)                                                                              \
+    if (r_max <= 16)                                                                                             \
+        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 4>, grid, kThreads, 0, s, pre_src, a.ho.n_shrink,    \
+                   a.per_tile, a.ho.e_per_tile, a);                                                              \
+    else if (r_max <= 32)                                                                                        \
+        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 8>, grid, kThreads, 0, s, pre_src, a.ho.n_shrink,    \
+                   a.per_tile, a.ho.e_per_tile, a);                                                              \
+    else                                                                                                         \
+        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 16>, grid, kThreads, 0, s, pre_src, a.ho.n_shrink,   \
+                   a.per_tile, a.ho.e_per_tile, a)
 #define LORA_HANDOFF_JW(PG, NR)                      \
     if (a.jw == 1) { LORA_HANDOFF_RU(PG, 1, NR); }    \
     else if (a.jw == 2) { LORA_HANDOFF_RU(PG, 2, NR); } \
