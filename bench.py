@@ -171,10 +171,10 @@ def make_ops(spec, layers, device, tile_rows=None):
     return groups
 
 
-def launch_unit(kind, ops, fused_chunks):
-    """One launch over `ops` (projections sharing x): kind is "shrink", "expand",
-    "handoff" (both steps of the per-row form in one launch, v handed off) or "fused"
-    (both steps in one launch, v recomputed per workgroup)."""
+def launch_unit(kind, ops):
+    """One launch over `ops` (projections sharing x): kind is "shrink", "expand" or
+    "handoff" (both steps in one launch, v handed from the shrink's workgroups to the
+    expand's)."""
     from segmented_gather_matmul_amd import binding as B
     op0 = ops[0]
     items = [(op.ws if kind == "shrink" else op.w, op.v, op.y) for op in ops]
@@ -183,8 +183,6 @@ def launch_unit(kind, ops, fused_chunks):
         B.lora_bgmv_multi_handoff(op0.x, op0.idx, items, op0.work)
     elif kind == "handoff":
         B.lora_sgmv_multi_handoff(op0.x, op0.segs, items, n, op0.work)
-    elif kind == "fused":
-        B.lora_bgmv_multi(op0.x, op0.idx, items, chunks=fused_chunks)
     elif op0.segs is None:
         if kind == "shrink":
             B.lora_bgmv_shrink_multi(op0.x, op0.idx, items)
@@ -198,29 +196,25 @@ def launch_unit(kind, ops, fused_chunks):
         B.lora_sgmv_expand_multi(op0.segs, items, n)
 
 
-def launches(groups, grouped, fused_chunks, handoff=False):
+def launches(groups, grouped, handoff=False):
     """(kind, ops) of every launch of one step, in order.  With handoff each unit of the
-    per-row or segment form is one hand-off launch; with fused_chunks >= 1 each unit of
-    the per-row form is one fused launch."""
+    per-row or segment form is one hand-off launch."""
     out = []
     for ops in groups:
         units = [ops] if grouped else [[op] for op in ops]
         for u in units:
-            one = fused_chunks >= 1 or handoff
-            if one and any(op.shrink_rank is not None for op in u):
+            if handoff and any(op.shrink_rank is not None for op in u):
                 raise SystemExit("the one-launch forms read one weight descriptor; this workload's shrink has its own")
             if handoff and not u[0].expand_per_row:
                 out.append(("handoff", u))
-            elif u[0].segs is None and fused_chunks >= 1:
-                out.append(("fused", u))
             else:
                 out += [("shrink", u), ("expand", u)]
     return out
 
 
-def step(plan, fused_chunks):
+def step(plan):
     for kind, ops in plan:
-        launch_unit(kind, ops, fused_chunks)
+        launch_unit(kind, ops)
 
 
 # ------------------------------------------------------------------ HIP events (raw handles)
@@ -247,7 +241,7 @@ class HipEvents:
         self.hip.hipEventDestroy(e)
 
 
-def kernel_durations(plan, fused_chunks, steps):
+def kernel_durations(plan, steps):
     """Duration of every launch, from event pairs attached to the launches themselves
     (hipExtLaunchKernel records start and stop on the launch stream)."""
     from segmented_gather_matmul_amd import binding as B
@@ -258,7 +252,7 @@ def kernel_durations(plan, fused_chunks, steps):
         for kind, u in plan:
             e0, e1 = ev.create(), ev.create()
             B.lora_set_launch_events(e0, e1)
-            launch_unit(kind, u, fused_chunks)
+            launch_unit(kind, u)
             recs.append((kind, u, e0, e1))
     torch.cuda.synchronize()
     out = {}
@@ -320,7 +314,7 @@ def unit_counts(spec, ops):
     sf = sum(cm.shrink_flops(idx, sr, o.d_in) for o, sr in zip(ops, srank))
     ef = sum(cm.expand_flops(idx, rank, o.d_out) for o in ops)
     return dict(shrink_bytes=sb, expand_bytes=eb, shrink_flops=sf, expand_flops=ef,
-                fused_bytes=sb + eb, fused_flops=sf + ef, handoff_bytes=sb + eb, handoff_flops=sf + ef)
+                handoff_bytes=sb + eb, handoff_flops=sf + ef)
 
 
 def kernel_source_sha():
@@ -669,14 +663,12 @@ def layer_sweep(args):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
     side = torch.cuda.Stream()
-    out = {"sweep": "layer", "form": args.layer_form, "chunks": args.layer_chunks, "rank": r,
+    out = {"sweep": "layer", "form": args.layer_form, "rank": r,
            "resident_adapters": slots, "layers": L, "steps": K, "results": []}
     for model in args.sweep_models.split(","):
         shape = LY.SHAPES[model]
         log(f"[layer] {shape.name}: drawing {L} layers")
         layers = [LY.random_layer(shape, slots, r, max(ns), gen) for _ in range(L)]
-        for lay in layers:
-            lay.chunks = args.layer_chunks
         dims = LY.proj_dims(shape)
         for seq in seqs:
             for n in ns:
@@ -768,9 +760,6 @@ def main():
                     help="per-row and segment forms: one launch per unit with v handed from the shrink's "
                          "workgroups to the expand's (auto: the per-row form with dense weights, where it measures "
                          "faster than two launches)")
-    ap.add_argument("--fused-chunks", type=int, default=-1,
-                    help="per-row form: -1 = separate shrink and expand launches (the library's choice); c >= 1 = "
-                         "one launch per unit, each workgroup covering c 512-column chunks")
     ap.add_argument("--no-floors", action="store_true", help="skip the empty-launch and copy reference steps")
     ap.add_argument("--plan", default="0,0", metavar="JW,NR",
                     help="fix rank-rows per VALU shrink workgroup and rows per pass of the segment-form VALU "
@@ -792,8 +781,6 @@ def main():
     ap.add_argument("--sweep-seqs", default="512,2048", help="layer sweep: cache lengths")
     ap.add_argument("--layer-form", choices=["bgmv", "sgmv"], default="bgmv",
                     help="layer sweep: add-ons in the per-row or the segment form")
-    ap.add_argument("--layer-chunks", type=int, default=0,
-                    help="layer sweep, per-row form: 0 = library's choice, -1 = two launches, c >= 1 = one launch")
     args = ap.parse_args()
     if args.calibrate_copy:
         import torch
@@ -843,31 +830,28 @@ def main():
     decode_form = spec["form"] in ("bgmv", "sgmv")
     if args.handoff == "on" and not decode_form:
         raise SystemExit("--handoff on needs the per-row or segment form (--form bgmv or sgmv)")
-    if args.handoff == "on" and args.fused_chunks >= 1:
-        raise SystemExit("--handoff on and --fused-chunks >= 1 are two different one-launch forms")
     # the library's hand-off form where it measures faster: the per-row form with dense
     # weights (the segment form's two launches are as fast or faster since its expand runs
     # the planned tile in one pass)
-    handoff = args.handoff == "on" or (args.handoff == "auto" and spec["form"] == "bgmv" and spec["layout"] == "dense"
-                                       and args.fused_chunks < 1)
+    handoff = args.handoff == "on" or (args.handoff == "auto" and spec["form"] == "bgmv" and spec["layout"] == "dense")
     if handoff:
         work = B.handoff_workspace(spec["batch"].n, device)
         for ops in groups:
             for op in ops:
                 op.work = work
-    plan = launches(groups, grouped, args.fused_chunks, handoff)
+    plan = launches(groups, grouped, handoff)
     n_launch = len(plan)
 
     log(f"[bench] {n_launch} launches/step, {step_bytes / 1e6:.1f} MB algorithmic per step; warmup {args.warmup}")
     stream = torch.cuda.current_stream()
     if args.no_graph:
-        run = lambda: step(plan, args.fused_chunks)
+        run = lambda: step(plan)
     else:
-        step(plan, args.fused_chunks)  # first eager pass (loads kernels)
+        step(plan)  # first eager pass (loads kernels)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step(plan, args.fused_chunks)
+            step(plan)
         run = g.replay
     for _ in range(args.warmup):
         run()
@@ -884,7 +868,7 @@ def main():
     log(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step (wall {wall_ms:.4f})")
 
     log(f"[bench] per-launch event pass: {args.kernel_steps} steps")
-    kd = kernel_durations(plan, args.fused_chunks, args.kernel_steps)
+    kd = kernel_durations(plan, args.kernel_steps)
     per_kernel, totals = {}, {}
     for k in kd:
         recs = kd[k]
@@ -908,7 +892,7 @@ def main():
                 for key, (n, t, nb) in by_shape.items()}
     dom = max(per_kernel, key=lambda k: totals[k])
     pk = per_kernel[dom]
-    kernel_name = {"shrink": "lora_shrink_kernel", "expand": "lora_expand_kernel", "fused": "lora_fused_row_kernel",
+    kernel_name = {"shrink": "lora_shrink_kernel", "expand": "lora_expand_kernel",
                    "handoff": "lora_handoff_kernel"}[dom]
     traffic = None if args.rows is not None else traffic_from_profile(args.workload, dom)
     roofline = dict(bound="hbm", achieved=pk["gbs"], peak=cm.HBM_PEAK_GBS, unit="GB/s",
@@ -945,7 +929,7 @@ def main():
                    "num_slots": spec["num_slots"], "rank": sorted(set(int(r) for r in spec["rank"])),
                    "popularity": spec["popularity"], "form": spec["form"], "layout": spec["layout"],
                    "grouped": grouped, "launches_per_step": n_launch, "tile_rows": args.tile_rows,
-                   "fused_chunks": args.fused_chunks if spec["form"] == "bgmv" else None, "handoff": handoff,
+                   "handoff": handoff,
                    "plan": args.plan,
                    "graph": not args.no_graph,
                    "parallelism": "none"},

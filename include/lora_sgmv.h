@@ -276,7 +276,7 @@ int lora_bgmv_expand(void *stream, void *y, int64_t ldy, const float *v, int64_t
  * The whole add-on in decode form (Punica digest, section 5.5, BGMV; blog reference
  * loop): the result of lora_bgmv_shrink followed by lora_bgmv_expand, bit for bit.
  * v (device fp32 [n_rows][ldv]) receives the shrink result as documented above.
- * Same as lora_bgmv_multi with one projection and chunks = 0.
+ * Same as lora_bgmv_multi with one projection.
  */
 int lora_bgmv(void *stream, void *y, int64_t ldy, const void *x, int64_t ldx, const int32_t *idx,
               int32_t n_rows, const lora_weights *w, float *v, int64_t ldv);
@@ -303,21 +303,11 @@ int lora_bgmv_expand_multi(void *stream, const int32_t *idx, int32_t n_rows, int
 
 /*
  * Shrink and expand of the decode form for up to LORA_MAX_PROJ projections sharing x:
- * every projection p gets, bit for bit, the v and y of lora_bgmv_shrink_multi followed
- * by lora_bgmv_expand_multi.  Argument rules are the union of theirs, all checked
- * before anything is launched.
- *   chunks = -1: those two launches;
- *   chunks >= 1: one launch.  Each workgroup covers `chunks` 512-column pieces of one
- *                row's d_out and recomputes that row's v itself, so no step waits for
- *                another workgroup; the workgroup holding the row's first piece
- *                stores v;
- *   chunks = 0:  the library chooses (currently the two launches, which measure faster
- *                at the Llama-2 decode shapes).
- * With one launch, v must not overlap x, y or the weights (it is written while they
- * are read).
+ * lora_bgmv_shrink_multi followed by lora_bgmv_expand_multi (two launches), with the
+ * arguments of both checked before either is launched.
  */
 int lora_bgmv_multi(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows,
-                    int32_t n_proj, const lora_proj *proj, int32_t chunks);
+                    int32_t n_proj, const lora_proj *proj);
 
 /*
  * The same result as lora_bgmv_multi (bit for bit, v included) in ONE launch without

@@ -104,7 +104,7 @@ def lib() -> ctypes.CDLL:
             "lora_bgmv_shrink_multi": [P, P, I64, P, I32, I32, P],
             "lora_bgmv_expand_multi": [P, P, I32, I32, P],
             "lora_pick_tile_rows": [P, I32],
-            "lora_bgmv_multi": [P, P, I64, P, I32, I32, P, I32],
+            "lora_bgmv_multi": [P, P, I64, P, I32, I32, P],
             "lora_set_plan": [I32, I32],
             "lora_bgmv_multi_handoff": [P, P, I64, P, I32, I32, P, P, ctypes.c_size_t],
             "lora_set_handoff_polls": [I32],
@@ -662,15 +662,14 @@ def lora_sgmv_multi_handoff(x, segs, items, n_rows, work, stream=None):
     _check(lib().lora_sgmv_multi_handoff(_stream(stream), _ptr(x), _ld(x), n_rows, segs.ref, len(items), arr, wp, wb))
 
 
-def lora_bgmv_multi(x, idx, items, chunks=0, stream=None):
-    """Shrink and expand of the decode form; chunks: 0 library's choice, -1 two launches,
-    c >= 1 one launch with c 512-column chunks per workgroup."""
+def lora_bgmv_multi(x, idx, items, stream=None):
+    """Shrink and expand of the decode form (two launches, arguments of both checked first)."""
     n_rows = _rows_arg(x.shape[0])
     _x(x, n_rows, items[0][0].d_in)
     _idx(idx, n_rows)
     arr = proj_list(items, n_rows, expand=True)
     _gpu(x=x, idx=idx)
-    _check(lib().lora_bgmv_multi(_stream(stream), _ptr(x), _ld(x), _ptr(idx), n_rows, len(items), arr, int(chunks)))
+    _check(lib().lora_bgmv_multi(_stream(stream), _ptr(x), _ld(x), _ptr(idx), n_rows, len(items), arr))
 
 
 # ------------------------------------------------------------------ adapter pool

@@ -27,10 +27,6 @@ int32_t plan_shrink_jw(int32_t work_tiles, int32_t r_max);
 // workgroup and rows per pass of the segment-form VALU kernels (0 = planned).
 extern thread_local int32_t t_plan_jw, t_plan_nr;
 
-// Chunks of 512 columns per workgroup of the fused per-row launch, or -1 for two
-// launches (shrink, then expand); both give the same bits.
-int32_t plan_fused_chunks(int32_t n_rows, int32_t n_proj, const lora_proj *proj);
-
 // Tile height for a segment batch known only by its size (the offsets form, whose
 // segment lengths are on the device): 64 when the segments average at least
 // kLongSegment rows (n_rows >= kLongSegment * n_seg), else 2.

@@ -31,8 +31,8 @@
 //     by every 16-row slice; D^T = B^T (s v)^T runs on v_mfma_f32_16x16x16_f16 with s*v
 //     split into fp16 hi + lo/2048 parts (two MFMAs, ~22 bits kept); the accumulator
 //     starts from y and each lane moves 8 consecutive y elements of one row.
-// Optionally, the per-row form runs both steps in one launch, each workgroup
-// recomputing its row's v (lora_fused_row_kernel); the bits match the two launches.
+// The per-row and the segment forms of decode batches also run both steps in one launch,
+// the shrink's workgroups handing v to the expand's (lora_handoff_kernel).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -106,7 +106,6 @@ struct Args {
     int64_t ldx;
     int32_t n_rows, n_tiles, n_proj, per_tile, grid;
     int32_t jw;         // shrink: rank-rows per workgroup
-    int32_t gc;         // fused: 512-column chunks of d_out per workgroup
     int32_t off[LORA_MAX_PROJ];  // first slice of projection p within a tile's items
     TileSrc ts;
     ProjDev p[LORA_MAX_PROJ];
@@ -118,8 +117,6 @@ constexpr int kWaves = 4;
 constexpr int kRowsPerPass = 4;     // rows per pass of the VALU kernels (segment form)
 constexpr int kCols = 512;           // expand columns per workgroup
 constexpr int kMfmaShrinkThreads = 1024;  // 16 wavefronts split d_in in the MFMA shrink
-constexpr int kFusedGroups = 4;            // 256-lane groups of a fused workgroup
-constexpr int kFusedThreads = kFusedGroups * kThreads;
 
 // The kernel arguments, read through a pointer that comes out of one scalar load per
 // 64-byte line of them, all issued before a single wait: every argument read that
@@ -1613,167 +1610,6 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args args)
     }
 }
 
-// ------------------------------------------------------------------------ fused (per-row form)
-// Shrink and expand of the per-row form in one launch.  Workgroup = one row x one
-// projection x `gc` consecutive 512-column chunks of d_out, as four 256-lane groups.
-//   1. v of the row: each batch of 16 rank-rows gives group g rank-rows
-//      [4g, 4g + 4); every rank-row is summed with lora_shrink_valu_kernel's lane
-//      striping, per-lane order and wavefront order, so v is bit-identical to the
-//      separate shrink.  The workgroup holding the row's first chunk stores v.
-//   2. Group g applies lora_expand_valu_kernel's arithmetic to chunks g, g + 4, ...
-//      of the range, so y is bit-identical to the separate expand.
-// Every workgroup of a row recomputes v from the row's A^T rank-rows; they are
-// consecutive work items, so they run on one XCD and all but the first read of A
-// hit its L2.  For r_max <= 32, B and y of a group's first chunk are requested before
-// the shrink's loads, so they arrive while v is being summed.
-template <bool PAGED, int RU>
-__global__ __launch_bounds__(kFusedThreads) void lora_fused_row_kernel(Args args)
-{
-    const Args &a = kernel_args<!PAGED>(args);
-    constexpr int RJ = 4;  // rank-rows per group per batch
-    __shared__ float sred[kFusedGroups][kWaves][RJ];
-    __shared__ float vrow[LORA_MAX_RANK];
-    __shared__ float ered[kFusedGroups][kWaves][8][64];
-    __shared__ int pcache[PAGED ? kPageCache : 1];
-    const Item it = work(a);
-    if (!it.ok) return;
-    const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
-    const TileHead th = tile_head<true>(a.ts, pd.w, it.tile);
-    const int row = row_of<true>(a.ts, th.pos0, a.n_rows);
-    if (!th.valid || row < 0) return;
-    const int rank = slot_rank(pd.w, th.slot);
-    const int r_max = pd.w.r_max;
-    const int jload = PAGED ? min(r_max, rank) : r_max;  // shrink loads
-    const int jlim = PAGED ? rank : r_max;                // expand loads
-    const int tid = threadIdx.x, g = tid >> 8, gt = tid & 255, lane = tid & 63, wave = (tid >> 6) & 3;
-    const int n_chunks = (pd.w.d_out + kCols - 1) / kCols;
-    const int ch0 = it.slice * a.gc, ch1 = min(ch0 + a.gc, n_chunks);
-    const int passes = (ch1 - ch0 + kFusedGroups - 1) / kFusedGroups;
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
-
-    // B (first block of rank-rows) and y of the first pass, ahead of the shrink's loads
-    constexpr int UB = RU < 8 ? RU : 8;  // rank-rows per wavefront per block of B loads
-    constexpr bool kEarly = RU <= 8;     // registers allow B to wait through the shrink
-    uint4 bv[UB], yv = z4;
-    int c = (ch0 + g) * kCols + 8 * lane;
-    bool cin = ch0 + g < ch1 && c < pd.w.d_out;
-    if (kEarly) {
-        load_b_octets<PAGED, UB>(pd.w, th.slot, jlim, wave, 0, c, cin, bv);
-        if (wave == 0 && cin) yv = load16(pd.y + (int64_t)row * pd.ldy + c);
-    }
-
-    // 1. v
-    bool cached = false;
-    int64_t ptb = 0;
-    if (PAGED) {
-        ptb = pt_base<false>(pd.w, th.slot);
-        if (jload > 0) cached = cache_a_pages<kFusedThreads>(pd.w, th.slot, 0, jload, pcache);
-    }
-    const int n_oct = pd.w.d_in >> 3;
-    const uint16_t *xr = a.x + (int64_t)row * a.ldx;
-    for (int jb = 0; jb < r_max; jb += kFusedGroups * RJ) {
-        const int jg = jb + g * RJ;
-        float acc[RJ];
-#pragma unroll
-        for (int jj = 0; jj < RJ; ++jj) acc[jj] = 0.f;
-        for (int o = gt; o < n_oct; o += 2 * kThreads) {
-            const int o2 = o + kThreads;
-            const bool in2 = o2 < n_oct;
-            const uint4 xv = load16(xr + 8 * o), xw = in2 ? load16(xr + 8 * o2) : z4;
-            uint4 av[RJ], aw[RJ];
-#pragma unroll
-            for (int jj = 0; jj < RJ; ++jj) {
-                av[jj] = aw[jj] = z4;
-                const int j = jg + jj;
-                if (j >= jload) continue;
-                if (!PAGED) {
-                    const uint16_t *r = dense_row<false>(pd.w, th.slot, j);
-                    av[jj] = load16(r + 8 * o);
-                    if (in2) aw[jj] = load16(r + 8 * o2);
-                } else {
-                    const uint16_t *p = a_paged(pd.w, pcache, cached, ptb, 0, j, 8 * o);
-                    if (p) av[jj] = load16(p);
-                    if (in2) {
-                        const uint16_t *p2 = a_paged(pd.w, pcache, cached, ptb, 0, j, 8 * o2);
-                        if (p2) aw[jj] = load16(p2);
-                    }
-                }
-            }
-#pragma unroll
-            for (int jj = 0; jj < RJ; ++jj) acc[jj] = dot8(xw, aw[jj], dot8(xv, av[jj], acc[jj]));
-        }
-#pragma unroll
-        for (int jj = 0; jj < RJ; ++jj) {
-            const float s = wave_sum(acc[jj]);
-            if (lane == 0) sred[g][wave][jj] = s;
-        }
-        __syncthreads();
-        if (gt < RJ && jg + gt < r_max) {
-            const int j = jg + gt;
-            const float s = sred[g][0][gt] + sred[g][1][gt] + sred[g][2][gt] + sred[g][3][gt];
-            const float vj = j < rank ? s : 0.f;
-            vrow[j] = vj;
-            if (it.slice == 0 && rank > 0) pd.v[(int64_t)row * pd.ldv + j] = vj;
-        }
-        __syncthreads();
-    }
-
-    // 2. y += scale v B on this group's chunks
-    const float sc = pd.w.scale[th.slot];
-    const float sv = lane < rank ? sc * vrow[lane] : 0.f;
-    for (int ps = 0; ps < passes; ++ps) {
-        if (ps > 0 || !kEarly) {
-            c = (ch0 + g + kFusedGroups * ps) * kCols + 8 * lane;
-            cin = ch0 + g + kFusedGroups * ps < ch1 && c < pd.w.d_out;
-            load_b_octets<PAGED, UB>(pd.w, th.slot, jlim, wave, 0, c, cin, bv);
-            yv = (wave == 0 && cin) ? load16(pd.y + (int64_t)row * pd.ldy + c) : z4;
-        }
-        float acc[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll
-        for (int ub = 0; ub < RU; ub += UB) {
-            if (ub > 0) load_b_octets<PAGED, UB>(pd.w, th.slot, jlim, wave, ub, c, cin, bv);
-#pragma unroll
-            for (int u = 0; u < UB; ++u) {
-                const int j = wave + kWaves * (ub + u);
-                if (j >= rank) break;
-                const uint32_t bw[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
-                float bf[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    bf[2 * e] = h2f((uint16_t)(bw[e] & 0xffff));
-                    bf[2 * e + 1] = h2f((uint16_t)(bw[e] >> 16));
-                }
-                const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv), j));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(s, bf[e], acc[e]);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ered[g][wave][e][lane] = acc[e];
-        __syncthreads();
-        if (wave == 0 && cin && rank > 0) {
-            const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w};
-            uint32_t out[4];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                float d[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int e = 2 * e2 + h;
-                    d[h] = ered[g][0][e][lane] + ered[g][1][e][lane] + ered[g][2][e][lane] + ered[g][3][e][lane];
-                }
-                const float lo = h2f((uint16_t)(yw[e2] & 0xffff)) + d[0];
-                const float hi = h2f((uint16_t)(yw[e2] >> 16)) + d[1];
-                out[e2] = (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
-            }
-            *reinterpret_cast<uint4 *>(pd.y + (int64_t)row * pd.ldy + c) = make_uint4(out[0], out[1], out[2], out[3]);
-        }
-        __syncthreads();
-    }
-}
-
 // ------------------------------------------------------------------------ launchers
 // Event pair attached to this thread's next kernel launch (lora_set_launch_events).
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
@@ -2097,39 +1933,6 @@ TileSrc row_src(const int32_t *idx)
     return ts;
 }
 
-// Per-row form, shrink and expand in one launch (lora_fused_row_kernel); gc >= 1 chunks
-// of 512 columns per workgroup.  Arguments are checked by the caller.
-int fused_row_impl(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows, int32_t n_proj,
-                   const lora_proj *proj, int32_t gc, Args &a, bool paged)
-{
-    int32_t r_max = 0, most = 1;
-    for (int32_t p = 0; p < n_proj; ++p) most = std::max(most, (proj[p].w->d_out + kCols - 1) / kCols);
-    gc = std::min(gc, most);  // more chunks than the widest projection has change nothing
-    for (int32_t p = 0; p < n_proj; ++p) {
-        const int32_t chunks = (proj[p].w->d_out + kCols - 1) / kCols;
-        a.p[p].slices = (chunks + gc - 1) / gc;
-        r_max = std::max(r_max, proj[p].w->r_max);
-    }
-    int st = finish_layout(a, n_rows);
-    if (st) return st;
-    a.gc = gc;
-    a.x = static_cast<const uint16_t *>(x);
-    a.ldx = ldx;
-    a.n_rows = n_rows;
-    a.n_tiles = n_rows;
-    a.ts = row_src(idx);
-    const dim3 grid((unsigned)a.grid);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-#define LORA_FUSED(RU)                                                                     \
-    (paged ? launch(lora_fused_row_kernel<true, RU>, grid, kFusedThreads, 0, s, a)         \
-           : launch(lora_fused_row_kernel<false, RU>, grid, kFusedThreads, 0, s, a))
-    if (r_max <= 16) LORA_FUSED(4);
-    else if (r_max <= 32) LORA_FUSED(8);
-    else LORA_FUSED(16);
-#undef LORA_FUSED
-    return launch_status("fused bgmv");
-}
-
 constexpr int32_t kHandoffPolls = 1 << 15;  // ~30 ms of polling before computing v locally
 thread_local int32_t t_handoff_polls = kHandoffPolls;
 constexpr int64_t kResidentGroups = 2048;   // 256 CUs x 8 workgroups of 4 wavefronts (<= 64 VGPRs)
@@ -2235,18 +2038,6 @@ lora_proj one_proj(const lora_weights *w, float *v, int64_t ldv, void *y, int64_
 }  // namespace
 
 thread_local int32_t t_plan_jw = 0, t_plan_nr = 0;
-
-int32_t plan_fused_chunks(int32_t n_rows, int32_t n_proj, const lora_proj *proj)
-{
-    // Two launches.  Measured on MI355X at the Llama-2 7B and 70B decode shapes, the one-
-    // launch form is slower (e.g. 50 vs 44 us per 7B layer): each workgroup streams the
-    // row's whole A^T through one CU, whose load path sustains roughly 25-30 GB/s, and
-    // the recomputation multiplies what the CUs ingest, while a launch costs ~2.5 us.
-    (void)n_rows;
-    (void)n_proj;
-    (void)proj;
-    return -1;
-}
 
 int32_t plan_shrink_jw(int32_t work_tiles, int32_t r_max)
 {
@@ -2409,17 +2200,14 @@ static int check_bgmv_multi(const void *x, int64_t ldx, const int32_t *idx, int3
 }
 
 int lora_bgmv_multi(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows, int32_t n_proj,
-                    const lora_proj *proj, int32_t chunks)
+                    const lora_proj *proj)
 {
     clear_error();
     // Check everything both steps need before launching either.
     Args a{};
     bool paged = false;
-    if (chunks < -1) return fail(LORA_E_SHAPE, "chunks = %d (-1, 0 or a chunk count)", chunks);
     int st = check_bgmv_multi(x, ldx, idx, n_rows, n_proj, proj, a, paged);
     if (st || n_rows == 0) return st;
-    const int32_t gc = chunks == 0 ? plan_fused_chunks(n_rows, n_proj, proj) : chunks;
-    if (gc > 0) return fused_row_impl(stream, x, ldx, idx, n_rows, n_proj, proj, gc, a, paged);
     st = shrink_impl<true>(stream, x, ldx, n_rows, row_src(idx), n_rows, 1, n_proj, proj);
     if (st) return st;
     return expand_impl<true>(stream, n_rows, row_src(idx), n_rows, 1, n_proj, proj);
@@ -2501,7 +2289,7 @@ int lora_bgmv(void *stream, void *y, int64_t ldy, const void *x, int64_t ldx, co
               const lora_weights *w, float *v, int64_t ldv)
 {
     const lora_proj p = one_proj(w, v, ldv, y, ldy);
-    return lora_bgmv_multi(stream, x, ldx, idx, n_rows, 1, &p, 0);
+    return lora_bgmv_multi(stream, x, ldx, idx, n_rows, 1, &p);
 }
 
 }  // extern "C"

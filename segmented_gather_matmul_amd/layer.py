@@ -108,17 +108,15 @@ class LoraDecoderLayer:
     seven projections.  max_rows bounds the batch (it sizes the v buffers).  Each add-on call
     hands v from the shrink's workgroups to the expand's in one launch (handoff, through a
     workspace the layer owns; the segment form does so for tiles of fewer than 8 rows);
-    with handoff False, chunks is passed to the per-row form's lora_bgmv_multi (0: the
-    library's choice of one or two launches).  overlap:
+    with handoff False, each call makes a shrink and an expand launch.  overlap:
     each shrink runs on a second stream (default priority) concurrently with the backbone
     GEMM of its projections, the expand after that GEMM.  The results are the same bits
     in every case."""
 
-    def __init__(self, shape: LlamaShape, backbone: dict, adapters: dict, rank, scale, max_rows, chunks=0,
-                 overlap=False, handoff=True):
+    def __init__(self, shape: LlamaShape, backbone: dict, adapters: dict, rank, scale, max_rows, overlap=False,
+                 handoff=True):
         import torch
         self.shape = shape
-        self.chunks = int(chunks)
         self.side = torch.cuda.Stream(device=rank.device) if overlap else None
         self.work = B.handoff_workspace(max_rows, rank.device) if handoff and not overlap else None
         self.bb = backbone
@@ -179,7 +177,7 @@ class LoraDecoderLayer:
             if meta.form == "bgmv" and self.work is not None:
                 B.lora_bgmv_multi_handoff(x, meta.idx, items, self.work)
             elif meta.form == "bgmv":
-                B.lora_bgmv_multi(x, meta.idx, items, chunks=self.chunks)
+                B.lora_bgmv_multi(x, meta.idx, items)
             elif self.work is not None:
                 B.lora_sgmv_multi_handoff(x, meta.segs, items, n, self.work)
             else:

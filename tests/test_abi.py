@@ -279,19 +279,17 @@ def test_multi_projection_errors():
     assert L.lora_bgmv_expand_multi(None, FAKE, 0, 2, arr) == B.LORA_OK                     # no rows: no launch
 
 
-def test_one_launch_decode_errors():
+def test_two_step_decode_errors():
     """lora_bgmv_multi checks what both steps need before launching anything."""
     L = B.lib()
     c1, c2 = _desc(), _desc(d_in=2048)
     arr = (B.CProj * 2)()
     for i in range(2):
         arr[i].w, arr[i].v, arr[i].ldv, arr[i].y, arr[i].ldy = ctypes.addressof(c1), FAKE, 16, FAKE, 1024
-    call = lambda x=FAKE, ldx=1024, idx=FAKE, n=8, n_proj=2, a=arr, chunks=0: \
-        L.lora_bgmv_multi(None, x, ldx, idx, n, n_proj, a, chunks)
+    call = lambda x=FAKE, ldx=1024, idx=FAKE, n=8, n_proj=2, a=arr: L.lora_bgmv_multi(None, x, ldx, idx, n, n_proj, a)
     assert call(idx=None) == B.LORA_E_NULL
     assert call(n_proj=0) == B.LORA_E_SHAPE
     assert call(a=None) == B.LORA_E_NULL
-    assert call(chunks=-2) == B.LORA_E_SHAPE
     assert call(n=-1) == B.LORA_E_SHAPE
     assert call(x=None) == B.LORA_E_NULL
     assert call(x=FAKE + 8) == B.LORA_E_ALIGN
@@ -305,7 +303,7 @@ def test_one_launch_decode_errors():
     arr[1].w = ctypes.addressof(c2)
     assert call() == B.LORA_E_SHAPE and "share x" in B.last_error()
     arr[1].w = ctypes.addressof(c1)
-    assert call(n=0) == B.LORA_OK and call(n=0, chunks=-1) == B.LORA_OK and call(n=0, chunks=3) == B.LORA_OK
+    assert call(n=0) == B.LORA_OK
 
 
 def test_handoff_decode_errors():

@@ -1,7 +1,7 @@
 """GPU: shrink and expand in one launch with v handed from the shrink's workgroups to the
 expand's, against the two-launch path bit for bit on whole buffers (guard rows and
 padding included), and the two-launch path against the fp64 oracle: the per-row form
-(lora_bgmv_multi_handoff vs lora_bgmv_multi with chunks = -1) and the segment form
+(lora_bgmv_multi_handoff vs lora_bgmv_multi) and the segment form
 (lora_sgmv_multi_handoff vs lora_sgmv_shrink_multi + lora_sgmv_expand_multi, over tiles
 of 1, 2 and 4 rows, and over taller tiles and paged weights, where it makes the two
 launches itself).
@@ -58,7 +58,7 @@ def _compare(label, x_d, idx_d, ws, dcs, work):
             dc.reset()
         items = [(w, dc.v, dc.y) for w, dc in zip(ws, dcs)]
         if mode == "two":
-            B.lora_bgmv_multi(x_d, idx_d, items, chunks=-1)
+            B.lora_bgmv_multi(x_d, idx_d, items)
         else:
             B.lora_set_handoff_polls(0 if mode == "local" else -1)
             try:
