@@ -538,7 +538,7 @@ def operator_sweep(args):
 # ------------------------------------------------------------------ adapter loading
 def load_sweep(args):
     """Loading adapters into one paged pool (lora_pool_load: one host-to-device copy of a
-    page-locked blob, one scatter kernel).  A Llama-2-7B adapter set (32 layers x 7
+    page-locked blob, one scatter kernel on a small fixed grid).  A Llama-2-7B adapter set (32 layers x 7
     projections, rank 16, 256-element pages) per model; `--sweep-batches` models per call.
     Reported next to a plain host-to-device copy of the same blob (the link's rate) and to
     the 7B decode step's time with and without a load running on a side stream."""
@@ -552,12 +552,16 @@ def load_sweep(args):
     # the decode step, to see what a concurrent load costs it
     spec = workload_spec("decode_distinct_7b")
     groups = make_ops(spec, spec["layers"], dev)
-    plan = launches(groups, True, -1)
-    step(plan, -1)
+    work = B.handoff_workspace(spec["batch"].n, dev)   # the bench default: one hand-off launch per unit
+    for ops in groups:
+        for op in ops:
+            op.work = work
+    plan = launches(groups, True, handoff=True)
+    step(plan)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        step(plan, -1)
+        step(plan)
     side = torch.cuda.Stream()
     for models in [int(v) for v in (args.sweep_batches or "1,2,4").split(",")]:
         per_model_pages = layers * sum(r * (di // P + do // P) for di, do in shapes.values())

@@ -4,9 +4,9 @@
 //
 // Pages all hold P fp16 elements, so allocation is a stack of page ids and never
 // fragments.  Loading is one host-to-device copy of a caller-packed blob (job table,
-// rank-rows, page ids) into a staging buffer, then one kernel (grid y = job, x = page
-// groups) that scatters every page, writes its page-table entry and sets each slot's
-// rank, scale and offsets.
+// rank-rows, page ids) into a staging buffer, then one kernel with a small fixed grid that
+// scatters every page, writes its page-table entry and sets each slot's rank, scale and
+// offsets.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -64,19 +64,27 @@ struct alignas(16) LoadJobDev {
 static_assert(sizeof(LoadJobDev) % 16 == 0, "job records keep 16-byte alignment");
 
 constexpr int kLoadThreads = 256;
-constexpr int kLoadMaxJobsY = 65535;  // grid y limit; more jobs are taken in a loop
+constexpr int kLoadUnroll = 8;        // pages per lane group per work item (loads in flight per lane)
+#ifndef LORA_LOAD_WORKGROUPS
+#define LORA_LOAD_WORKGROUPS 1024
+#endif
+constexpr int kLoadWorkgroups = LORA_LOAD_WORKGROUPS;  // the scatter's grid: four workgroups per CU
 
-// Job blockIdx.y (+ gridDim.y, ...): workgroup x takes pages [x*ppw, (x+1)*ppw) of the
-// job, ppw = pages per workgroup, each page copied by P/8 lanes (16 bytes per lane) or,
-// for P > 2048, by the whole workgroup in a loop.  The first workgroup of a job also
-// writes the slot's rank, scale and page-table offsets.
-__global__ __launch_bounds__(kLoadThreads) void lora_pool_scatter_kernel(const unsigned char *staging, int32_t n_jobs)
+// Work item f (of n_jobs * gx) is job f / gx, page block f % gx: kLoadUnroll groups of
+// ppw pages, each page copied by P/8 lanes (16 bytes per lane) or, for P > 2048, by the
+// whole workgroup in a loop.  The small fixed grid walks the items in a grid-stride loop,
+// so a load takes few CU slots from kernels running beside it, and each lane has
+// kLoadUnroll loads in flight before its stores.  The first item of a job also writes
+// the slot's rank, scale and page-table offsets.
+__global__ __launch_bounds__(kLoadThreads) void lora_pool_scatter_kernel(const unsigned char *staging, int32_t n_jobs,
+                                                                         int64_t gx)
 {
     const LoadJobDev *jobs = reinterpret_cast<const LoadJobDev *>(staging);
     const int tid = threadIdx.x;
-    for (int64_t jx = blockIdx.y; jx < n_jobs; jx += gridDim.y) {
+    for (int64_t f = blockIdx.x; f < (int64_t)n_jobs * gx; f += gridDim.x) {
+        const int64_t jx = f / gx, bx = f - jx * gx;
         const LoadJobDev &jb = jobs[jx];
-        if (blockIdx.x == 0 && tid == 0) {
+        if (bx == 0 && tid == 0) {
             jb.rank[jb.slot] = jb.r;
             if (jb.r > 0) {
                 jb.scale[jb.slot] = jb.sc;
@@ -85,25 +93,42 @@ __global__ __launch_bounds__(kLoadThreads) void lora_pool_scatter_kernel(const u
             }
         }
         const int lanes = min(kLoadThreads, jb.P / 8);  // lanes per page
-        const int ppw = kLoadThreads / lanes;             // pages per workgroup
-        const int64_t e = (int64_t)blockIdx.x * ppw + tid / lanes;
-        if (e >= jb.n_pages || tid / lanes >= ppw) continue;
-        const int32_t id = reinterpret_cast<const int32_t *>(staging + jb.pages_off)[e];
+        const int ppw = kLoadThreads / lanes;             // pages per workgroup and unroll step
+        const int g = tid / lanes, lane = tid % lanes;
+        if (g >= ppw) continue;
         const int64_t a_pages = (int64_t)jb.r * (jb.d_in / jb.P);
-        int64_t src;  // element offset of the page's first element in the job's data
-        if (e < a_pages) {
-            const int64_t per = jb.d_in / jb.P, j = e / per, q = e - j * per;
-            src = j * jb.d_in + q * jb.P;
-        } else {
+        const uint16_t *data = reinterpret_cast<const uint16_t *>(staging + jb.data_off);
+        const int32_t *ids = reinterpret_cast<const int32_t *>(staging + jb.pages_off);
+        int64_t e0 = bx * ppw * kLoadUnroll + g;
+        // element offset of page e's first element in the job's data
+        auto src_of = [&](int64_t e) {
+            if (e < a_pages) {
+                const int64_t per = jb.d_in / jb.P, j = e / per, q = e - j * per;
+                return j * jb.d_in + q * jb.P;
+            }
             const int64_t per = jb.d_out / jb.P, e2 = e - a_pages, j = e2 / per, q = e2 - j * per;
-            src = (int64_t)jb.r * jb.d_in + j * jb.d_out + q * jb.P;
+            return (int64_t)jb.r * jb.d_in + j * jb.d_out + q * jb.P;
+        };
+        for (int k = 8 * lane; k < jb.P; k += 8 * lanes) {
+            uint4 v[kLoadUnroll];
+#pragma unroll
+            for (int u = 0; u < kLoadUnroll; ++u) {
+                const int64_t e = e0 + (int64_t)u * ppw;
+                if (e < jb.n_pages) v[u] = *reinterpret_cast<const uint4 *>(data + src_of(e) + k);
+            }
+#pragma unroll
+            for (int u = 0; u < kLoadUnroll; ++u) {
+                const int64_t e = e0 + (int64_t)u * ppw;
+                if (e < jb.n_pages) *reinterpret_cast<uint4 *>(jb.pool + (int64_t)ids[e] * jb.P + k) = v[u];
+            }
         }
-        const uint16_t *from = reinterpret_cast<const uint16_t *>(staging + jb.data_off) + src;
-        uint16_t *to = jb.pool + (int64_t)id * jb.P;
-        const int lane = tid % lanes;
-        for (int k = 8 * lane; k < jb.P; k += 8 * lanes)
-            *reinterpret_cast<uint4 *>(to + k) = *reinterpret_cast<const uint4 *>(from + k);
-        if (lane == 0) jb.page_table[jb.pt_off + e] = id;
+        if (lane == 0) {
+#pragma unroll
+            for (int u = 0; u < kLoadUnroll; ++u) {
+                const int64_t e = e0 + (int64_t)u * ppw;
+                if (e < jb.n_pages) jb.page_table[jb.pt_off + e] = ids[e];
+            }
+        }
     }
 }
 
@@ -321,16 +346,17 @@ int lora_pool_load(void *stream, int32_t n_jobs, const lora_load_job *jobs, void
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipMemcpyAsync(staging, blob, blob_bytes, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return fail(LORA_E_HIP, "pool load copy: %s", hipGetErrorString(e));
-    // x: enough workgroups for the job with the most pages; y: jobs
+    // work items per job: enough page blocks for the job with the most pages
     int64_t gx = 1;
     for (int32_t i = 0; i < n_jobs; ++i) {
         const LoadJobDev &d = table[i];
-        const int ppw = kLoadThreads / std::min(kLoadThreads, d.P / 8);
-        gx = std::max<int64_t>(gx, (d.n_pages + ppw - 1) / ppw);
+        const int64_t block = (int64_t)(kLoadThreads / std::min(kLoadThreads, d.P / 8)) * kLoadUnroll;
+        gx = std::max<int64_t>(gx, (d.n_pages + block - 1) / block);
     }
-    const dim3 grid((unsigned)gx, (unsigned)std::min(n_jobs, kLoadMaxJobsY));
+    const int64_t items = (int64_t)n_jobs * gx;
+    const dim3 grid((unsigned)std::min<int64_t>(items, kLoadWorkgroups));
     hipLaunchKernelGGL(lora_pool_scatter_kernel, grid, dim3(kLoadThreads), 0, s,
-                       static_cast<const unsigned char *>(staging), n_jobs);
+                       static_cast<const unsigned char *>(staging), n_jobs, gx);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(LORA_E_HIP, "pool load launch: %s", hipGetErrorString(e));
     return LORA_OK;
