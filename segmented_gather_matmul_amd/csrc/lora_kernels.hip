@@ -388,13 +388,14 @@ __device__ void derive_tile(const TileSrc &ts, int n_rows, int t)
 }
 
 // Every segment-form kernel calls this first (all threads, after uniform early exits):
-// in the offsets form it finds the workgroup's tile; with a tile list it does nothing.
-template <bool PERROW, int NT>
+// in the offsets form (OFFS) it finds the workgroup's tile; with a tile list it does
+// nothing.  The two forms are separate kernel instances: the scan's barriers, even in a
+// branch a tile-list launch never takes, keep the compiler from moving the kernel's first
+// loads ahead of it (the paged 70B layer measured 8 % slower with one instance for both).
+template <bool PERROW, bool OFFS, int NT>
 __device__ inline void prepare_tile(const TileSrc &ts, int n_rows, int t)
 {
-    if constexpr (!PERROW) {
-        if (!ts.tiles) derive_tile<NT>(ts, n_rows, t);
-    }
+    if constexpr (!PERROW && OFFS) derive_tile<NT>(ts, n_rows, t);
 }
 
 // ------------------------------------------------------------------------ common head
@@ -418,7 +419,7 @@ __device__ inline TileHead head_of(const lora_tile &tl, const WeightsDev &w)
     return th;
 }
 
-template <bool PERROW>
+template <bool PERROW, bool OFFS>
 __device__ inline TileHead tile_head(const TileSrc &ts, const WeightsDev &w, int t)
 {
     TileHead th;
@@ -428,7 +429,7 @@ __device__ inline TileHead tile_head(const TileSrc &ts, const WeightsDev &w, int
         th.nrows = 1;
     } else {
         lora_tile tl;
-        if (ts.tiles) {
+        if constexpr (!OFFS) {
             tl = ts.tiles[t];
         } else {
             // uniform over the workgroup: kept in scalar registers like the tile list's
@@ -587,7 +588,7 @@ enum class VSink { Global, Lds, Handoff };
 // DH: halves of octet pairs in flight together (0: about 16 loads per lane); it changes
 // the batching of the loads, not the order of any sum.  only_rg >= 0: only the pass over
 // the tile's rows [only_rg, only_rg + NR).
-template <bool PAGED, bool PERROW, int RJ, int NR, VSink SINK, int DH = 0>
+template <bool PAGED, bool PERROW, int RJ, int NR, VSink SINK, int DH = 0, bool OFFS = false>
 __device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *red, int *pcache, float *vlds,
                                         int only_rg = -1, bool use_known = false, lora_tile known = lora_tile{})
 {
@@ -596,7 +597,7 @@ __device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *re
     const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
     const int j0 = it.slice * a.jw;
     const int jend = min(j0 + a.jw, pd.w.r_max);
-    const TileHead th = use_known ? head_of(known, pd.w) : tile_head<PERROW>(a.ts, pd.w, it.tile);
+    const TileHead th = use_known ? head_of(known, pd.w) : tile_head<PERROW, OFFS>(a.ts, pd.w, it.tile);
     if (!th.valid || j0 >= jend) return false;
     const int rank = slot_rank(pd.w, th.slot);
     const int jload = PAGED ? min(jend, rank) : jend;
@@ -662,7 +663,7 @@ __device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *re
     return rank > 0;
 }
 
-template <bool PAGED, bool PERROW, int RJ, int NR>
+template <bool PAGED, bool PERROW, int RJ, int NR, bool OFFS>
 __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args args)
 {
     const Args &a = kernel_args<!PAGED>(args);
@@ -670,8 +671,8 @@ __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args args)
     __shared__ int pcache[PAGED ? kPageCache : 1];
     const Item it = work(a);
     if (!it.ok) return;
-    prepare_tile<PERROW, kThreads>(a.ts, a.n_rows, it.tile);
-    shrink_valu_item<PAGED, PERROW, RJ, NR, VSink::Global>(a, it, red, pcache, nullptr);
+    prepare_tile<PERROW, OFFS, kThreads>(a.ts, a.n_rows, it.tile);
+    shrink_valu_item<PAGED, PERROW, RJ, NR, VSink::Global, 0, OFFS>(a, it, red, pcache, nullptr);
 }
 
 // Rank slices of an MFMA shrink workgroup: slices g0 .. g0 + NS - 1 of the launch's
@@ -740,7 +741,7 @@ __device__ inline void mfma_shrink_store(const Args &a, const TileHead &th, cons
 // k-steps, U of them in flight each, and their sums are added in LDS in wavefront
 // order, one rank slice at a time.  Neither NS nor MTX changes the order in which any
 // element is summed, so every split gives the same bits.
-template <bool PAGED, int MTX, int NS>
+template <bool PAGED, int MTX, int NS, bool OFFS>
 __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Args args)
 {
     const Args &a = kernel_args<!PAGED>(args);
@@ -753,8 +754,8 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_kernel(Ar
     const int groups = (a.per_tile + NS - 1) / NS;
     const int tile = wi / groups, g0 = (wi - tile * groups) * NS;
     if (tile >= a.n_tiles) return;
-    prepare_tile<false, kMfmaShrinkThreads>(a.ts, a.n_rows, tile);
-    const TileHead th = tile_head<false>(a.ts, a.p[0].w, tile);
+    prepare_tile<false, OFFS, kMfmaShrinkThreads>(a.ts, a.n_rows, tile);
+    const TileHead th = tile_head<false, OFFS>(a.ts, a.p[0].w, tile);
     if (th.slot < 0 || th.nrows <= 0) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;       // operand row/col, k-group of the lane
@@ -865,7 +866,7 @@ __device__ inline void stage_load(const uint16_t *const (&src)[RPW], int k, int 
     for (int i = 0; i < RPW; ++i) st[i] = (src[i] && k < d_in) ? load16(src[i] + k) : z4;
 }
 
-template <int MTX, int NS, int RB>
+template <int MTX, int NS, int RB, bool OFFS>
 __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_kernel(Args args)
 {
     const Args &a = kernel_args<true>(args);
@@ -881,8 +882,8 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_ke
     const int tile = wi / (groups * RB), rem = wi - tile * (groups * RB);
     const int b = RB == 1 ? 0 : rem / groups, g0 = (rem - b * groups) * NS;
     if (tile >= a.n_tiles) return;
-    prepare_tile<false, kMfmaShrinkThreads>(a.ts, a.n_rows, tile);
-    const TileHead th = tile_head<false>(a.ts, a.p[0].w, tile);
+    prepare_tile<false, OFFS, kMfmaShrinkThreads>(a.ts, a.n_rows, tile);
+    const TileHead th = tile_head<false, OFFS>(a.ts, a.p[0].w, tile);
     if (th.slot < 0 || th.nrows <= 0) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
@@ -1100,7 +1101,7 @@ __device__ inline void expand_pass(const ProjDev &pd, const ExpandPass<PERROW, N
 template <bool PAGED, int NR, int RU>
 constexpr int expand_valu_waves() { return PAGED && NR == 4 && RU == 16 ? 1 : 4; }
 
-template <bool PAGED, bool PERROW, int NR, int RU>
+template <bool PAGED, bool PERROW, int NR, int RU, bool OFFS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(expand_valu_waves<PAGED, NR, RU>())))
 void lora_expand_valu_kernel(Args args)
 {
@@ -1108,9 +1109,9 @@ void lora_expand_valu_kernel(Args args)
     __shared__ float red[kWaves * NR * 8 * 64];
     const Item it = work_by_slice(a);
     if (!it.ok) return;
-    prepare_tile<PERROW, kThreads>(a.ts, a.n_rows, it.tile);
+    prepare_tile<PERROW, OFFS, kThreads>(a.ts, a.n_rows, it.tile);
     const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
-    const TileHead th = tile_head<PERROW>(a.ts, pd.w, it.tile);
+    const TileHead th = tile_head<PERROW, OFFS>(a.ts, pd.w, it.tile);
     if (!th.valid) return;
     const int rank = slot_rank(pd.w, th.slot);
     const int jlim = PAGED ? rank : pd.w.r_max;
@@ -1238,7 +1239,7 @@ constexpr int kHandoffArgsOffset = 24;  // byte offset of the argument block aft
                                         // leading arguments (8 + 3 * 4 bytes, 8-byte aligned)
 static_assert(alignof(Args) == 8, "argument block alignment");
 
-template <bool PAGED, bool PERROW, int RJ, int NR, int RU>
+template <bool PAGED, bool PERROW, int RJ, int NR, int RU, bool OFFS>
 __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(const void *__restrict__ pre_src, int32_t pre_n_shrink,
                                                                 int32_t pre_per_tile, int32_t pre_e_per_tile, Args args)
 {
@@ -1269,16 +1270,15 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(const void *__re
     const Item it = tile_item(shrink ? b : b - a.ho.n_shrink, shrink ? a.per_tile : a.ho.e_per_tile, off, a.n_proj,
                               a.n_tiles);
     if (!it.ok) return;
-    prepare_tile<PERROW, kThreads>(a.ts, a.n_rows, it.tile);
+    prepare_tile<PERROW, OFFS, kThreads>(a.ts, a.n_rows, it.tile);
     if (shrink) {
-        const bool stored =
-            shrink_valu_item<PAGED, PERROW, RJ, NR, VSink::Handoff, kDH>(a, it, red, pcache, nullptr, -1, have_early,
-                                                                         early);
+        const bool stored = shrink_valu_item<PAGED, PERROW, RJ, NR, VSink::Handoff, kDH, OFFS>(
+            a, it, red, pcache, nullptr, -1, have_early, early);
         // wavefront 0 made every v store of this workgroup
         if (stored && wave == 0) {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the hand-off stores have completed
             const ProjDev &pd = a.p[it.p];
-            const TileHead th = have_early ? head_of(early, pd.w) : tile_head<PERROW>(a.ts, pd.w, it.tile);
+            const TileHead th = have_early ? head_of(early, pd.w) : tile_head<PERROW, OFFS>(a.ts, pd.w, it.tile);
             for (int rg = 0; rg < th.nrows; rg += NR) {
                 int rows[NR];
                 tile_rows<PERROW, NR>(a, th, rg, rows);
@@ -1288,7 +1288,7 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(const void *__re
         return;
     }
     const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
-    const TileHead th = have_early ? head_of(early, pd.w) : tile_head<PERROW>(a.ts, pd.w, it.tile);
+    const TileHead th = have_early ? head_of(early, pd.w) : tile_head<PERROW, OFFS>(a.ts, pd.w, it.tile);
     if (!th.valid) return;
     const int rank = slot_rank(pd.w, th.slot);
     const int jlim = PAGED ? rank : pd.w.r_max;
@@ -1302,7 +1302,7 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(const void *__re
         for (int r = 0; r < th.nrows; ++r) {
             for (int sl = 0; sl < a.p[it.p].slices; ++sl) {
                 const Item si{it.tile, it.p, sl, true};
-                shrink_valu_item<PAGED, PERROW, 1, 1, VSink::Lds, 2>(a, si, red, pcache, &vrow[0][0], r, have_early,
+                shrink_valu_item<PAGED, PERROW, 1, 1, VSink::Lds, 2, OFFS>(a, si, red, pcache, &vrow[0][0], r, have_early,
                                                                      early);
             }
             ExpandPass<PERROW, 1> ps;
@@ -1358,7 +1358,7 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(const void *__re
                 const Item si{it.tile, it.p, sl, true};
                 // one rank-row and one pair of halves at a time: few registers on a path
                 // that only runs when the poll limit runs out
-                shrink_valu_item<PAGED, PERROW, 1, NR, VSink::Lds, 2>(a, si, red, pcache, &vrow[0][0], 0, have_early,
+                shrink_valu_item<PAGED, PERROW, 1, NR, VSink::Lds, 2, OFFS>(a, si, red, pcache, &vrow[0][0], 0, have_early,
                                                                       early);
             }
         }
@@ -1387,7 +1387,7 @@ constexpr int kYStride = kCols + 8;  // halves per row of the staged y slice (th
 
 __host__ __device__ constexpr int bt_stride(int rq) { return 16 * rq + kBtPad; }
 
-template <bool PAGED, int RQ, bool SY>
+template <bool PAGED, int RQ, bool SY, bool OFFS>
 __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args args)
 {
     const Args &a = kernel_args<!PAGED>(args);
@@ -1398,9 +1398,9 @@ __global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args args)
     uint16_t *ys = bt + kCols * KS;                      // SY: y of the slice, [16][kYStride]
     const Item it = work(a);
     if (!it.ok) return;
-    prepare_tile<false, kThreads>(a.ts, a.n_rows, it.tile);
+    prepare_tile<false, OFFS, kThreads>(a.ts, a.n_rows, it.tile);
     const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
-    const TileHead th = tile_head<false>(a.ts, pd.w, it.tile);
+    const TileHead th = tile_head<false, OFFS>(a.ts, pd.w, it.tile);
     if (!th.valid) return;
     const int rank = slot_rank(pd.w, th.slot);
     const float sc = pd.w.scale[th.slot];
@@ -1782,31 +1782,32 @@ int rows_per_pass(int32_t max_rows)
     return max_rows <= 1 ? 1 : max_rows <= 2 ? 2 : kRowsPerPass;
 }
 
-template <bool PERROW, int NR>
+template <bool PERROW, int NR, bool OFFS>
 void shrink_valu_launch(bool paged, int32_t jw, dim3 grid, hipStream_t s, const Args &a)
 {
-#define LORA_SHRINK_VALU(RJ)                                                                   \
-    (paged ? launch(lora_shrink_valu_kernel<true, PERROW, RJ, NR>, grid, kThreads, 0, s, a)   \
-           : launch(lora_shrink_valu_kernel<false, PERROW, RJ, NR>, grid, kThreads, 0, s, a))
+#define LORA_SHRINK_VALU(RJ)                                                                         \
+    (paged ? launch(lora_shrink_valu_kernel<true, PERROW, RJ, NR, OFFS>, grid, kThreads, 0, s, a)   \
+           : launch(lora_shrink_valu_kernel<false, PERROW, RJ, NR, OFFS>, grid, kThreads, 0, s, a))
     if (jw == 1) LORA_SHRINK_VALU(1);
     else if (jw == 2) LORA_SHRINK_VALU(2);
     else LORA_SHRINK_VALU(4);
 #undef LORA_SHRINK_VALU
 }
 
-template <bool PERROW, int NR>
+template <bool PERROW, int NR, bool OFFS>
 void expand_valu_launch(bool paged, int32_t r_max, dim3 grid, hipStream_t s, const Args &a)
 {
-#define LORA_EXPAND_VALU(RU)                                                                  \
-    (paged ? launch(lora_expand_valu_kernel<true, PERROW, NR, RU>, grid, kThreads, 0, s, a)  \
-           : launch(lora_expand_valu_kernel<false, PERROW, NR, RU>, grid, kThreads, 0, s, a))
+#define LORA_EXPAND_VALU(RU)                                                                        \
+    (paged ? launch(lora_expand_valu_kernel<true, PERROW, NR, RU, OFFS>, grid, kThreads, 0, s, a)  \
+           : launch(lora_expand_valu_kernel<false, PERROW, NR, RU, OFFS>, grid, kThreads, 0, s, a))
     if (r_max <= 16) LORA_EXPAND_VALU(4);
     else if (r_max <= 32) LORA_EXPAND_VALU(8);
     else LORA_EXPAND_VALU(16);
 #undef LORA_EXPAND_VALU
 }
 
-template <bool PERROW>
+// OFFS: the segment form given as offsets (each workgroup derives its tile).
+template <bool PERROW, bool OFFS = false>
 int shrink_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSrc ts, int32_t n_tiles,
                 int32_t max_rows, int32_t n_proj, const lora_proj *proj)
 {
@@ -1849,11 +1850,11 @@ int shrink_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSr
         a.grid = pad8((int64_t)n_tiles * rb * ((a.per_tile + ns - 1) / ns));
         const dim3 g((unsigned)a.grid);
 #define LORA_SHRINK_STAGED(MTX, NS) \
-    launch(lora_shrink_mfma_staged_kernel<MTX, NS, 1>, g, kMfmaShrinkThreads, stage_lds_bytes(MTX, NS), s, a)
+    launch(lora_shrink_mfma_staged_kernel<MTX, NS, 1, OFFS>, g, kMfmaShrinkThreads, stage_lds_bytes(MTX, NS), s, a)
         if (paged) {
-            if (mtx <= 1) launch(lora_shrink_mfma_kernel<true, 1, 1>, g, kMfmaShrinkThreads, 0, s, a);
-            else if (mtx == 2) launch(lora_shrink_mfma_kernel<true, 2, 1>, g, kMfmaShrinkThreads, 0, s, a);
-            else launch(lora_shrink_mfma_kernel<true, 4, 1>, g, kMfmaShrinkThreads, 0, s, a);
+            if (mtx <= 1) launch(lora_shrink_mfma_kernel<true, 1, 1, OFFS>, g, kMfmaShrinkThreads, 0, s, a);
+            else if (mtx == 2) launch(lora_shrink_mfma_kernel<true, 2, 1, OFFS>, g, kMfmaShrinkThreads, 0, s, a);
+            else launch(lora_shrink_mfma_kernel<true, 4, 1, OFFS>, g, kMfmaShrinkThreads, 0, s, a);
         } else if (mtx <= 1) {
             if (ns == 1) LORA_SHRINK_STAGED(1, 1);
             else if (ns == 2) LORA_SHRINK_STAGED(1, 2);
@@ -1865,7 +1866,7 @@ int shrink_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSr
             else if (ns == 3) LORA_SHRINK_STAGED(2, 3);
             else LORA_SHRINK_STAGED(2, 4);
         } else if (rb == 4) {
-            launch(lora_shrink_mfma_staged_kernel<1, 1, 4>, g, kMfmaShrinkThreads, stage_lds_bytes(1, 1), s, a);
+            launch(lora_shrink_mfma_staged_kernel<1, 1, 4, OFFS>, g, kMfmaShrinkThreads, stage_lds_bytes(1, 1), s, a);
         } else {
             if (ns == 1) LORA_SHRINK_STAGED(4, 1);
             else if (ns == 2) LORA_SHRINK_STAGED(4, 2);
@@ -1873,17 +1874,17 @@ int shrink_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSr
         }
 #undef LORA_SHRINK_STAGED
     } else if constexpr (PERROW) {
-        shrink_valu_launch<true, 1>(paged, a.jw, grid, s, a);
+        shrink_valu_launch<true, 1, false>(paged, a.jw, grid, s, a);
     } else {
         const int nr = rows_per_pass(max_rows);
-        if (nr == 1) shrink_valu_launch<false, 1>(paged, a.jw, grid, s, a);
-        else if (nr == 2) shrink_valu_launch<false, 2>(paged, a.jw, grid, s, a);
-        else shrink_valu_launch<false, 4>(paged, a.jw, grid, s, a);
+        if (nr == 1) shrink_valu_launch<false, 1, OFFS>(paged, a.jw, grid, s, a);
+        else if (nr == 2) shrink_valu_launch<false, 2, OFFS>(paged, a.jw, grid, s, a);
+        else shrink_valu_launch<false, 4, OFFS>(paged, a.jw, grid, s, a);
     }
     return launch_status("shrink");
 }
 
-template <bool PERROW>
+template <bool PERROW, bool OFFS = false>
 int expand_impl(void *stream, int32_t n_rows, TileSrc ts, int32_t n_tiles, int32_t max_rows, int32_t n_proj,
                 const lora_proj *proj)
 {
@@ -1908,20 +1909,20 @@ int expand_impl(void *stream, int32_t n_rows, TileSrc ts, int32_t n_tiles, int32
         const size_t lds = (size_t)kCols * bt_stride(rq) * sizeof(uint16_t);
         const size_t lds_sy = lds + (size_t)16 * kYStride * sizeof(uint16_t);  // dense: plus the staged y slice
 #define LORA_EXPAND_MFMA(RQ)                                                                 \
-    (paged ? launch(lora_expand_mfma_kernel<true, RQ, false>, grid, kThreads, lds, s, a)     \
-           : launch(lora_expand_mfma_kernel<false, RQ, true>, grid, kThreads, lds_sy, s, a))
+    (paged ? launch(lora_expand_mfma_kernel<true, RQ, false, OFFS>, grid, kThreads, lds, s, a)     \
+           : launch(lora_expand_mfma_kernel<false, RQ, true, OFFS>, grid, kThreads, lds_sy, s, a))
         if (rq == 1) LORA_EXPAND_MFMA(1);
         else if (rq == 2) LORA_EXPAND_MFMA(2);
         else if (rq == 3) LORA_EXPAND_MFMA(3);
         else LORA_EXPAND_MFMA(4);
 #undef LORA_EXPAND_MFMA
     } else if constexpr (PERROW) {
-        expand_valu_launch<true, 1>(paged, r_max, grid, s, a);
+        expand_valu_launch<true, 1, false>(paged, r_max, grid, s, a);
     } else {
         const int nr = rows_per_pass(max_rows);
-        if (nr == 1) expand_valu_launch<false, 1>(paged, r_max, grid, s, a);
-        else if (nr == 2) expand_valu_launch<false, 2>(paged, r_max, grid, s, a);
-        else expand_valu_launch<false, 4>(paged, r_max, grid, s, a);
+        if (nr == 1) expand_valu_launch<false, 1, OFFS>(paged, r_max, grid, s, a);
+        else if (nr == 2) expand_valu_launch<false, 2, OFFS>(paged, r_max, grid, s, a);
+        else expand_valu_launch<false, 4, OFFS>(paged, r_max, grid, s, a);
     }
     return launch_status("expand");
 }
@@ -1951,7 +1952,7 @@ int check_workspace(const void *work, size_t work_bytes, int32_t n_rows)
 // max_rows rows (the per-row form: one row per tile).  Arguments other than the
 // workspace are checked by the caller; the segment form comes here with dense weights
 // and tiles of fewer than kMfmaMinRows rows only.
-template <bool PERROW>
+template <bool PERROW, bool OFFS = false>
 int handoff_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSrc ts, int32_t n_tiles,
                  int32_t max_rows, int32_t n_proj, const lora_proj *proj, Args &a, bool paged, void *work,
                  size_t work_bytes)
@@ -1996,13 +1997,13 @@ int handoff_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileS
     const void *pre_src = PERROW ? static_cast<const void *>(ts.idx) : static_cast<const void *>(ts.tiles);
 #define LORA_HANDOFF_RU(PG, RJ, NR)                                                                              \
     if (r_max <= 16)                                                                                             \
-        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 4>, grid, kThreads, 0, s, pre_src, a.ho.n_shrink,    \
+        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 4, OFFS>, grid, kThreads, 0, s, pre_src, a.ho.n_shrink,    \
                    a.per_tile, a.ho.e_per_tile, a);                                                              \
     else if (r_max <= 32)                                                                                        \
-        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 8>, grid, kThreads, 0, s, pre_src, a.ho.n_shrink,    \
+        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 8, OFFS>, grid, kThreads, 0, s, pre_src, a.ho.n_shrink,    \
                    a.per_tile, a.ho.e_per_tile, a);                                                              \
     else                                                                                                         \
-        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 16>, grid, kThreads, 0, s, pre_src, a.ho.n_shrink,   \
+        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 16, OFFS>, grid, kThreads, 0, s, pre_src, a.ho.n_shrink,   \
                    a.per_tile, a.ho.e_per_tile, a)
 #define LORA_HANDOFF_JW(PG, NR)                      \
     if (a.jw == 1) { LORA_HANDOFF_RU(PG, 1, NR); }    \
@@ -2127,7 +2128,8 @@ int lora_sgmv_shrink_multi(void *stream, const void *x, int64_t ldx, int32_t n_r
     SegLaunch sl;
     int st = check_segments(seg);
     if (st || (st = seg_launch(seg, n_rows, sl))) return st;
-    return shrink_impl<false>(stream, x, ldx, n_rows, sl.ts, sl.n_tiles, sl.max_rows, n_proj, proj);
+    return sl.ts.tiles ? shrink_impl<false, false>(stream, x, ldx, n_rows, sl.ts, sl.n_tiles, sl.max_rows, n_proj, proj)
+                       : shrink_impl<false, true>(stream, x, ldx, n_rows, sl.ts, sl.n_tiles, sl.max_rows, n_proj, proj);
 }
 
 int lora_sgmv_expand_multi(void *stream, int32_t n_rows, const lora_segments *seg, int32_t n_proj,
@@ -2137,7 +2139,8 @@ int lora_sgmv_expand_multi(void *stream, int32_t n_rows, const lora_segments *se
     SegLaunch sl;
     int st = check_segments(seg);
     if (st || (st = seg_launch(seg, n_rows, sl))) return st;
-    return expand_impl<false>(stream, n_rows, sl.ts, sl.n_tiles, sl.max_rows, n_proj, proj);
+    return sl.ts.tiles ? expand_impl<false, false>(stream, n_rows, sl.ts, sl.n_tiles, sl.max_rows, n_proj, proj)
+                       : expand_impl<false, true>(stream, n_rows, sl.ts, sl.n_tiles, sl.max_rows, n_proj, proj);
 }
 
 int lora_bgmv_shrink_multi(void *stream, const void *x, int64_t ldx, const int32_t *idx, int32_t n_rows,
@@ -2270,12 +2273,18 @@ int lora_sgmv_multi_handoff(void *stream, const void *x, int64_t ldx, int32_t n_
     if (paged || max_rows >= kMfmaMinRows) {
         // the two launches: the MFMA kernels' tiles and paged weights hand nothing off
         if ((st = check_workspace(work, work_bytes, n_rows))) return st;
-        st = shrink_impl<false>(stream, x, ldx, n_rows, sl.ts, sl.n_tiles, max_rows, n_proj, proj);
-        if (st) return st;
-        return expand_impl<false>(stream, n_rows, sl.ts, sl.n_tiles, max_rows, n_proj, proj);
+        if (sl.ts.tiles) {
+            st = shrink_impl<false, false>(stream, x, ldx, n_rows, sl.ts, sl.n_tiles, max_rows, n_proj, proj);
+            return st ? st : expand_impl<false, false>(stream, n_rows, sl.ts, sl.n_tiles, max_rows, n_proj, proj);
+        }
+        st = shrink_impl<false, true>(stream, x, ldx, n_rows, sl.ts, sl.n_tiles, max_rows, n_proj, proj);
+        return st ? st : expand_impl<false, true>(stream, n_rows, sl.ts, sl.n_tiles, max_rows, n_proj, proj);
     }
-    return handoff_impl<false>(stream, x, ldx, n_rows, sl.ts, sl.n_tiles, max_rows, n_proj, proj, a, paged,
-                               work, work_bytes);
+    if (sl.ts.tiles)
+        return handoff_impl<false, false>(stream, x, ldx, n_rows, sl.ts, sl.n_tiles, max_rows, n_proj, proj, a, paged,
+                                          work, work_bytes);
+    return handoff_impl<false, true>(stream, x, ldx, n_rows, sl.ts, sl.n_tiles, max_rows, n_proj, proj, a, paged,
+                                     work, work_bytes);
 }
 
 int lora_set_handoff_polls(int32_t polls)
