@@ -617,11 +617,15 @@ def load_sweep(args):
         torch.cuda.synchronize()
         step_ms = e0.elapsed_time(e1) / reps
         def step_during(fn, per_ms):
-            """Decode step time while `fn` runs back to back on the side stream."""
-            e0.record()
+            """Decode step time while `fn` runs back to back on the side stream.  The side
+            work is queued first (twice what the replays take, since some of it runs while
+            the host is still queueing) and the timed window opens after it, so that the
+            host's own time in `fn` (argument checks, the job table) is not counted as a
+            slower decode step."""
             with torch.cuda.stream(side):
-                for _ in range(max(1, int(reps * step_ms / max(per_ms, 1e-3)))):
+                for _ in range(max(2, int(2 * reps * step_ms / max(per_ms, 1e-3)) + 1)):
                     fn()
+            e0.record()
             for _ in range(reps):
                 g.replay()
             e1.record()
@@ -631,12 +635,43 @@ def load_sweep(args):
 
         step_ms_loaded = step_during(lambda: B.lora_pool_load(jobs, blob, staging, stream=side), load_ms)
         step_ms_copies = step_during(lambda: staging.copy_(blob, non_blocking=True), copy_ms)
+        # the same copies, each followed by a trivial kernel on the side stream (a 4 KiB fill)
+        tiny = torch.empty(1024, dtype=torch.int32, device=dev)
+        step_ms_copies_kernel = step_during(lambda: (staging.copy_(blob, non_blocking=True), tiny.fill_(1)), copy_ms)
+
+        def step_paced(fn, every):
+            """Decode step time in a host loop that keeps at most two steps queued (it waits
+            for step i-1 once step i is queued) and issues `fn` on the side stream after
+            every `every`-th step, so loads start as the decode reaches them and never queue
+            behind one another (fn=None: the same loop without loads)."""
+            evs = [torch.cuda.Event() for _ in range(reps)]
+            e0.record()
+            for i in range(reps):
+                g.replay()
+                evs[i].record()
+                if i >= 1:
+                    evs[i - 1].synchronize()
+                if fn is not None and i % every == 0:
+                    with torch.cuda.stream(side):
+                        fn()
+            e1.record()
+            torch.cuda.synchronize()
+            side.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        every = int(np.ceil(load_ms / step_ms)) + 1
+        step_ms_paced_alone = step_paced(None, every)
+        step_ms_paced = step_paced(lambda: B.lora_pool_load(jobs, blob, staging, stream=side), every)
         rec = dict(models=models, jobs=len(jobs), weight_bytes=weight_bytes, blob_bytes=int(blob.numel()),
                    load_ms=round(load_ms, 4), load_gbs=round(weight_bytes / (load_ms * 1e-3) / 1e9, 2),
                    ms_per_model=round(load_ms / models, 4), h2d_copy_ms=round(copy_ms, 4),
                    h2d_copy_gbs=round(blob.numel() / (copy_ms * 1e-3) / 1e9, 2),
                    decode_step_ms=round(step_ms, 4), decode_step_ms_during_loads=round(step_ms_loaded, 4),
-                   decode_step_ms_during_copies=round(step_ms_copies, 4))
+                   decode_step_ms_during_copies=round(step_ms_copies, 4),
+                   decode_step_ms_during_copies_and_fills=round(step_ms_copies_kernel, 4),
+                   paced_every_steps=every, decode_step_ms_paced_alone=round(step_ms_paced_alone, 4),
+                   decode_step_ms_paced_loads=round(step_ms_paced, 4),
+                   paced_load_gbs=round(weight_bytes / (every * step_ms_paced * 1e-3) / 1e9, 2))
         log(f"[load] {rec}")
         out["results"].append(rec)
         del pool, staging, blob, targets, ads

@@ -373,8 +373,10 @@ int lora_sgmv_multi_handoff(void *stream, const void *x, int64_t ldx, int32_t n_
  *
  * Free-page list.  Its state lives in caller-owned host memory of
  * lora_pool_state_bytes(num_pages) bytes (the library keeps none).  lora_pool_alloc
- * hands out the most recently returned pages first.  Neither call is thread-safe on
- * one state.
+ * hands out the pages of the most recent lora_pool_release first, in the order that
+ * call listed them (a fresh list hands out 0, 1, 2, ...), so pages taken and returned
+ * in runs of consecutive ids come back as the same runs.  Neither call is thread-safe
+ * on one state.
  */
 size_t lora_pool_state_bytes(int64_t num_pages);
 int lora_pool_init(void *state, size_t state_bytes, int64_t num_pages);  /* num_pages in 1..2^31-1 */
@@ -407,13 +409,19 @@ typedef struct lora_load_job {
 size_t lora_pool_load_header_bytes(int32_t n_jobs);
 
 /*
- * Places n_jobs adapters with one host-to-device copy and one kernel, in order on
- * `stream`:
+ * Places n_jobs adapters, in order on `stream`:
  *   1. writes the job table into blob[0 .. lora_pool_load_header_bytes(n_jobs));
- *   2. copies blob[0 .. blob_bytes) into staging (device, >= blob_bytes bytes, 16-byte
- *      aligned; it must not be reused before the kernel has finished);
- *   3. writes every job's rank-rows into its pages (A^T rank-row j, page q <- elements
- *      q*P .. q*P+P-1), page_table[pt_off + e] <- the page ids, and the slot's
+ *   2. copies blob to staging (device, >= blob_bytes bytes, 16-byte aligned; it must not
+ *      be reused before the load's kernel has finished) and the rank-rows into their
+ *      pages (A^T rank-row j, page q <- elements q*P .. q*P+P-1), by one of two routes:
+ *      - direct, when every page-id list lies before every job's rank-rows in the blob
+ *        and the call's pages form at most 64 runs (consecutive pages of the blob to
+ *        consecutive ids of one pool, across jobs too): blob[0 .. end of the last
+ *        page-id list) goes to staging and each run host-to-device straight into its
+ *        pool pages, by the copy engine;
+ *      - staged, otherwise: all of blob goes to staging, and the kernel of step 3 also
+ *        copies every page from there;
+ *   3. one kernel writes page_table[pt_off + e] <- the page ids, and the slot's
  *      a_pt_off = pt_off, b_pt_off = pt_off + rank*d_in/P, rank and scale.
  * blob: host memory, 16-byte aligned, page-locked (hipHostMalloc) for the copy to be
  * asynchronous; it must stay unchanged until the copy has completed.  Every argument is

@@ -714,6 +714,9 @@ def pack_adapters(adapters, pinned=True):
     off = int(lib().lora_pool_load_header_bytes(n))
     jobs = (CLoadJob * n)()
     parts = []
+    # the job table, then every page-id list, then every job's rank-rows back to back (the
+    # layout lora_pool_load's direct route takes: consecutive pages become one copy)
+    datas = []
     for i, ad in enumerate(adapters):
         j = jobs[i]
         j.w = ctypes.addressof(ad["w"].c)
@@ -721,15 +724,16 @@ def pack_adapters(adapters, pinned=True):
         j.pt_off = int(ad.get("pt_off", 0))
         if ad["rank"] == 0:
             continue
-        data = np.concatenate([np.ascontiguousarray(ad["a_t"], np.float16).ravel(),
-                               np.ascontiguousarray(ad["b"], np.float16).ravel()]).view(np.uint8)
         ids = np.ascontiguousarray(ad["pages"], np.int32).view(np.uint8)
-        j.data_off = off
-        parts.append((off, data))
-        off = -(-(off + len(data)) // 16) * 16
         j.pages_off = off
         parts.append((off, ids))
         off = -(-(off + len(ids)) // 16) * 16
+        datas.append((j, np.concatenate([np.ascontiguousarray(ad["a_t"], np.float16).ravel(),
+                                         np.ascontiguousarray(ad["b"], np.float16).ravel()]).view(np.uint8)))
+    for j, data in datas:
+        j.data_off = off
+        parts.append((off, data))
+        off = -(-(off + len(data)) // 16) * 16
     blob = torch.zeros(max(off, 16), dtype=torch.uint8, pin_memory=pinned)
     view = blob.numpy()
     for o, d in parts:

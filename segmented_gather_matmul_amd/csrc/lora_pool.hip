@@ -3,10 +3,15 @@
 // I/O with Computation"; Punica summary, "On-Demand LoRA Weight Loading").
 //
 // Pages all hold P fp16 elements, so allocation is a stack of page ids and never
-// fragments.  Loading is one host-to-device copy of a caller-packed blob (job table,
-// rank-rows, page ids) into a staging buffer, then one kernel with a small fixed grid that
-// scatters every page, writes its page-table entry and sets each slot's rank, scale and
-// offsets.
+// fragments.  Loading takes one of two routes:
+//   direct: when the adapters' pages form few runs of consecutive ids (a fresh pool, or
+//     pages released and taken again in order) and the blob holds its job table and page
+//     ids ahead of all rank-rows, the rank-rows go host-to-device straight into the pool,
+//     one copy per run (the copy engine; no kernel reads or writes them), and only the
+//     job table and page ids go to the staging buffer for a small kernel that writes the
+//     page-table entries and each slot's rank, scale and offsets;
+//   staged: otherwise one host-to-device copy of the whole blob into the staging buffer,
+//     then one kernel with a small fixed grid that scatters every page as well.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -69,6 +74,35 @@ constexpr int kLoadUnroll = 8;        // pages per lane group per work item (loa
 #define LORA_LOAD_WORKGROUPS 1024
 #endif
 constexpr int kLoadWorkgroups = LORA_LOAD_WORKGROUPS;  // the scatter's grid: four workgroups per CU
+
+constexpr int kMetaWorkgroups = 256;  // the direct route's kernel: page-table entries and slot fields only
+constexpr size_t kDirectRuns = 64;    // most runs of consecutive pages the direct route copies one by one
+
+// The direct route's kernel (the pages are already in place): work item f (of n_jobs *
+// gx) is job f / gx, entries [256 (f % gx), 256 (f % gx) + 256) of its page-table range,
+// one per thread; the first item of a job also writes the slot's rank, scale and
+// page-table offsets.
+__global__ __launch_bounds__(kLoadThreads) void lora_pool_meta_kernel(const unsigned char *staging, int32_t n_jobs,
+                                                                      int64_t gx)
+{
+    const LoadJobDev *jobs = reinterpret_cast<const LoadJobDev *>(staging);
+    const int tid = threadIdx.x;
+    for (int64_t f = blockIdx.x; f < (int64_t)n_jobs * gx; f += gridDim.x) {
+        const int64_t jx = f / gx, bx = f - jx * gx;
+        const LoadJobDev &jb = jobs[jx];
+        if (bx == 0 && tid == 0) {
+            jb.rank[jb.slot] = jb.r;
+            if (jb.r > 0) {
+                jb.scale[jb.slot] = jb.sc;
+                jb.a_pt_off[jb.slot] = jb.pt_off;
+                jb.b_pt_off[jb.slot] = jb.pt_off + (int64_t)jb.r * (jb.d_in / jb.P);
+            }
+        }
+        const int64_t e = bx * kLoadThreads + tid;
+        if (e < jb.n_pages)
+            jb.page_table[jb.pt_off + e] = reinterpret_cast<const int32_t *>(staging + jb.pages_off)[e];
+    }
+}
 
 // Work item f (of n_jobs * gx) is job f / gx, page block f % gx: kLoadUnroll groups of
 // ppw pages, each page copied by P/8 lanes (16 bytes per lane) or, for P > 2048, by the
@@ -207,8 +241,10 @@ int lora_pool_release(void *state, int32_t n, const int32_t *pages)
     for (int32_t i = 0; i < (bad < 0 ? n : bad); ++i) tk[pages[i]] = 1;
     if (bad >= 0)
         return fail(LORA_E_INDEX, "page %d (entry %d) is out of range, not taken, or listed twice", pages[bad], bad);
+    // pushed last to first: the next lora_pool_alloc hands them out in the order listed,
+    // so pages released in ascending runs come back as the same runs
     int32_t *st = stack_of(h);
-    for (int32_t i = 0; i < n; ++i) {
+    for (int32_t i = n - 1; i >= 0; --i) {
         tk[pages[i]] = 0;
         st[h->free_top++] = pages[i];
     }
@@ -343,22 +379,69 @@ int lora_pool_load(void *stream, int32_t n_jobs, const lora_load_job *jobs, void
         d.sc = jb.scale;
         table[i] = d;
     }
+    // The direct route's runs: page e of a job sits at data_off + e * 2P bytes of the blob
+    // (its rank-rows are contiguous) and goes to page ids[e] of its pool; consecutive
+    // pages extend a run while both sides stay contiguous, across jobs too.
+    struct Run {
+        unsigned char *dst;
+        int64_t src, bytes;
+    };
+    std::vector<Run> runs;
+    size_t meta_end = header;  // the job table and every page-id list end here ...
+    int64_t data_begin = (int64_t)blob_bytes;  // ... and must not reach into the rank-rows
+    bool direct = true;
+    for (int32_t i = 0; i < n_jobs && direct; ++i) {
+        const LoadJobDev &d = table[i];
+        if (d.n_pages == 0) continue;
+        meta_end = std::max(meta_end, (size_t)(d.pages_off + 4 * (int64_t)d.n_pages));
+        data_begin = std::min(data_begin, d.data_off);
+        const int32_t *ids = reinterpret_cast<const int32_t *>(bytes + d.pages_off);
+        const int64_t pb = 2 * (int64_t)d.P;
+        auto *pool = reinterpret_cast<unsigned char *>(d.pool);
+        for (int64_t e = 0; e < d.n_pages; ++e) {
+            unsigned char *dst = pool + (int64_t)ids[e] * pb;
+            const int64_t src = d.data_off + e * pb;
+            if (!runs.empty() && runs.back().dst + runs.back().bytes == dst && runs.back().src + runs.back().bytes == src) {
+                runs.back().bytes += pb;
+            } else if (runs.size() == kDirectRuns) {
+                direct = false;
+                break;
+            } else {
+                runs.push_back(Run{dst, src, pb});
+            }
+        }
+    }
+    direct = direct && (int64_t)meta_end <= data_begin;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(staging, blob, blob_bytes, hipMemcpyHostToDevice, s);
+    hipError_t e = hipMemcpyAsync(staging, blob, direct ? meta_end : blob_bytes, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return fail(LORA_E_HIP, "pool load copy: %s", hipGetErrorString(e));
-    // work items per job: enough page blocks for the job with the most pages
+    // work items per job: enough blocks (of pages, or of page-table entries on the direct
+    // route) for the job with the most pages
     int64_t gx = 1;
     for (int32_t i = 0; i < n_jobs; ++i) {
         const LoadJobDev &d = table[i];
-        const int64_t block = (int64_t)(kLoadThreads / std::min(kLoadThreads, d.P / 8)) * kLoadUnroll;
+        const int64_t block =
+            direct ? kLoadThreads : (int64_t)(kLoadThreads / std::min(kLoadThreads, d.P / 8)) * kLoadUnroll;
         gx = std::max<int64_t>(gx, (d.n_pages + block - 1) / block);
     }
     const int64_t items = (int64_t)n_jobs * gx;
-    const dim3 grid((unsigned)std::min<int64_t>(items, kLoadWorkgroups));
-    hipLaunchKernelGGL(lora_pool_scatter_kernel, grid, dim3(kLoadThreads), 0, s,
-                       static_cast<const unsigned char *>(staging), n_jobs, gx);
+    const dim3 grid((unsigned)std::min<int64_t>(items, direct ? kMetaWorkgroups : kLoadWorkgroups));
+    const auto *stg = static_cast<const unsigned char *>(staging);
+    // The direct route's kernel runs right after the small staging copy and before the
+    // rank-rows' copies: a kernel queued behind a long copy would hold its compute queue
+    // (and whatever else shares that queue) until the copy is done.  The page-table
+    // entries and slot fields may land before the pages; readers order themselves after
+    // the whole load anyway.
+    if (direct) hipLaunchKernelGGL(lora_pool_meta_kernel, grid, dim3(kLoadThreads), 0, s, stg, n_jobs, gx);
+    else hipLaunchKernelGGL(lora_pool_scatter_kernel, grid, dim3(kLoadThreads), 0, s, stg, n_jobs, gx);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(LORA_E_HIP, "pool load launch: %s", hipGetErrorString(e));
+    if (direct) {
+        for (const Run &r : runs) {
+            e = hipMemcpyAsync(r.dst, bytes + r.src, (size_t)r.bytes, hipMemcpyHostToDevice, s);
+            if (e != hipSuccess) return fail(LORA_E_HIP, "pool load copy: %s", hipGetErrorString(e));
+        }
+    }
     return LORA_OK;
 }
 

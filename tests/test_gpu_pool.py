@@ -182,3 +182,75 @@ def test_page_sizes(page_elems, d_in, d_out):
     dc = G.DeviceCase(x, y0, R_MAX)
     y, v = G.run_bgmv(w, dc, idx)
     G.check(dc, y, v, y_ref, v_ref, G.active_rows(idx, rank), f"pool-pages-{page_elems}")
+
+
+def _pack_data_first(adapters):
+    """A blob with each job's rank-rows before its page ids (valid for lora_pool_load, but
+    not the direct route's layout, so it takes the staged route)."""
+    import ctypes
+    import torch
+    n = len(adapters)
+    off = int(B.lib().lora_pool_load_header_bytes(n))
+    jobs = (B.CLoadJob * n)()
+    parts = []
+    for i, ad in enumerate(adapters):
+        j = jobs[i]
+        j.w = ctypes.addressof(ad["w"].c)
+        j.slot, j.rank, j.scale, j.reserved = int(ad["slot"]), int(ad["rank"]), float(ad["scale"]), 0
+        j.pt_off = int(ad["pt_off"])
+        data = np.concatenate([ad["a_t"].ravel(), ad["b"].ravel()]).astype(np.float16).view(np.uint8)
+        j.data_off = off
+        parts.append((off, data))
+        off = -(-(off + len(data)) // 16) * 16
+        j.pages_off = off
+        ids = np.ascontiguousarray(ad["pages"], np.int32).view(np.uint8)
+        parts.append((off, ids))
+        off = -(-(off + len(ids)) // 16) * 16
+    blob = torch.zeros(off, dtype=torch.uint8, pin_memory=True)
+    view = blob.numpy()
+    for o, d in parts:
+        view[o:o + len(d)] = d
+    return blob, jobs
+
+
+@pytest.mark.parametrize("layout", ["fresh", "runs", "data_first"])
+def test_direct_and_staged_routes(layout):
+    """fresh: a new free list hands out consecutive pages, so the call's rank-rows are one
+    run per pool (the direct route: copies straight into the pool); runs: pages released
+    as three ascending ranges, the middle one handed out first, come back as three runs
+    (direct); data_first: the same pages
+    from a blob whose rank-rows precede the page ids (the staged route).  Every placement
+    checked bitwise and through the kernels."""
+    import torch
+    outs = (2048, 512)
+    rank = np.array([16, 0, 32, 8, 64, 16], dtype=np.int32)
+    need = sum(int(B.lora_pool_pages_for(int(r), D_IN, d, P)) for d in outs for r in rank)
+    num_pages = need + 40
+    pool = torch.full((num_pages, P), float("nan"), dtype=torch.float16, device="cuda")
+    rank_t = torch.zeros(S, dtype=torch.int32, device="cuda")
+    scale_t = torch.zeros(S, dtype=torch.float32, device="cuda")
+    st = B.PoolState(num_pages)
+    if layout == "runs":
+        taken = st.alloc(num_pages)                     # 0 .. num_pages-1
+        third = num_pages // 3
+        st.release(taken[2 * third:])                   # handed out last
+        st.release(taken[:third])
+        st.release(taken[third:2 * third])              # handed out first
+    targets = [_target(d, num_pages, rank_t, scale_t, pool) for d in outs]
+    G.say(f"case pool-route-{layout} pages={num_pages}")
+    ads = [_adapter(w, cap, st, p, s, int(r), d) for p, ((w, cap), d) in enumerate(zip(targets, outs))
+           for s, r in enumerate(rank) if r > 0]
+    ids = np.concatenate([ad["pages"] for ad in ads])
+    breaks = int(np.count_nonzero(np.diff(ids) != 1))
+    assert breaks == (0 if layout != "runs" else 2), breaks   # the runs the direct route copies
+    if layout == "data_first":
+        blob, jobs = _pack_data_first(ads)
+        staging = torch.empty(blob.numel(), dtype=torch.uint8, device="cuda")
+        B.lora_pool_load(jobs, blob, staging)
+        torch.cuda.synchronize()
+    else:
+        _load(ads)
+    for ad in ads:
+        _check_placed(ad["w"], pool, ad, ad["b"].shape[1])
+    for p, ((w, _), d) in enumerate(zip(targets, outs)):
+        _compute_and_check(w, rank, d, p, f"pool-route-{layout}-proj{p}")

@@ -17,7 +17,7 @@ def test_free_list_order_and_counts():
     assert a.tolist() == [0, 1, 2, 3, 4] and st.free == 3
     st.release([3, 1])
     assert st.free == 5
-    assert st.alloc(3).tolist() == [1, 3, 5]          # most recently returned first
+    assert st.alloc(3).tolist() == [3, 1, 5]          # the last release first, in its order
     assert st.alloc(2).tolist() == [6, 7] and st.free == 0
 
 
