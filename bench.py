@@ -679,6 +679,116 @@ def load_sweep(args):
     print(json.dumps(out), flush=True)
 
 
+# ------------------------------------------------------------------ serving with an adapter cache
+def serve_sweep(args):
+    """The 7B decode step (32 rows, 32 distinct rank-16 adapters, every layer and projection
+    adapted) served from an AdapterCache over a paged pool: each step's adapters are made
+    resident (normally already, by the prefetch), the compute stream waits on the cache's
+    event, the step's graph replays with the step's slots, and the next step's adapters are
+    prefetched on the side stream as soon as it is queued.  The host loop keeps at most two
+    steps queued (it waits for step i-1 once step i and the next prefetch are queued).  Every
+    `every` steps `turn` new adapters enter the batch (and `turn` leave), each an 80 MB load;
+    turn 0 is the same loop with every adapter resident."""
+    import torch
+    from segmented_gather_matmul_amd import binding as B
+    from segmented_gather_matmul_amd import workloads as wl
+    from segmented_gather_matmul_amd.adapters import AdapterCache, HostAdapter, PagedModel
+    dev, P, r, n, layers = "cuda", 256, 16, 32, 32
+    names = list(wl.LLAMA2_7B)
+    shapes = [wl.LLAMA2_7B[p] for _ in range(layers) for p in names]
+    universe, slots = 40, 36
+    per_adapter = sum(B.lora_pool_pages_for(r, di, do, P) for di, do in shapes)
+    model = PagedModel(shapes, slots, r, P, slots * per_adapter, dev)
+    rng = np.random.default_rng(7)
+    tmpl = {}
+    for di, do in set(shapes):
+        tmpl[(di, do)] = ((rng.standard_normal((r, di)) * 0.02).astype(np.float16),
+                          (rng.standard_normal((r, do)) * 0.02).astype(np.float16))
+    store = {k: HostAdapter(model, r, 2.0, [tmpl[sh][0] for sh in shapes], [tmpl[sh][1] for sh in shapes])
+             for k in range(universe)}
+    weight_bytes = 2 * r * sum(di + do for di, do in shapes)
+    # the step: per layer, shrink + expand per input group, per-row form, one idx for all
+    idx_d = torch.full((n,), -1, dtype=torch.int32, device=dev)
+    # page-locked slots per step, a ring: a step's copy may still be queued when the host
+    # writes the next step's
+    idx_ring = [torch.full((n,), -1, dtype=torch.int32, pin_memory=True) for _ in range(4)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    units = []
+    for layer in range(layers):
+        for grp in INPUT_GROUPS:
+            d_in = wl.LLAMA2_7B[grp[0]][0]
+            x = (torch.randn(n, d_in, generator=gen, device=dev) * 0.02).half()
+            items = []
+            for pname in grp:
+                w = model.targets[layer * len(names) + names.index(pname)]
+                y = (torch.randn(n, w.d_out, generator=gen, device=dev) * 0.02).half()
+                v = torch.zeros((n, r), dtype=torch.float32, device=dev)
+                items.append((w, v, y))
+            units.append((x, items))
+
+    def step():
+        for x, items in units:
+            B.lora_bgmv_shrink_multi(x, idx_d, items)
+            B.lora_bgmv_expand_multi(idx_d, items, n)
+
+    def batch(i, turn, every):
+        base = (i // every) * turn if turn else 0
+        return [(base + j) % universe for j in range(n)]
+
+    cache = AdapterCache(model, store)
+    first, ready = cache.ensure(batch(0, 0, 1))
+    torch.cuda.synchronize()
+    idx_d.copy_(torch.from_numpy(first))
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    cur = torch.cuda.current_stream()
+    out = {"sweep": "serve", "model": "Llama-2-7B", "rows": n, "rank": r, "layers": layers, "page_elems": P,
+           "universe": universe, "slots": slots, "adapter_bytes": weight_bytes, "results": []}
+    reps = args.steps
+    for turn, every in [(0, 1), (1, 8), (1, 4), (1, 2), (1, 1)]:
+        loads0 = cache.loads
+        evs = [torch.cuda.Event() for _ in range(reps + 8)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(reps + 8):
+            if i == 8:
+                e0.record(cur)
+                l8 = cache.loads
+            keys = batch(i, turn, every)
+            sl, ready = cache.ensure(keys)
+            if ready is not None:
+                cur.wait_event(ready)
+            idx_h = idx_ring[i % len(idx_ring)]
+            idx_h.copy_(torch.from_numpy(sl))
+            idx_d.copy_(idx_h, non_blocking=True)
+            g.replay()
+            cache.mark_used(keys, cur)
+            evs[i].record(cur)
+            # the next step's adapters as soon as this step is queued: issued after the host
+            # waited for step i-1 instead, a load started well into step i and step i+1 waited
+            # for it (1 load every 2 steps: +36 % instead of +8 %)
+            cache.prefetch(batch(i + 1, turn, every))
+            if i >= 1:
+                evs[i - 1].synchronize()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        cache.side.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        loads = cache.loads - l8
+        rec = dict(turn=turn, every=every, step_ms=round(ms, 4), loads=loads,
+                   loads_per_step=round(loads / reps, 3),
+                   load_gbs_over_loop=round(loads * weight_bytes / (reps * ms * 1e-3) / 1e9, 2))
+        log(f"[serve] {rec}")
+        out["results"].append(rec)
+    base = out["results"][0]["step_ms"]
+    for rec in out["results"]:
+        rec["vs_resident"] = round(rec["step_ms"] / base - 1, 4)
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------ decoder layer
 def layer_sweep(args):
     """Decode step of whole Llama-2 decoder layers (RMSNorm, fused q/k/v GEMM, attention
@@ -805,11 +915,12 @@ def main():
                          "kernels (0 = library's choice; results are bit-identical either way)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (byte-counter calibration)")
-    ap.add_argument("--sweep", choices=["operator", "load", "layer"], default=None,
+    ap.add_argument("--sweep", choices=["operator", "load", "layer", "serve"], default=None,
                     help="instead of the step: 'operator' times one LoRA operator across batch sizes, popularity "
                          "and ranks against a loop over adapters and Gather-BMM; 'load' times placing 7B adapter "
                          "sets into a paged pool (--sweep-batches = models per call); 'layer' times whole "
-                         "decoder layers with and without the seven add-ons")
+                         "decoder layers with and without the seven add-ons; 'serve' serves the 7B decode step "
+                         "from an adapter cache with new adapters prefetched while steps run")
     ap.add_argument("--sweep-h", type=int, default=4096)
     ap.add_argument("--sweep-layers", type=int, default=None, help="layers per graph (operator 16, layer 4)")
     ap.add_argument("--sweep-batches", default=None,
@@ -850,6 +961,9 @@ def main():
         return
     if args.sweep == "layer":
         layer_sweep(args)
+        return
+    if args.sweep == "serve":
+        serve_sweep(args)
         return
     device = "cuda"
     grouped = not args.no_group
