@@ -683,12 +683,13 @@ def load_sweep(args):
 def serve_sweep(args):
     """The 7B decode step (32 rows, 32 distinct rank-16 adapters, every layer and projection
     adapted) served from an AdapterCache over a paged pool: each step's adapters are made
-    resident (normally already, by the prefetch), the compute stream waits on the cache's
-    event, the step's graph replays with the step's slots, and the next step's adapters are
-    prefetched on the side stream as soon as it is queued.  The host loop keeps at most two
-    steps queued (it waits for step i-1 once step i and the next prefetch are queued).  Every
-    `every` steps `turn` new adapters enter the batch (and `turn` leave), each an 80 MB load;
-    turn 0 is the same loop with every adapter resident."""
+    resident (normally already, by the prefetch), the compute stream waits for any of their
+    loads still in flight, the step's graph replays with the step's slots, and the adapters
+    of the step `--serve-lookahead` steps ahead are prefetched (their copies on the side
+    stream) as soon as it is queued, keeping those of the steps in between.  The host loop
+    keeps at most two steps queued (it waits for step i-1 once step i and the prefetch are
+    queued).  Every `every` steps `turn` new adapters enter the batch (and `turn` leave),
+    each an 80 MB load; turn 0 is the same loop with every adapter resident."""
     import torch
     from segmented_gather_matmul_amd import binding as B
     from segmented_gather_matmul_amd import workloads as wl
@@ -733,10 +734,12 @@ def serve_sweep(args):
             B.lora_bgmv_expand_multi(idx_d, items, n)
 
     def batch(i, turn, every):
-        base = (i // every) * turn if turn else 0
+        # turn new adapters every `every` steps, spread over the steps (turn > every: one
+        # or two new adapters at each step)
+        base = (i * turn) // every
         return [(base + j) % universe for j in range(n)]
 
-    cache = AdapterCache(model, store)
+    cache = AdapterCache(model, store, max_side=args.serve_side_streams)
     first, ready = cache.ensure(batch(0, 0, 1))
     torch.cuda.synchronize()
     idx_d.copy_(torch.from_numpy(first))
@@ -747,40 +750,81 @@ def serve_sweep(args):
         step()
     cur = torch.cuda.current_stream()
     out = {"sweep": "serve", "model": "Llama-2-7B", "rows": n, "rank": r, "layers": layers, "page_elems": P,
+           "side_streams": args.serve_side_streams,
            "universe": universe, "slots": slots, "adapter_bytes": weight_bytes, "results": []}
     reps = args.steps
-    for turn, every in [(0, 1), (1, 8), (1, 4), (1, 2), (1, 1)]:
-        loads0 = cache.loads
+    configs = [tuple(int(v) for v in c.split(":")) for c in args.serve_configs.split(",")]
+    L = max(1, args.serve_lookahead)
+    out["lookahead_steps"] = L
+    for turn, every in configs:
+        late0 = cache.late
         evs = [torch.cuda.Event() for _ in range(reps + 8)]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_pf = t_wait = 0.0
         for i in range(reps + 8):
             if i == 8:
                 e0.record(cur)
                 l8 = cache.loads
             keys = batch(i, turn, every)
-            sl, ready = cache.ensure(keys)
-            if ready is not None:
-                cur.wait_event(ready)
+            keep = [k for j in range(1, L) for k in batch(i + j, turn, every)]
+            sl, ready = cache.ensure(keys, keep)
+            for e in ready:
+                cur.wait_event(e)
             idx_h = idx_ring[i % len(idx_ring)]
             idx_h.copy_(torch.from_numpy(sl))
             idx_d.copy_(idx_h, non_blocking=True)
             g.replay()
             cache.mark_used(keys, cur)
             evs[i].record(cur)
-            # the next step's adapters as soon as this step is queued: issued after the host
-            # waited for step i-1 instead, a load started well into step i and step i+1 waited
-            # for it (1 load every 2 steps: +36 % instead of +8 %)
-            cache.prefetch(batch(i + 1, turn, every))
+            # step i+L's adapters as soon as this step is queued: issued after the host
+            # waited for step i-1 instead, a load started well into step i and step i+1
+            # waited for it (1 load every 2 steps: +36 % instead of +8 %)
+            t0 = time.perf_counter()
+            cache.prefetch(batch(i + L, turn, every), keep)
+            t1 = time.perf_counter()
+            if i >= 1:
+                evs[i - 1].synchronize()
+            if i >= 8:
+                t_pf += t1 - t0
+                t_wait += time.perf_counter() - t1
+        e1.record(cur)
+        torch.cuda.synchronize()
+        for side in cache.sides:
+            side.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        loads = cache.loads - l8
+        rec = dict(turn=turn, every=every, step_ms=round(ms, 4), loads=loads,
+                   loads_per_step=round(loads / reps, 3),
+                   load_gbs_over_loop=round(loads * weight_bytes / (reps * ms * 1e-3) / 1e9, 2),
+                   host_prefetch_ms_per_step=round(1e3 * t_pf / reps, 4),
+                   host_wait_ms_per_step=round(1e3 * t_wait / reps, 4),
+                   late_batches=cache.late - late0)
+        log(f"[serve] {rec}")
+        out["results"].append(rec)
+    # reference: the same loop with every adapter resident and, each k-th step, a plain
+    # host-to-device copy of one adapter's bytes on the side stream into scratch memory
+    hsrc = torch.empty(weight_bytes, dtype=torch.uint8, pin_memory=True)
+    dscratch = torch.empty(weight_bytes, dtype=torch.uint8, device=dev)
+    for every in ((2, 1) if args.serve_copies else ()):
+        keys = batch(0, 0, 1)
+        evs = [torch.cuda.Event() for _ in range(reps + 8)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(reps + 8):
+            if i == 8:
+                e0.record(cur)
+            g.replay()
+            evs[i].record(cur)
+            if i % every == 0:
+                with torch.cuda.stream(cache.side):
+                    dscratch.copy_(hsrc, non_blocking=True)
             if i >= 1:
                 evs[i - 1].synchronize()
         e1.record(cur)
         torch.cuda.synchronize()
         cache.side.synchronize()
         ms = e0.elapsed_time(e1) / reps
-        loads = cache.loads - l8
-        rec = dict(turn=turn, every=every, step_ms=round(ms, 4), loads=loads,
-                   loads_per_step=round(loads / reps, 3),
-                   load_gbs_over_loop=round(loads * weight_bytes / (reps * ms * 1e-3) / 1e9, 2))
+        rec = dict(turn=0, every=every, plain_copies=True, step_ms=round(ms, 4),
+                   copy_gbs_over_loop=round(weight_bytes / every / (ms * 1e-3) / 1e9, 2))
         log(f"[serve] {rec}")
         out["results"].append(rec)
     base = out["results"][0]["step_ms"]
@@ -921,6 +965,13 @@ def main():
                          "sets into a paged pool (--sweep-batches = models per call); 'layer' times whole "
                          "decoder layers with and without the seven add-ons; 'serve' serves the 7B decode step "
                          "from an adapter cache with new adapters prefetched while steps run")
+    ap.add_argument("--serve-configs", default="0:1,1:8,1:4,1:2,1:1,9:8,5:4", metavar="TURN:EVERY,...",
+                    help="serve sweep: new adapters per change and steps between changes, one loop each")
+    ap.add_argument("--serve-copies", type=int, default=1, help="serve sweep: also the plain-copy reference loops")
+    ap.add_argument("--serve-lookahead", type=int, default=3,
+                    help="serve sweep: the host prefetches the adapters of the batch this many steps ahead")
+    ap.add_argument("--serve-side-streams", type=int, default=4,
+                    help="serve sweep: most side streams the cache spreads its loads over")
     ap.add_argument("--sweep-h", type=int, default=4096)
     ap.add_argument("--sweep-layers", type=int, default=None, help="layers per graph (operator 16, layer 4)")
     ap.add_argument("--sweep-batches", default=None,

@@ -8,14 +8,16 @@ the path happens here.
 - PagedModel: one paged weight descriptor per adapted projection of a model (layer x
   projection), all sharing one pool of pages and one rank and scale array over the slots.
 - HostAdapter: one adapter's rank-rows for every target, packed once into a page-locked
-  blob laid out for the loader's direct route (job table, page ids, then all rank-rows),
-  so that loading it again rewrites only its page ids.
+  blob laid out for the loader's direct route (job table, the page ids of all targets
+  back to back, then all rank-rows), so that loading it again rewrites only its page ids
+  (one array) and two fields of its prepared job records.
 - AdapterCache: which adapter sits in which slot.  ensure(keys) loads the adapters a batch
-  needs that are not resident, on a side stream, evicting least recently used adapters
-  that the batch does not need; the compute stream waits on the returned event.  A slot is
-  reloaded (and its pages handed to another adapter) only after the last batch that read
-  it has finished: every load waits on the events mark_used recorded.  prefetch(keys) is
-  ensure for the next batch, issued while the current one runs.
+  needs that are not resident, each on a side stream with nothing in flight, evicting
+  least recently used adapters that the batch does not need (nor those of batches
+  prefetched but not yet run).  A slot is reloaded (and its pages handed to another
+  adapter) only after the last batch that read it has finished (the events mark_used
+  recorded).  prefetch(keys, keep) is ensure for a later batch, issued while the current
+  ones run.
 """
 from __future__ import annotations
 
@@ -69,10 +71,12 @@ class HostAdapter:
         n = len(model.shapes)
         self.n_pages = model.pages_for(self.rank)
         off = int(B.lib().lora_pool_load_header_bytes(n))
+        self.ids_off = off                       # every target's page ids, back to back
         self.pages_off = []
         for np_t in self.n_pages:
             self.pages_off.append(off)
-            off = -(-(off + 4 * np_t) // 16) * 16
+            off += 4 * np_t
+        off = -(-off // 16) * 16
         self.data_off, datas = [], []
         for (di, do), a, bb in zip(model.shapes, a_t, b):
             a = np.ascontiguousarray(a, dtype=np.float16)
@@ -88,57 +92,73 @@ class HostAdapter:
             na = a.size * 2
             view[o:o + na] = a.view(np.uint8).ravel()
             view[o + na:o + na + bb.size * 2] = bb.view(np.uint8).ravel()
-        self.load_done = None   # event of the last load that read the blob
+        self.last_load = (0, 0)  # (number, side stream) of the last load of this blob (AdapterCache)
+        self._jobs = None       # job records for `model`, all but slot and pt_off filled in
 
     def jobs(self, model: PagedModel, slot, pages):
-        """Load jobs placing this adapter into `slot` on the given pages (one id array per
-        target), with the page ids written into the blob."""
-        if self.load_done is not None:
-            self.load_done.synchronize()   # a load still reading the blob's page ids
-        view = self.blob.numpy()
-        jobs = (B.CLoadJob * len(model.targets))()
-        for t, (w, cap) in enumerate(zip(model.targets, model.caps)):
-            ids = np.ascontiguousarray(pages[t], dtype=np.int32)
-            if len(ids) != self.n_pages[t]:
-                raise ValueError(f"target {t}: {len(ids)} pages for {self.n_pages[t]}")
-            o = self.pages_off[t]
-            view[o:o + 4 * len(ids)] = ids.view(np.uint8)
-            j = jobs[t]
-            j.w = ctypes.addressof(w.c)
-            j.slot, j.rank, j.scale, j.reserved = int(slot), self.rank, self.scale, 0
-            j.pt_off = int(slot) * cap
-            j.data_off, j.pages_off = self.data_off[t], o
-        return jobs
+        """Load jobs placing this adapter into `slot` on the given pages (the ids of all
+        targets back to back, target by target), with the page ids written into the blob.
+        The caller makes sure no earlier load still reads the blob."""
+        ids = np.ascontiguousarray(pages, dtype=np.int32)
+        if len(ids) != sum(self.n_pages):
+            raise ValueError(f"{len(ids)} pages for {sum(self.n_pages)}")
+        self.blob.numpy()[self.ids_off:self.ids_off + 4 * len(ids)] = ids.view(np.uint8)
+        if self._jobs is None:
+            self._jobs = (B.CLoadJob * len(model.targets))()
+            for t, w in enumerate(model.targets):
+                j = self._jobs[t]
+                j.w = ctypes.addressof(w.c)
+                j.rank, j.scale, j.reserved = self.rank, self.scale, 0
+                j.data_off, j.pages_off = self.data_off[t], self.pages_off[t]
+        for j, cap in zip(self._jobs, model.caps):
+            j.slot, j.pt_off = int(slot), int(slot) * cap
+        return self._jobs
 
 
 class AdapterCache:
-    """Slots of a PagedModel holding adapters from a host store (key -> HostAdapter)."""
+    """Slots of a PagedModel holding adapters from a host store (key -> HostAdapter).
 
-    def __init__(self, model: PagedModel, store, stream=None):
+    Anything queued on a stream behind a host-to-device copy still in flight (a kernel, an
+    event, a wait) holds back the kernels of the other streams until the copy ends: a 7B
+    decode step ran a fifth slower with one event recorded behind each load's copies, and
+    2 % slower with the copies alone.  So each load (lora_pool_load: a small copy, a small
+    kernel, then the long copies of the rank-rows) goes to a side stream with nothing in
+    flight (up to `max_side` of them; past that the host waits for the oldest), and
+    nothing is queued behind its copies: what a load must wait for is waited for on the
+    host (normally long finished), and whether it has landed is asked on the host of its
+    side stream, which has finished every earlier load once it has taken a later one.
+    Only a batch whose load is still in flight gets an event behind it to wait on."""
+
+    def __init__(self, model: PagedModel, store, streams=None, max_side=4):
         import torch
         self.model, self.store = model, store
-        self.side = stream if stream is not None else torch.cuda.Stream()
+        self.sides = list(streams) if streams is not None else [torch.cuda.Stream()]
+        self.max_side = max(max_side, len(self.sides))
+        self.side_load = [0] * len(self.sides)          # the last load each side stream took
+        self.side = self.sides[0]
         self.slot_of = {}                                   # resident key -> slot
         self.key_in = [None] * model.num_slots              # slot -> key
         self.lru = collections.OrderedDict()                # resident keys, least recently used first
-        self.pages = {}                                      # resident key -> page ids per target
+        self.pages = {}                                      # resident key -> its page ids (all targets)
         self.last_use = [None] * model.num_slots            # event after the last batch that read the slot
-        self.loaded = {}                                     # resident key -> (load number, event after its load)
-        self.staging = None
-        self.loads = 0
+        self.loaded = {}                                     # resident key -> (its load's number, side stream)
+        self.staging = [None] * len(self.sides)             # per side stream (the staged route's copy)
+        self.loads = 0                                       # loads issued; number of the latest
+        self.late = 0                                        # batches that had to wait for a load in flight
 
     # -------------------------------------------------------------- host policy
-    def plan(self, keys):
+    def plan(self, keys, keep=()):
         """Where to put the batch's missing adapters and whom to evict, without changing
-        anything: [(key, slot, [evicted keys])] in batch order.  Keys the batch needs are
-        never evicted; free slots go first, then the least recently used residents, which
-        are also evicted while the pool lacks pages.  ValueError when the batch cannot fit
-        (more distinct adapters than slots, or too few pages even after every eviction);
-        KeyError for a key the host store lacks."""
+        anything: [(key, slot, [evicted keys])] in batch order.  Keys the batch needs, and
+        keys in `keep` (batches prefetched but not yet run), are never evicted; free slots
+        go first, then the least recently used residents, which are also evicted while the
+        pool lacks pages.  ValueError when the batch cannot fit (more distinct adapters than
+        slots, or too few pages even after every eviction); KeyError for a key the host
+        store lacks."""
         need = [k for k in dict.fromkeys(k for k in keys if k is not None)]
         if len(need) > self.model.num_slots:
             raise ValueError(f"{len(need)} distinct adapters in one batch, {self.model.num_slots} slots")
-        needed = set(need)
+        needed = set(need) | set(k for k in keep if k is not None)
         free_slots = [s for s, k in enumerate(self.key_in) if k is None]
         victims = [k for k in self.lru if k not in needed]
         free_pages = self.model.state.free
@@ -156,7 +176,7 @@ class AdapterCache:
                     raise ValueError(f"no room for adapter {k!r}: {free_pages} free pages, {want} needed")
                 v = victims.pop(0)
                 evicted.append(v)
-                free_pages += sum(len(p) for p in self.pages[v])
+                free_pages += len(self.pages[v])
                 if slot is None:
                     slot = self.slot_of[v]
                 else:
@@ -166,58 +186,100 @@ class AdapterCache:
         return out
 
     # -------------------------------------------------------------- GPU work
-    def ensure(self, keys):
-        """Makes every adapter named in keys (None = no adapter) resident; returns the device
-        slot per key as a numpy int32 array (-1 for None) and the event the compute stream
-        must wait on before reading those slots: the side stream's event after the latest
-        load of any of these adapters, issued now or by an earlier prefetch (the side stream
-        runs its loads in order), or None when none was ever loaded through this cache."""
+    def has_landed(self, load):
+        """True when `load` (number, side stream) has finished: its side stream has taken a
+        later load (it only takes one when idle) or has nothing in flight (asked on the host)."""
+        n, si = load
+        return n <= 0 or self.side_load[si] != n or self.sides[si].query()
+
+    def free_side(self):
+        """A side stream with nothing in flight: an idle one, a new one, or (at max_side
+        streams) the one with the oldest load, once the host has waited for it."""
         import torch
-        for k, slot, evicted in self.plan(keys):
+        for si, side in enumerate(self.sides):
+            if side.query():
+                return si
+        if len(self.sides) < self.max_side:
+            self.sides.append(torch.cuda.Stream())
+            self.side_load.append(0)
+            self.staging.append(None)   # allocated at the stream's first load, which waits for nothing
+            return len(self.sides) - 1
+        si = min(range(len(self.sides)), key=lambda i: self.side_load[i])
+        self.sides[si].synchronize()
+        return si
+
+    def ensure(self, keys, keep=()):
+        """Makes every adapter named in keys (None = no adapter) resident, keeping the keys
+        in `keep`; returns the device slot per key as a numpy int32 array (-1 for None) and
+        the events the stream that reads those slots must wait on first: none when their
+        loads (issued now or by an earlier prefetch) have landed, else one event after the
+        side stream's copies."""
+        import torch
+        self.prefetch(keys, keep)
+        slots = np.array([self.slot_of[k] if k is not None else -1 for k in keys], dtype=np.int32)
+        if all(self.has_landed(self.loaded[k]) for k in keys if k is not None):
+            return slots, []
+        self.late += 1
+        waits = []
+        for si in sorted(set(self.loaded[k][1] for k in keys if k is not None and not self.has_landed(self.loaded[k]))):
+            e = torch.cuda.Event()        # an event behind the copies of each load in flight
+            e.record(self.sides[si])
+            waits.append(e)
+        return slots, waits
+
+    def prefetch(self, keys, keep=()):
+        """The loads of ensure(keys, keep) without waiting for them: for a batch that runs
+        later, issued while earlier ones run."""
+        import torch
+        for k, slot, evicted in self.plan(keys, keep):
+            for v in evicted:              # pages still being written by an unfinished load
+                if not self.has_landed(self.loaded[v]):
+                    self.sides[self.loaded[v][1]].synchronize()
             pages, waits = self.take(k, slot, evicted)
             ad = self.store[k]
+            if not self.has_landed(ad.last_load):
+                self.sides[ad.last_load[1]].synchronize()    # its blob is still being read
             jobs = ad.jobs(self.model, slot, pages)
-            if self.staging is None or self.staging.numel() < ad.blob.numel():
-                self.side.synchronize()   # the previous staging may still be read
-                self.staging = torch.empty(ad.blob.numel(), dtype=torch.uint8, device=self.model.pool.device)
-            for e in waits:
-                self.side.wait_event(e)
-            B.lora_pool_load(jobs, ad.blob, self.staging, stream=self.side)
-            ad.load_done = torch.cuda.Event()
-            ad.load_done.record(self.side)
-            self.loaded[k] = (self.loads, ad.load_done)
-        latest = None
+            n = self.loads + 1
+            si = self.free_side()
+            side = self.sides[si]
+            if self.staging[si] is None or self.staging[si].numel() < ad.blob.numel():
+                if self.staging[si] is not None:
+                    torch.cuda.synchronize()   # the previous staging may still be read
+                size = max(ad.blob.numel(), max((a.blob.numel() for a in self.store.values()), default=0))
+                self.staging[si] = torch.empty(size, dtype=torch.uint8, device=self.model.pool.device)
+            for e in waits:               # the last readers of the slot and pages, normally done
+                if not e.query():
+                    e.synchronize()
+            B.lora_pool_load(jobs, ad.blob, self.staging[si], stream=side)
+            self.loads = n
+            self.side_load[si] = n
+            self.loaded[k] = ad.last_load = (n, si)
         for k in keys:
             if k is not None:
                 self.lru.move_to_end(k)
-                if latest is None or self.loaded[k][0] > latest[0]:
-                    latest = self.loaded[k]
-        slots = np.array([self.slot_of[k] if k is not None else -1 for k in keys], dtype=np.int32)
-        return slots, (latest[1] if latest is not None else None)
-
-    prefetch = ensure
 
     def take(self, k, slot, evicted):
         """The host side of one step of a plan: evicts (their pages back to the free list),
-        gives `slot` and fresh pages to k; returns k's page ids per target and the events
-        the load must wait for (the last batches that read the evicted slots and `slot`,
-        whose pages the free list may hand out again at once)."""
+        gives `slot` and fresh pages to k; returns k's page ids (all targets back to back,
+        one allocation) and the events the load must wait for (the last batches that read
+        the evicted slots and `slot`, whose pages the free list may hand out again at
+        once)."""
         waits = []
         for v in evicted:
             s = self.slot_of.pop(v)
             self.key_in[s] = None
             del self.lru[v]
             self.loaded.pop(v, None)
-            self.model.state.release(np.concatenate(self.pages.pop(v)))
+            self.model.state.release(self.pages.pop(v))
             if self.last_use[s] is not None:
                 waits.append(self.last_use[s])
         if self.last_use[slot] is not None and self.last_use[slot] not in waits:
             waits.append(self.last_use[slot])
-        pages = [self.model.state.alloc(n) for n in self.store[k].n_pages]
+        pages = self.model.state.alloc(sum(self.store[k].n_pages))
         self.slot_of[k], self.key_in[slot], self.pages[k] = slot, k, pages
         self.lru[k] = None
-        self.loads += 1
-        self.loaded[k] = (self.loads, None)
+        self.loaded[k] = (0, 0)          # set once its load is issued
         return pages, waits
 
     def mark_used(self, keys, stream=None):

@@ -15,7 +15,7 @@ def _cache(num_slots, num_pages, pages_of):
     whose adapters take pages_of[key] pages (split over two targets)."""
     model = types.SimpleNamespace(num_slots=num_slots, state=B.PoolState(num_pages))
     store = {k: types.SimpleNamespace(n_pages=[n // 2, n - n // 2]) for k, n in pages_of.items()}
-    return AdapterCache(model, store, stream=object())
+    return AdapterCache(model, store, streams=[object()])
 
 
 def _apply(c, keys, used=None):
@@ -41,7 +41,7 @@ def _invariants(c, num_pages):
         assert c.key_in[s] == k
     assert sum(k is not None for k in c.key_in) == len(c.slot_of)
     assert list(c.lru) == [k for k in c.lru if k in c.slot_of] and set(c.lru) == set(c.slot_of)
-    taken = np.concatenate([np.concatenate(p) for p in c.pages.values()]) if c.pages else np.zeros(0, np.int32)
+    taken = np.concatenate(list(c.pages.values())) if c.pages else np.zeros(0, np.int32)
     assert len(taken) == len(set(taken.tolist()))                       # no page in two adapters
     assert c.model.state.free == num_pages - len(taken)
 
@@ -92,7 +92,7 @@ def test_loads_wait_for_the_last_readers_of_what_they_reuse():
     steps, waits = _apply(c, ["c"])                   # evicts a: its slot and its pages
     assert steps == [("c", 0, ["a"])] and waits == [[e1]]
     # pages released in order come back as the same run
-    assert np.array_equal(np.concatenate(c.pages["c"]), np.arange(20))
+    assert np.array_equal(c.pages["c"], np.arange(20))
 
 
 def test_unknown_key():

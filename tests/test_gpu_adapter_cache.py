@@ -74,8 +74,8 @@ def test_batches_through_the_cache():
     for i, keys in enumerate(batches):
         if i > 0:
             slots, ready = cache.ensure(keys)          # resident already: prefetched below
-        if ready is not None:
-            cur.wait_event(ready)
+        for e in ready:
+            cur.wait_event(e)
         views = [_dense_view(model, store, host, cache, t) for t in range(len(SHAPES))]
         idx = torch.from_numpy(slots).cuda()
         outs = []
