@@ -88,23 +88,32 @@ class Op:
 INPUT_GROUPS = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
 
 
-def make_ops(spec, layers, device, tile_rows=None):
-    """Per layer: one x per input group, one y, v and weight descriptor per projection."""
+def make_ops(spec, layers, device, tile_rows=None, expand_tile_rows=None):
+    """Per layer: one x per input group, one y, v and weight descriptor per projection.
+    With expand_tile_rows the expand launches get a tile list of their own (the shrink
+    keeps tile_rows): the tile height is a launch shape, the results do not depend on it
+    beyond the tolerance."""
     import torch
     from segmented_gather_matmul_amd import binding as B
     b = spec["batch"]
     n, S, rank = b.n, spec["num_slots"], spec["rank"]
     r_max = int(rank.max())
     idx_d = torch.from_numpy(b.idx.astype(np.int32)).to(device)
-    segs = None
+    segs = segs_e = None
     if spec["form"].startswith("sgmv") or spec["form"] == "mixed":
         if spec["form"] in ("sgmv", "mixed"):
             row_map, seg_ptr, seg_slot, n_act = B.lora_build_segments(b.idx, S)
-            tiles = B.lora_build_tiles(seg_ptr, seg_slot, tile_rows)
-            segs = B.segments_to_device(tiles, row_map, n_act, device)
+            n_pos = n_act
         else:
-            tiles = B.lora_build_tiles(b.seg_ptr, b.seg_slot, tile_rows)
-            segs = B.segments_to_device(tiles, None, n, device)
+            row_map, seg_ptr, seg_slot, n_pos = None, b.seg_ptr, b.seg_slot, n
+        segs = B.segments_to_device(B.lora_build_tiles(seg_ptr, seg_slot, tile_rows), row_map, n_pos, device)
+        segs_e = segs
+        if expand_tile_rows is None and tile_rows is None:
+            expand_tile_rows = B.lora_pick_expand_tile_rows(seg_ptr)
+        if expand_tile_rows and expand_tile_rows != (tile_rows or B.lora_pick_tile_rows(seg_ptr)):
+            segs_e = B.segments_to_device(B.lora_build_tiles(seg_ptr, seg_slot, expand_tile_rows), row_map, n_pos,
+                                          device)
+        spec["expand_tile_rows"] = int(expand_tile_rows or tile_rows or B.lora_pick_tile_rows(seg_ptr))
     rank_d = torch.from_numpy(rank.astype(np.int32)).to(device)
     scale_d = torch.from_numpy(spec["scale"].astype(np.float32)).to(device)
     gen = torch.Generator(device=device)
@@ -164,7 +173,7 @@ def make_ops(spec, layers, device, tile_rows=None):
                                       b_pt_off=torch.from_numpy(b_off).to(device))
                     op.shrink_rank = rs
                 op.v = torch.zeros((n, ldv), dtype=torch.float32, device=device)
-                op.idx, op.segs = idx_d, segs
+                op.idx, op.segs, op.segs_e = idx_d, segs, segs_e
                 op.expand_per_row = spec["form"] == "mixed"
                 ops.append(op)
             groups.append(ops)
@@ -193,7 +202,7 @@ def launch_unit(kind, ops):
     elif op0.expand_per_row:
         B.lora_bgmv_expand_multi(op0.idx, items, n)
     else:
-        B.lora_sgmv_expand_multi(op0.segs, items, n)
+        B.lora_sgmv_expand_multi(op0.segs_e, items, n)
 
 
 def launches(groups, grouped, handoff=False):
@@ -946,6 +955,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tile-rows", type=int, default=None,
                     help="tile height for the segment form (default: lora_pick_tile_rows)")
+    ap.add_argument("--expand-tile-rows", type=int, default=None,
+                    help="segment form: a tile height of its own for the expand launches")
     ap.add_argument("--form", choices=["bgmv", "sgmv", "mixed"], default=None,
                     help="per-row slots (bgmv), rows grouped by adapter (sgmv), or the segment-form shrink with "
                          "the per-row expand (mixed); default: the workload's own")
@@ -1026,7 +1037,7 @@ def main():
     layers = args.layers or spec["layers"]
     B.lora_set_plan(*(int(v) for v in args.plan.split(",")))
     log(f"[bench] workload={args.workload} layers={layers} grouped={grouped} building inputs")
-    groups = make_ops(spec, layers, device, args.tile_rows)
+    groups = make_ops(spec, layers, device, args.tile_rows, args.expand_tile_rows)
     torch.cuda.synchronize()
     counts = [unit_counts(spec, ops) for ops in groups]
     step_bytes = sum(c["shrink_bytes"] + c["expand_bytes"] for c in counts)
@@ -1133,6 +1144,7 @@ def main():
                    "num_slots": spec["num_slots"], "rank": sorted(set(int(r) for r in spec["rank"])),
                    "popularity": spec["popularity"], "form": spec["form"], "layout": spec["layout"],
                    "grouped": grouped, "launches_per_step": n_launch, "tile_rows": args.tile_rows,
+                   "expand_tile_rows": spec.get("expand_tile_rows"),
                    "handoff": handoff,
                    "plan": args.plan,
                    "graph": not args.no_graph,

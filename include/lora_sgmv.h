@@ -209,6 +209,16 @@ int32_t lora_tiles_bound(int32_t n_pos, int32_t n_seg, int32_t max_tile_rows);
 int32_t lora_pick_tile_rows(const int32_t *seg_ptr, int32_t n_seg);
 
 /*
+ * Tile height suited to the expand launches of a batch, whose tile list may differ
+ * from the shrink's (the two are separate calls): lora_pick_tile_rows' height, except
+ * 16 for batches of short segments whose 16-row tiles average at least 6 rows, one of
+ * them at least 8 (tiles of 8 to 16 rows run an expand that reads each adapter's B
+ * once per tile).
+ * seg_ptr: host [n_seg + 1]; same tolerance statement as lora_pick_tile_rows.
+ */
+int32_t lora_pick_expand_tile_rows(const int32_t *seg_ptr, int32_t n_seg);
+
+/*
  * Cut segments into the flat tile work-list the SGMV kernels run on.  Segment g
  * (positions seg_ptr[g] .. seg_ptr[g+1]-1, slot seg_slot[g]) becomes
  * ceil(len / max_tile_rows) tiles of near-equal size; empty segments and segments

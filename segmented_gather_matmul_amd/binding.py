@@ -31,7 +31,8 @@ EXPORTS = ["lora_build_segments", "lora_tiles_bound", "lora_build_tiles", "lora_
            "lora_validate_segments_host", "lora_sgmv_shrink", "lora_sgmv_expand",
            "lora_bgmv_shrink", "lora_bgmv_expand", "lora_bgmv", "lora_last_error", "lora_status_str",
            "lora_abi_version", "lora_set_launch_events", "lora_sgmv_shrink_multi", "lora_sgmv_expand_multi",
-           "lora_bgmv_shrink_multi", "lora_bgmv_expand_multi", "lora_pick_tile_rows", "lora_bgmv_multi",
+           "lora_bgmv_shrink_multi", "lora_bgmv_expand_multi", "lora_pick_tile_rows", "lora_pick_expand_tile_rows",
+           "lora_bgmv_multi",
            "lora_set_plan", "lora_pool_state_bytes", "lora_pool_init", "lora_pool_alloc", "lora_pool_release",
            "lora_pool_free_count", "lora_pool_pages_for", "lora_pool_load_header_bytes", "lora_pool_load",
            "lora_handoff_bytes", "lora_bgmv_multi_handoff", "lora_sgmv_multi_handoff", "lora_set_handoff_polls",
@@ -104,6 +105,7 @@ def lib() -> ctypes.CDLL:
             "lora_bgmv_shrink_multi": [P, P, I64, P, I32, I32, P],
             "lora_bgmv_expand_multi": [P, P, I32, I32, P],
             "lora_pick_tile_rows": [P, I32],
+            "lora_pick_expand_tile_rows": [P, I32],
             "lora_bgmv_multi": [P, P, I64, P, I32, I32, P],
             "lora_set_plan": [I32, I32],
             "lora_bgmv_multi_handoff": [P, P, I64, P, I32, I32, P, P, ctypes.c_size_t],
@@ -129,6 +131,7 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes, fn.restype = args, res
         L.lora_pick_tile_rows.restype = ctypes.c_int32
+        L.lora_pick_expand_tile_rows.restype = ctypes.c_int32
         L.lora_last_error.restype = ctypes.c_char_p
         L.lora_status_str.restype = ctypes.c_char_p
         _lib = L
@@ -396,6 +399,12 @@ def lora_tiles_bound(n_pos, n_seg, max_tile_rows=MAX_TILE_ROWS):
 def lora_pick_tile_rows(seg_ptr):
     seg_ptr = np.ascontiguousarray(seg_ptr, dtype=np.int32)
     return int(lib().lora_pick_tile_rows(_ptr(seg_ptr), len(seg_ptr) - 1))
+
+
+def lora_pick_expand_tile_rows(seg_ptr):
+    """Host: the tile height suited to the expand launches of this batch."""
+    seg_ptr = np.ascontiguousarray(seg_ptr, dtype=np.int32)
+    return int(lib().lora_pick_expand_tile_rows(_ptr(seg_ptr), len(seg_ptr) - 1))
 
 
 def lora_build_tiles(seg_ptr, seg_slot, max_tile_rows=None):

@@ -23,11 +23,16 @@
 //   - tiles of 8..64 rows: v_mfma_f32_16x16x32_f16 over 16-rank slices, up to four of
 //     them (across the launch's projections) sharing each read of the tile's x rows;
 //     16 wavefronts split d_in.
-// Expand.  A workgroup owns 512 output columns of one tile.
+// Expand.  A workgroup owns 512 output columns of one tile (256 in the 8..16-row kernel
+// at ranks above 32).
 //   - tiles of < 8 rows: each wavefront loads its quarter of the rank-rows of B once
 //     (16-byte loads, contiguous in d_out, all in flight together), the quarters are
 //     added in LDS, and one fp32 -> fp16 rounding updates y;
-//   - tiles of 8..64 rows: B[0:r][512 columns] is staged transposed in LDS and reused
+//   - tiles of 8..16 rows (decode batches with rows sharing adapters): each wavefront
+//     holds its columns of every rank-row of B in registers and runs
+//     v_mfma_f32_16x16x16_f16 on s v (fp16 hi + lo/2048 parts) x B, so B is read once
+//     per 16 rows; no LDS;
+//   - tiles of 17..64 rows: B[0:r][512 columns] is staged transposed in LDS and reused
 //     by every 16-row slice; D^T = B^T (s v)^T runs on v_mfma_f32_16x16x16_f16 with s*v
 //     split into fp16 hi + lo/2048 parts (two MFMAs, ~22 bits kept); the accumulator
 //     starts from y and each lane moves 8 consecutive y elements of one row.
@@ -1145,6 +1150,224 @@ void lora_expand_valu_kernel(Args args)
     expand_pass<PERROW, NR, RU>(pd, ps, sc, rank, bv, yv, c, cin, red);
 }
 
+// Expand for tiles of 8 to 16 rows (the short segments of decode batches): workgroup =
+// (tile, 64 CW output columns, projection), each wavefront 16 CW of the columns with
+// every rank-row, so each adapter's B is read once per 16 rows, where the VALU expand's
+// 2-row tiles read it once per 2, and no sums cross wavefronts.  CW (8 or 4 columns per
+// lane) trades columns per workgroup for registers: 4 at ranks above 32.  Products on
+// v_mfma_f32_16x16x16_f16 with A = s v (16 rows x 16 ranks, split into fp16 hi +
+// lo/2048 parts: two MFMAs, ~22 bits kept) and B = the rank-rows, exact in fp16.  In
+// 16-rank step s, lane (li, lg) loads rank-rows 16 s + 4 lg .. + 3 of B at its CW columns
+// c .. c + CW - 1 (c = 16 CW w + CW li in the chunk) and gives MFMA m the four elements
+// of column c + m, so MFMA m's output columns are c + m over the 16 lanes li; after the
+// steps the lane holds rows 4 lg .. 4 lg + 3 of columns c .. c + CW - 1 and updates them
+// in y (one fp16 rounding of y + the fp32 sum); each row span of 16 lanes is one or two
+// whole 128-byte lines.  Each row's products
+// run on s v 2^-ex with 2^ex above the row's largest |s v|, and the sum is scaled back,
+// so the fp16 parts stay in fp16's normal range whatever the magnitude of v.  Every load
+// is issued from an in-bounds (clamped) address and masked where its value is used, so
+// a tile's loads are in flight together.  Work items are slice-major, as in the VALU
+// expand.  Tiles taller than 16 rows (the row height is only a hint) take one 16-row
+// block after another with B kept in registers.
+
+// Row of position pos0 + min(i, nrows - 1) of a tile (a position inside the tile, so a
+// row-map read stays in bounds), or -1 for i >= nrows or a row outside [0, n_rows).
+// The per-lane read carries no branch of its own (only the uniform row-map test), so
+// the compiler does not wait for every load in flight before it.
+__device__ inline int tile_row(const TileSrc &ts, const TileHead &th, int i, int n_rows)
+{
+    const int pos = th.pos0 + min(i, th.nrows - 1);
+    const bool pin = !ts.row_map || (pos >= 0 && pos < ts.n_pos);
+    const int row = ts.row_map ? ts.row_map[min(max(pos, 0), max(ts.n_pos - 1, 0))] : pos;
+    return (i < th.nrows && pin && row >= 0 && row < n_rows) ? row : -1;
+}
+
+// CW fp16 values (CW = 8 or 4) in 16 or 8 bytes.
+template <int CW>
+struct HalfVec {
+    uint32_t w[CW / 2];
+    __device__ uint32_t half(int m) const { return (m & 1) ? (w[m >> 1] >> 16) : (w[m >> 1] & 0xffff); }
+};
+
+template <int CW>
+__device__ inline HalfVec<CW> load_halves(const uint16_t *p)
+{
+    HalfVec<CW> h;
+    if constexpr (CW == 8) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(p);
+        h.w[0] = q.x, h.w[1] = q.y, h.w[2] = q.z, h.w[3] = q.w;
+    } else {
+        const uint2 q = *reinterpret_cast<const uint2 *>(p);
+        h.w[0] = q.x, h.w[1] = q.y;
+    }
+    return h;
+}
+
+template <int CW>
+__device__ inline void store_halves(uint16_t *p, const HalfVec<CW> &h)
+{
+    if constexpr (CW == 8) *reinterpret_cast<uint4 *>(p) = make_uint4(h.w[0], h.w[1], h.w[2], h.w[3]);
+    else *reinterpret_cast<uint2 *>(p) = make_uint2(h.w[0], h.w[1]);
+}
+
+// keep a loaded value in flight where it was issued (see the callers)
+template <int CW>
+__device__ inline void pin(HalfVec<CW> &h)
+{
+#pragma unroll
+    for (int i = 0; i < CW / 2; ++i) asm volatile("" : "+v"(h.w[i]));
+}
+
+template <bool PAGED, int RQ, int CW, bool OFFS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void lora_expand_t16_kernel(Args args)
+{
+    static_assert(CW == 8 || CW == 4, "columns per lane");
+    constexpr int NB = 4 * RQ;  // rank-rows of B per lane: 4 in each 16-rank step
+    const Args &a = kernel_args<!PAGED>(args);
+    const Item it = work_by_slice(a);
+    if (!it.ok) return;
+    prepare_tile<false, OFFS, kThreads>(a.ts, a.n_rows, it.tile);
+    const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
+    TileHead th = tile_head<false, OFFS>(a.ts, pd.w, it.tile);
+    // uniform: the slot's rank, scale and B addresses come from scalar loads
+    th.slot = __builtin_amdgcn_readfirstlane(th.slot);
+    th.pos0 = __builtin_amdgcn_readfirstlane(th.pos0);
+    th.nrows = __builtin_amdgcn_readfirstlane(th.nrows);
+    if (!th.valid) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+    const int c = it.slice * (64 * CW) + 16 * CW * wave + CW * li;  // this lane's CW columns
+    const bool cin = c < pd.w.d_out;
+    const int cc = cin ? c : pd.w.d_out - CW;  // in-bounds stand-in (d_out is a multiple of 8)
+    // operand row li of the first 16-row block; the rows this lane updates, 4 lg + e, are
+    // the operand rows of lanes 4 lg + e
+    int vr = tile_row(a.ts, th, li, a.n_rows);
+    const int rank = slot_rank(pd.w, th.slot);
+    const float sc = pd.w.scale[th.slot];
+    const int r4 = (pd.w.r_max + 3) & ~3;  // a v row holds at least this many floats (ldv % 4 == 0)
+    // B rank-rows 16 s + 4 lg + i at columns c .. c + 7.  Rank-rows below r_max are in
+    // bounds (dense) or have their page-table entries checked (paged), so no load waits
+    // for the rank.  Paged: page ids first (reads without a branch, so that what follows
+    // waits for them alone), then v and y, then B's data.
+    HalfVec<CW> bq[NB];
+    int bpg[NB];
+    const int P = PAGED ? pd.w.page_elems : 1, pq = cc / P, within = cc - pq * P;
+    if (PAGED) {
+        const int64_t ptb = pt_base<true>(pd.w, th.slot);
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {
+            const int j = min(16 * (k >> 2) + 4 * lg + (k & 3), pd.w.r_max - 1);
+            const int64_t off = ptb + (int64_t)j * (pd.w.d_out / P) + pq;
+            const bool in = off >= 0 && off < pd.w.pt_entries;
+            const int e = pd.w.page_table[in ? off : 0];
+            bpg[k] = in ? e : -1;
+        }
+    }
+    float4 vq[RQ];
+#pragma unroll
+    for (int s = 0; s < RQ; ++s)
+        vq[s] = *reinterpret_cast<const float4 *>(pd.v + (int64_t)max(vr, 0) * pd.ldv + min(16 * s + 4 * lg, r4 - 4));
+    int yr[4];
+    HalfVec<CW> yv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        yr[e] = __shfl(vr, 4 * lg + e);
+        yv[e] = load_halves<CW>(pd.y + (int64_t)max(yr[e], 0) * pd.ldy + cc);
+    }
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+        if (!PAGED) {
+            bpg[k] = 0;
+            bq[k] = load_halves<CW>(dense_row<true>(pd.w, th.slot, min(16 * (k >> 2) + 4 * lg + (k & 3), pd.w.r_max - 1)) +
+                                    cc);
+        } else {
+            bpg[k] = page_ok(pd.w, bpg[k]);  // page 0 stands in for a missing entry
+            bq[k] = load_halves<CW>(page_ptr(pd.w, max(bpg[k], 0), within));
+        }
+    }
+    // keep the y loads here, in flight with the others: otherwise the compiler sinks them
+    // into the conditional update at the end, one more round trip after the products
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pin<CW>(yv[e]);
+    // B rank-rows at or past the rank (NaN in unfilled storage), past d_out or without a page: 0
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+        if (!(cin && 16 * (k >> 2) + 4 * lg + (k & 3) < rank && bpg[k] >= 0))
+#pragma unroll
+            for (int i = 0; i < CW / 2; ++i) bq[k].w[i] = 0;
+    // A rank-0 slot stores nothing (y stays as it is, bit for bit); tested as a predicate
+    // at the store rather than by an early return, which the compiler would hoist above
+    // the loads and so hold them back behind the rank.
+    for (int m0 = 0;;) {
+        // row li's scale 2^ex: above max_j |s v[row][j]| (its four 16-lane groups)
+        float mx = 0.f;
+#pragma unroll
+        for (int s = 0; s < RQ; ++s) {
+            const float sv[4] = {vq[s].x, vq[s].y, vq[s].z, vq[s].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (vr >= 0 && 16 * s + 4 * lg + e < rank) mx = __builtin_fmaxf(mx, __builtin_fabsf(sc * sv[e]));
+        }
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
+        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+        const int ex = mx > 0.f && mx <= 3.0e38f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+        f4_t acc[CW];
+#pragma unroll
+        for (int m = 0; m < CW; ++m) acc[m] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < RQ; ++s) {
+            if (16 * s >= rank) break;
+            const float sv[4] = {vq[s].x, vq[s].y, vq[s].z, vq[s].w};
+            h4_t vhi, vlo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float m = (vr >= 0 && 16 * s + 4 * lg + e < rank) ? __builtin_ldexpf(sc * sv[e], -ex) : 0.f;
+                const _Float16 hv = (_Float16)m;
+                vhi[e] = hv;
+                vlo[e] = (_Float16)((m - (float)hv) * 2048.f);
+            }
+#pragma unroll
+            for (int m = 0; m < CW; ++m) {
+                // column c + m of rank-rows 16 s + 4 lg .. + 3
+                const uint32_t lo2 = bq[4 * s].half(m) | (bq[4 * s + 1].half(m) << 16);
+                const uint32_t hi2 = bq[4 * s + 2].half(m) | (bq[4 * s + 3].half(m) << 16);
+                const h4_t bop = __builtin_bit_cast(h4_t, make_uint2(lo2, hi2));
+                f4_t lo = f4_t{0.f, 0.f, 0.f, 0.f};
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x16f16(vhi, bop, acc[m], 0, 0, 0);
+                lo = __builtin_amdgcn_mfma_f32_16x16x16f16(vlo, bop, lo, 0, 0, 0);
+                acc[m] += lo * (1.f / 2048.f);
+            }
+        }
+        // lane (li, lg): acc[m][e] = row 4 lg + e, column c + m, in units of that row's 2^ex
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int exr = __shfl(ex, 4 * lg + e);
+            if (yr[e] >= 0 && cin && rank > 0) {
+                HalfVec<CW> out;
+#pragma unroll
+                for (int e2 = 0; e2 < CW / 2; ++e2) {
+                    const float lo = h2f((uint16_t)yv[e].half(2 * e2)) + __builtin_ldexpf(acc[2 * e2][e], exr);
+                    const float hi = h2f((uint16_t)yv[e].half(2 * e2 + 1)) + __builtin_ldexpf(acc[2 * e2 + 1][e], exr);
+                    out.w[e2] = (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
+                }
+                store_halves<CW>(pd.y + (int64_t)yr[e] * pd.ldy + c, out);
+            }
+        }
+        m0 += 16;
+        if (m0 >= th.nrows) break;
+        // a tile taller than the planned 16 rows: the next block's v and y
+        vr = tile_row(a.ts, th, m0 + li, a.n_rows);
+#pragma unroll
+        for (int s = 0; s < RQ; ++s)
+            vq[s] = *reinterpret_cast<const float4 *>(pd.v + (int64_t)max(vr, 0) * pd.ldv +
+                                                      min(16 * s + 4 * lg, r4 - 4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            yr[e] = __shfl(vr, 4 * lg + e);
+            yv[e] = load_halves<CW>(pd.y + (int64_t)max(yr[e], 0) * pd.ldy + cc);
+        }
+    }
+}
+
 // ------------------------------------------------------------------------ one launch, v handed off
 // Shrink and expand in one launch, v passed from the shrink's workgroups to the
 // expand's through a caller-owned workspace: the per-row form, and the segment form
@@ -1896,15 +2119,30 @@ int expand_impl(void *stream, int32_t n_rows, TileSrc ts, int32_t n_tiles, int32
     if (n_rows == 0 || n_tiles == 0) return LORA_OK;
     int32_t r_max = 0;
     for (int32_t p = 0; p < n_proj; ++p) r_max = std::max(r_max, proj[p].w->r_max);
-    const bool mfma = !PERROW && max_rows >= kMfmaMinRows;
-    for (int32_t p = 0; p < n_proj; ++p) a.p[p].slices = (proj[p].w->d_out + kCols - 1) / kCols;
+    // tiles of 8 to 16 rows: the register-only MFMA expand; taller: the LDS-staged MFMA
+    // expand; shorter: VALU (whose results the one-launch segment form reproduces bit
+    // for bit)
+    const bool t16 = !PERROW && max_rows >= kMfmaMinRows && max_rows <= 16;
+    const bool mfma = !PERROW && max_rows > 16;
+    const int cols = t16 && r_max > 32 ? 256 : kCols;  // the tall-tile kernel's columns per workgroup
+    for (int32_t p = 0; p < n_proj; ++p) a.p[p].slices = (proj[p].w->d_out + cols - 1) / cols;
     if ((st = finish_layout(a, n_tiles))) return st;
     a.n_rows = n_rows;
     a.n_tiles = n_tiles;
     a.ts = ts;
     const dim3 grid((unsigned)a.grid);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (mfma) {
+    if (t16) {
+#define LORA_EXPAND_T16(RQ)                                                                          \
+    (paged ? launch(lora_expand_t16_kernel<true, RQ, (RQ > 2 ? 4 : 8), OFFS>, grid, kThreads, 0, s, a) \
+           : launch(lora_expand_t16_kernel<false, RQ, (RQ > 2 ? 4 : 8), OFFS>, grid, kThreads, 0, s, a))
+        const int rq = (r_max + 15) / 16;
+        if (rq == 1) LORA_EXPAND_T16(1);
+        else if (rq == 2) LORA_EXPAND_T16(2);
+        else if (rq == 3) LORA_EXPAND_T16(3);
+        else LORA_EXPAND_T16(4);
+#undef LORA_EXPAND_T16
+    } else if (mfma) {
         const int rq = (r_max + 15) / 16;
         const size_t lds = (size_t)kCols * bt_stride(rq) * sizeof(uint16_t);
         const size_t lds_sy = lds + (size_t)16 * kYStride * sizeof(uint16_t);  // dense: plus the staged y slice

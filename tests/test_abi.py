@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
+from segmented_gather_matmul_amd import workloads as wl
 from segmented_gather_matmul_amd import binding as B
 from segmented_gather_matmul_amd import build as build_mod
 
@@ -33,7 +34,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 35 and set(names) == set(B.EXPORTS)
+    assert len(names) == 36 and set(names) == set(B.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", build_mod.LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (lora_\w+)", out))
@@ -368,6 +369,22 @@ def test_pick_tile_rows():
     assert B.lora_pick_tile_rows(np.array([0, 5, 133], np.int32)) == 64         # one of 128 or more
     assert B.lora_pick_tile_rows(np.array([0, 128], np.int32)) == 64
     assert B.lora_pick_tile_rows(np.array([0], np.int32)) == 2                  # no segments
+
+
+def test_pick_expand_tile_rows():
+    """16-row expand tiles for decode batches whose 16-row tiles average >= 6 rows; else
+    the general choice (2 for short segments, 64 for long ones)."""
+    seg = wl.segments_from_lengths
+    assert B.lora_pick_expand_tile_rows(seg([58])) == 16                        # identical mix
+    assert B.lora_pick_expand_tile_rows(seg([30, 11, 9, 5, 1, 1, 1])) == 16     # skewed mix: 58 rows, 8 tiles
+    assert B.lora_pick_expand_tile_rows(seg([6, 5, 5, 5, 4, 4, 4, 4, 3, 3, 3, 3, 2, 2, 1])) == 2  # uniform
+    assert B.lora_pick_expand_tile_rows(seg([58, 31, 14, 11, 10, 8] + [1] * 92)) == 2   # paged pool mix
+    assert B.lora_pick_expand_tile_rows(seg([7, 7, 7])) == 2                    # no tile reaches 8 rows
+    assert B.lora_pick_expand_tile_rows(seg([5, 6, 1])) == 2                    # 12 rows in 3 tiles
+    assert B.lora_pick_expand_tile_rows(seg([0, 12, 0])) == 16                  # empty segments ignored
+    assert B.lora_pick_expand_tile_rows(seg([5, 200])) == 64                    # prefill: long segments
+    assert B.lora_pick_expand_tile_rows(np.array([0], np.int32)) == 2           # no segments
+    assert B.lora_pick_expand_tile_rows(np.array([0, 9], np.int32)) == 16
 
 
 # ------------------------------------------------------------------ offsets form of the segment descriptor
