@@ -23,19 +23,16 @@
 //   - tiles of 8..64 rows: v_mfma_f32_16x16x32_f16 over 16-rank slices, up to four of
 //     them (across the launch's projections) sharing each read of the tile's x rows;
 //     16 wavefronts split d_in.
-// Expand.  A workgroup owns 512 output columns of one tile (256 in the 8..16-row kernel
-// at ranks above 32).
+// Expand.  A workgroup owns 512 output columns of one tile (256 in the MFMA kernel at
+// ranks above 32).
 //   - tiles of < 8 rows: each wavefront loads its quarter of the rank-rows of B once
 //     (16-byte loads, contiguous in d_out, all in flight together), the quarters are
 //     added in LDS, and one fp32 -> fp16 rounding updates y;
-//   - tiles of 8..16 rows (decode batches with rows sharing adapters): each wavefront
-//     holds its columns of every rank-row of B in registers and runs
-//     v_mfma_f32_16x16x16_f16 on s v (fp16 hi + lo/2048 parts) x B, so B is read once
-//     per 16 rows; no LDS;
-//   - tiles of 17..64 rows: B[0:r][512 columns] is staged transposed in LDS and reused
-//     by every 16-row slice; D^T = B^T (s v)^T runs on v_mfma_f32_16x16x16_f16 with s*v
-//     split into fp16 hi + lo/2048 parts (two MFMAs, ~22 bits kept); the accumulator
-//     starts from y and each lane moves 8 consecutive y elements of one row.
+//   - tiles of 8..64 rows: each wavefront holds its columns of every rank-row of B in
+//     registers and runs v_mfma_f32_16x16x16_f16 on s v (fp16 hi + lo/2048 parts, ~22
+//     bits kept) x B, one 16-row block after another, the next block's y and v
+//     requested before the current block's products; B is read once per tile, y and v
+//     move in whole lines, and nothing passes through LDS.
 // The per-row and the segment forms of decode batches also run both steps in one launch,
 // the shrink's workgroups handing v to the expand's (lora_handoff_kernel).
 #include <hip/hip_ext.h>
@@ -1150,10 +1147,10 @@ void lora_expand_valu_kernel(Args args)
     expand_pass<PERROW, NR, RU>(pd, ps, sc, rank, bv, yv, c, cin, red);
 }
 
-// Expand for tiles of 8 to 16 rows (the short segments of decode batches): workgroup =
-// (tile, 64 CW output columns, projection), each wavefront 16 CW of the columns with
-// every rank-row, so each adapter's B is read once per 16 rows, where the VALU expand's
-// 2-row tiles read it once per 2, and no sums cross wavefronts.  CW (8 or 4 columns per
+// MFMA expand for tiles of 8 to 64 rows (prefill segments, and decode batches whose rows
+// share adapters): workgroup = (tile, 64 CW output columns, projection), each wavefront
+// 16 CW of the columns with every rank-row, so each adapter's B is read once per tile
+// (the VALU expand's 2-row tiles read it once per 2 rows) and no sums cross wavefronts.  CW (8 or 4 columns per
 // lane) trades columns per workgroup for registers: 4 at ranks above 32.  Products on
 // v_mfma_f32_16x16x16_f16 with A = s v (16 rows x 16 ranks, split into fp16 hi +
 // lo/2048 parts: two MFMAs, ~22 bits kept) and B = the rank-rows, exact in fp16.  In
@@ -1166,9 +1163,11 @@ void lora_expand_valu_kernel(Args args)
 // run on s v 2^-ex with 2^ex above the row's largest |s v|, and the sum is scaled back,
 // so the fp16 parts stay in fp16's normal range whatever the magnitude of v.  Every load
 // is issued from an in-bounds (clamped) address and masked where its value is used, so
-// a tile's loads are in flight together.  Work items are slice-major, as in the VALU
-// expand.  Tiles taller than 16 rows (the row height is only a hint) take one 16-row
-// block after another with B kept in registers.
+// a tile's loads are in flight together.  Tiles taller than 16 rows take one 16-row
+// block after another with B kept in registers, the next block's v and y requested
+// before the current block's products.  Work items are slice-major for tiles of up to 16
+// rows (the tiles of one adapter then reuse each B chunk from L2, as in the VALU expand)
+// and tile-major for taller tiles (prefill: consecutive workgroups sweep whole y rows).
 
 // Row of position pos0 + min(i, nrows - 1) of a tile (a position inside the tile, so a
 // row-map read stays in bounds), or -1 for i >= nrows or a row outside [0, n_rows).
@@ -1218,13 +1217,19 @@ __device__ inline void pin(HalfVec<CW> &h)
     for (int i = 0; i < CW / 2; ++i) asm volatile("" : "+v"(h.w[i]));
 }
 
-template <bool PAGED, int RQ, int CW, bool OFFS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void lora_expand_t16_kernel(Args args)
+// Wavefronts per SIMD the MFMA expand is built for: four (at most 128 VGPRs) where that
+// needs no spills, else three.
+template <int RQ, int CW, bool TM>
+constexpr int expand_mfma_waves() { return (TM && RQ > 1) || (!TM && RQ == 2) ? 3 : 4; }
+
+template <bool PAGED, int RQ, int CW, bool TM, bool OFFS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(expand_mfma_waves<RQ, CW, TM>())))
+void lora_expand_mfma_kernel(Args args)
 {
     static_assert(CW == 8 || CW == 4, "columns per lane");
     constexpr int NB = 4 * RQ;  // rank-rows of B per lane: 4 in each 16-rank step
     const Args &a = kernel_args<!PAGED>(args);
-    const Item it = work_by_slice(a);
+    const Item it = TM ? work(a) : work_by_slice(a);
     if (!it.ok) return;
     prepare_tile<false, OFFS, kThreads>(a.ts, a.n_rows, it.tile);
     const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
@@ -1298,6 +1303,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     // at the store rather than by an early return, which the compiler would hoist above
     // the loads and so hold them back behind the rank.
     for (int m0 = 0;;) {
+        // tile-major (tall tiles): the next 16-row block's rows, v and y go out before this
+        // block's products (otherwise, for a tile taller than the hint, after them)
+        const bool more = m0 + 16 < th.nrows;
+        int vr_n = -1, yr_n[4] = {-1, -1, -1, -1};
+        float4 vq_n[RQ];
+        HalfVec<CW> yv_n[4];
+        if (TM && more) {
+            vr_n = tile_row(a.ts, th, m0 + 16 + li, a.n_rows);
+#pragma unroll
+            for (int s = 0; s < RQ; ++s)
+                vq_n[s] = *reinterpret_cast<const float4 *>(pd.v + (int64_t)max(vr_n, 0) * pd.ldv +
+                                                            min(16 * s + 4 * lg, r4 - 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                yr_n[e] = __shfl(vr_n, 4 * lg + e);
+                yv_n[e] = load_halves<CW>(pd.y + (int64_t)max(yr_n[e], 0) * pd.ldy + cc);
+            }
+        }
         // row li's scale 2^ex: above max_j |s v[row][j]| (its four 16-lane groups)
         float mx = 0.f;
 #pragma unroll
@@ -1352,18 +1375,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                 store_halves<CW>(pd.y + (int64_t)yr[e] * pd.ldy + c, out);
             }
         }
+        if (!more) break;
         m0 += 16;
-        if (m0 >= th.nrows) break;
-        // a tile taller than the planned 16 rows: the next block's v and y
-        vr = tile_row(a.ts, th, m0 + li, a.n_rows);
+        if (TM) {
+            vr = vr_n;
 #pragma unroll
-        for (int s = 0; s < RQ; ++s)
-            vq[s] = *reinterpret_cast<const float4 *>(pd.v + (int64_t)max(vr, 0) * pd.ldv +
-                                                      min(16 * s + 4 * lg, r4 - 4));
+            for (int s = 0; s < RQ; ++s) vq[s] = vq_n[s];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            yr[e] = __shfl(vr, 4 * lg + e);
-            yv[e] = load_halves<CW>(pd.y + (int64_t)max(yr[e], 0) * pd.ldy + cc);
+            for (int e = 0; e < 4; ++e) {
+                yr[e] = yr_n[e];
+                yv[e] = yv_n[e];
+            }
+        } else {
+            vr = tile_row(a.ts, th, m0 + li, a.n_rows);
+#pragma unroll
+            for (int s = 0; s < RQ; ++s)
+                vq[s] = *reinterpret_cast<const float4 *>(pd.v + (int64_t)max(vr, 0) * pd.ldv +
+                                                          min(16 * s + 4 * lg, r4 - 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                yr[e] = __shfl(vr, 4 * lg + e);
+                yv[e] = load_halves<CW>(pd.y + (int64_t)max(yr[e], 0) * pd.ldy + cc);
+            }
         }
     }
 }
@@ -1590,246 +1623,6 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(const void *__re
         expand_pass<PERROW, NR, RU>(pd, ps, sc, rank, bv, yv, c, cin, red);
         if (wave == 0 && active)
             handoff_count<NR>(a.ho, ps.rows, it.p, 1u << 8, pd.slices, a.ho.e_slices[it.p], pd.w.r_max);
-    }
-}
-
-// MFMA expand for tiles of up to 64 rows.  B[0:r][512 columns] is staged in LDS
-// transposed, column-major with a padded stride (kBtPad), so the 4 consecutive ranks a
-// lane feeds to an MFMA are one 8-byte LDS read.  Per 16-row slice D^T[cols][rows] =
-// B^T (s v)^T runs with s*v split into fp16 hi + lo/2048 operands (two MFMAs, ~22
-// bits kept) and the accumulator starts from y.  MFMAs go in pairs whose output
-// columns are interleaved so that each lane ends up with 8 consecutive columns of one
-// row: y is read and written with 16-byte accesses.  The next slice's y and v are
-// requested before the current slice's products.  With SY (dense weights) the slice's
-// y passes through LDS: each wavefront loads and stores whole 1 KB rows (full cache
-// lines, where the operand layout touches 64 bytes of each of 16 rows), and the lanes
-// read and write their operand layout in LDS; the arithmetic is the same, so SY
-// changes no bits.
-constexpr int kBtPad = 4;  // halves of padding per column of the transposed B chunk
-constexpr int kYStride = kCols + 8;  // halves per row of the staged y slice (the pad spreads rows over banks)
-
-__host__ __device__ constexpr int bt_stride(int rq) { return 16 * rq + kBtPad; }
-
-template <bool PAGED, int RQ, bool SY, bool OFFS>
-__global__ __launch_bounds__(kThreads) void lora_expand_mfma_kernel(Args args)
-{
-    const Args &a = kernel_args<!PAGED>(args);
-    constexpr int kStage = RQ * 16 * (kCols / 8) / kThreads;  // 16-byte loads per lane to stage B
-    constexpr int KS = bt_stride(RQ);
-    extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t *bt = reinterpret_cast<uint16_t *>(smem);  // bt[col * KS + k] = B[k][c0 + col]
-    uint16_t *ys = bt + kCols * KS;                      // SY: y of the slice, [16][kYStride]
-    const Item it = work(a);
-    if (!it.ok) return;
-    prepare_tile<false, OFFS, kThreads>(a.ts, a.n_rows, it.tile);
-    const ProjDev pd = a.p[it.p];  // by value: the fields stay in registers
-    const TileHead th = tile_head<false, OFFS>(a.ts, pd.w, it.tile);
-    if (!th.valid) return;
-    const int rank = slot_rank(pd.w, th.slot);
-    const float sc = pd.w.scale[th.slot];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int li = lane & 15, lg = lane >> 4;
-    const int c0 = it.slice * kCols;
-    const int cw = c0 + 128 * wave;  // this wavefront's 128 columns = 4 pairs of 16x16 products
-    const int MT = (th.nrows + 15) >> 4;
-    // Row, y (accumulator start) and v of 16-row slice mt: lane holds y[row][cw + 32 p +
-    // 8 lg .. +7] for pair p and v[row][16 kq + 4 lg .. +3].
-    auto slice_row = [&](int mt) {
-        const int rr = 16 * mt + li;
-        return (mt < MT && rr < th.nrows) ? row_of<false>(a.ts, th.pos0 + rr, a.n_rows) : -1;
-    };
-    auto load_yv = [&](int row, uint4 (&yq)[4], float4 (&vq)[RQ]) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int col = cw + 32 * p + 8 * lg;
-            yq[p] = (!SY && row >= 0 && col < pd.w.d_out) ? load16(pd.y + (int64_t)row * pd.ldy + col)
-                                                           : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int kq = 0; kq < RQ; ++kq) {
-            const int j = 16 * kq + 4 * lg;
-            vq[kq] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (row >= 0 && j < pd.w.r_max) vq[kq] = *reinterpret_cast<const float4 *>(pd.v + (int64_t)row * pd.ldv + j);
-        }
-    };
-    // SY: wavefront w moves rows 4 w .. 4 w + 3 of a slice between memory and LDS, one
-    // whole 1 KB row per load or store (lane l: columns c0 + 8 l .. + 7)
-    const int ycol = c0 + 8 * lane;
-    const bool ycin = ycol < pd.w.d_out;
-    auto stage_rows = [&](int mt, int (&lrow)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = 16 * mt + 4 * wave + i;
-            lrow[i] = (mt < MT && rr < th.nrows) ? row_of<false>(a.ts, th.pos0 + rr, a.n_rows) : -1;
-        }
-    };
-    auto stage_load = [&](const int (&lrow)[4], uint4 (&yr)[4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            yr[i] = (lrow[i] >= 0 && ycin) ? load16(pd.y + (int64_t)lrow[i] * pd.ldy + ycol) : make_uint4(0, 0, 0, 0);
-    };
-    int lrow[4] = {-1, -1, -1, -1};
-    uint4 yr[4];
-    if (SY) {
-        stage_rows(0, lrow);
-        stage_load(lrow, yr);
-    }
-    int row = slice_row(0);
-    uint4 yq[4];
-    float4 vq[RQ];
-    load_yv(row, yq, vq);
-    {
-        // stage B while the y and v loads are in flight: all loads first, then LDS;
-        // rows past the rank become 0, rows past r_max (dense) are not read
-        uint4 q[kStage];
-        if (!PAGED) {
-#pragma unroll
-            for (int i = 0; i < kStage; ++i) {
-                const int o = tid + i * kThreads, k = o >> 6, oc = (o & 63) * 8;
-                q[i] = make_uint4(0, 0, 0, 0);
-                if (k < pd.w.r_max && k < rank && c0 + oc < pd.w.d_out) q[i] = load16(dense_row<true>(pd.w, th.slot, k) + c0 + oc);
-            }
-        } else {
-            // page ids first, then all the data
-            const int64_t ptb = pt_base<true>(pd.w, th.slot);
-            const int P = pd.w.page_elems;
-            int pg[kStage];
-#pragma unroll
-            for (int i = 0; i < kStage; ++i) {
-                const int o = tid + i * kThreads, k = o >> 6, c = c0 + (o & 63) * 8;
-                pg[i] = (k < rank && c < pd.w.d_out) ? page_entry<true>(pd.w, ptb, k, c / P) : -1;
-            }
-#pragma unroll
-            for (int i = 0; i < kStage; ++i) {
-                const int o = tid + i * kThreads, c = c0 + (o & 63) * 8;
-                q[i] = make_uint4(0, 0, 0, 0);
-                const int g = page_ok(pd.w, pg[i]);
-                if (g >= 0) q[i] = load16(page_ptr(pd.w, g, c % P));
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < kStage; ++i) {
-            const int o = tid + i * kThreads, k = o >> 6, oc = (o & 63) * 8;
-            const uint32_t w4[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bt[(oc + 2 * e) * KS + k] = (uint16_t)(w4[e] & 0xffff);
-                bt[(oc + 2 * e + 1) * KS + k] = (uint16_t)(w4[e] >> 16);
-            }
-        }
-        __syncthreads();
-        if (rank <= 0) return;
-    }
-    for (int mt = 0; mt < MT; ++mt) {
-        if (SY) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(ys + (4 * wave + i) * kYStride + 8 * lane) = yr[i];
-            __syncthreads();
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-                yq[p] = *reinterpret_cast<const uint4 *>(ys + li * kYStride + 128 * wave + 32 * p + 8 * lg);
-        }
-        // the next slice's loads go out before this slice's products
-        const int row_n = slice_row(mt + 1);
-        uint4 yn[4];
-        float4 vn[RQ];
-        int lrow_n[4] = {-1, -1, -1, -1};
-        if (mt + 1 < MT) {
-            load_yv(row_n, yn, vn);
-            if (SY) {
-                stage_rows(mt + 1, lrow_n);
-                stage_load(lrow_n, yr);
-            }
-        }
-        // Row li's power-of-two exponent ex with max_j |s v[row][j]| < 2^ex: the products
-        // run on s v 2^-ex and y 2^-ex, and the result is scaled back by 2^ex, so the fp16
-        // hi/lo parts of s v stay inside fp16's normal range whatever the magnitude of v
-        // (a power-of-two scaling changes no rounding while nothing overflows or
-        // underflows, so in-range values give the same bits as unscaled arithmetic).
-        float mx = 0.f;
-#pragma unroll
-        for (int kq = 0; kq < RQ; ++kq) {
-            const float sv[4] = {vq[kq].x, vq[kq].y, vq[kq].z, vq[kq].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (16 * kq + 4 * lg + e < rank) mx = __builtin_fmaxf(mx, __builtin_fabsf(sc * sv[e]));
-        }
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));  // the row's four k-groups
-        mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-        const int ex = mx > 0.f && mx <= 3.0e38f ? __builtin_amdgcn_frexp_expf(mx) : 0;
-        f4_t acc[4][2];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t yw[4] = {yq[p].x, yq[p].y, yq[p].z, yq[p].w};
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                acc[p][h] = f4_t{__builtin_ldexpf(h2f((uint16_t)(yw[2 * h] & 0xffff)), -ex),
-                                 __builtin_ldexpf(h2f((uint16_t)(yw[2 * h] >> 16)), -ex),
-                                 __builtin_ldexpf(h2f((uint16_t)(yw[2 * h + 1] & 0xffff)), -ex),
-                                 __builtin_ldexpf(h2f((uint16_t)(yw[2 * h + 1] >> 16)), -ex)};
-        }
-#pragma unroll
-        for (int kq = 0; kq < RQ; ++kq) {
-            if (16 * kq >= rank) break;
-            const int j = 16 * kq + 4 * lg;
-            const float sv[4] = {vq[kq].x, vq[kq].y, vq[kq].z, vq[kq].w};
-            h4_t vhi, vlo;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float m = (j + e < rank) ? __builtin_ldexpf(sc * sv[e], -ex) : 0.f;
-                const _Float16 hv = (_Float16)m;
-                vhi[e] = hv;
-                vlo[e] = (_Float16)((m - (float)hv) * 2048.f);
-            }
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    // A operand: B^T row li of this product = column 32 p + 8 (li / 4) + 4 h + li % 4
-                    // of the wavefront's range, ranks j .. j+3 (one 8-byte LDS read)
-                    const int lc = 128 * wave + 32 * p + 8 * (li >> 2) + 4 * h + (li & 3);
-                    const h4_t bop = *reinterpret_cast<const h4_t *>(bt + lc * KS + j);
-                    f4_t lo = f4_t{0.f, 0.f, 0.f, 0.f};
-                    acc[p][h] = __builtin_amdgcn_mfma_f32_16x16x16f16(bop, vhi, acc[p][h], 0, 0, 0);
-                    lo = __builtin_amdgcn_mfma_f32_16x16x16f16(bop, vlo, lo, 0, 0, 0);
-                    acc[p][h] += lo * (1.f / 2048.f);
-                }
-        }
-        if (SY || row >= 0) {
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int col = cw + 32 * p + 8 * lg;
-                if (!SY && col >= pd.w.d_out) continue;
-                uint32_t o[4];
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int e2 = 0; e2 < 2; ++e2)
-                        o[2 * h + e2] = (uint32_t)f2h(__builtin_ldexpf(acc[p][h][2 * e2], ex)) |
-                                        ((uint32_t)f2h(__builtin_ldexpf(acc[p][h][2 * e2 + 1], ex)) << 16);
-                const uint4 ov = make_uint4(o[0], o[1], o[2], o[3]);
-                if (SY) *reinterpret_cast<uint4 *>(ys + li * kYStride + 128 * wave + 32 * p + 8 * lg) = ov;
-                else *reinterpret_cast<uint4 *>(pd.y + (int64_t)row * pd.ldy + col) = ov;
-            }
-        }
-        if (SY) {
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (lrow[i] >= 0 && ycin)
-                    *reinterpret_cast<uint4 *>(pd.y + (int64_t)lrow[i] * pd.ldy + ycol) =
-                        *reinterpret_cast<const uint4 *>(ys + (4 * wave + i) * kYStride + 8 * lane);
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lrow[i] = lrow_n[i];
-        }
-        if (mt + 1 < MT) {
-            row = row_n;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) yq[p] = yn[p];
-#pragma unroll
-            for (int kq = 0; kq < RQ; ++kq) vq[kq] = vn[kq];
-        }
     }
 }
 
@@ -2119,12 +1912,11 @@ int expand_impl(void *stream, int32_t n_rows, TileSrc ts, int32_t n_tiles, int32
     if (n_rows == 0 || n_tiles == 0) return LORA_OK;
     int32_t r_max = 0;
     for (int32_t p = 0; p < n_proj; ++p) r_max = std::max(r_max, proj[p].w->r_max);
-    // tiles of 8 to 16 rows: the register-only MFMA expand; taller: the LDS-staged MFMA
-    // expand; shorter: VALU (whose results the one-launch segment form reproduces bit
-    // for bit)
-    const bool t16 = !PERROW && max_rows >= kMfmaMinRows && max_rows <= 16;
-    const bool mfma = !PERROW && max_rows > 16;
-    const int cols = t16 && r_max > 32 ? 256 : kCols;  // the tall-tile kernel's columns per workgroup
+    // tiles of 8 rows or more: the MFMA expand (tile-major items above 16 rows); shorter:
+    // VALU (whose results the one-launch segment form reproduces bit for bit)
+    const bool mfma = !PERROW && max_rows >= kMfmaMinRows;
+    const bool tm = max_rows > 16;
+    const int cols = mfma && r_max > 32 ? 256 : kCols;  // the MFMA expand's columns per workgroup
     for (int32_t p = 0; p < n_proj; ++p) a.p[p].slices = (proj[p].w->d_out + cols - 1) / cols;
     if ((st = finish_layout(a, n_tiles))) return st;
     a.n_rows = n_rows;
@@ -2132,23 +1924,13 @@ int expand_impl(void *stream, int32_t n_rows, TileSrc ts, int32_t n_tiles, int32
     a.ts = ts;
     const dim3 grid((unsigned)a.grid);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (t16) {
-#define LORA_EXPAND_T16(RQ)                                                                          \
-    (paged ? launch(lora_expand_t16_kernel<true, RQ, (RQ > 2 ? 4 : 8), OFFS>, grid, kThreads, 0, s, a) \
-           : launch(lora_expand_t16_kernel<false, RQ, (RQ > 2 ? 4 : 8), OFFS>, grid, kThreads, 0, s, a))
+    if (mfma) {
+#define LORA_EXPAND_MFMA(RQ)                                                                             \
+    (paged ? (tm ? launch(lora_expand_mfma_kernel<true, RQ, (RQ > 2 ? 4 : 8), true, OFFS>, grid, kThreads, 0, s, a)   \
+                 : launch(lora_expand_mfma_kernel<true, RQ, (RQ > 2 ? 4 : 8), false, OFFS>, grid, kThreads, 0, s, a))  \
+           : (tm ? launch(lora_expand_mfma_kernel<false, RQ, (RQ > 2 ? 4 : 8), true, OFFS>, grid, kThreads, 0, s, a)  \
+                 : launch(lora_expand_mfma_kernel<false, RQ, (RQ > 2 ? 4 : 8), false, OFFS>, grid, kThreads, 0, s, a)))
         const int rq = (r_max + 15) / 16;
-        if (rq == 1) LORA_EXPAND_T16(1);
-        else if (rq == 2) LORA_EXPAND_T16(2);
-        else if (rq == 3) LORA_EXPAND_T16(3);
-        else LORA_EXPAND_T16(4);
-#undef LORA_EXPAND_T16
-    } else if (mfma) {
-        const int rq = (r_max + 15) / 16;
-        const size_t lds = (size_t)kCols * bt_stride(rq) * sizeof(uint16_t);
-        const size_t lds_sy = lds + (size_t)16 * kYStride * sizeof(uint16_t);  // dense: plus the staged y slice
-#define LORA_EXPAND_MFMA(RQ)                                                                 \
-    (paged ? launch(lora_expand_mfma_kernel<true, RQ, false, OFFS>, grid, kThreads, lds, s, a)     \
-           : launch(lora_expand_mfma_kernel<false, RQ, true, OFFS>, grid, kThreads, lds_sy, s, a))
         if (rq == 1) LORA_EXPAND_MFMA(1);
         else if (rq == 2) LORA_EXPAND_MFMA(2);
         else if (rq == 3) LORA_EXPAND_MFMA(3);
