@@ -22,7 +22,11 @@
 //     loads of x rows and A^T rank-rows, both contiguous in d_in, many in flight;
 //   - tiles of 8..64 rows: v_mfma_f32_16x16x32_f16 over 16-rank slices, up to four of
 //     them (across the launch's projections) sharing each read of the tile's x rows;
-//     16 wavefronts split d_in.
+//     16 wavefronts split d_in, which goes through LDS in 512-column chunks; a single
+//     slice on 64-row tiles (one projection of rank <= 16) takes the wave-staged kernel
+//     instead: two 32-row workgroups per tile, four wavefronts that each stage their own
+//     128-column chunks through LDS, with no barrier in the k loop.  Every MFMA shrink
+//     sums each element in the same order, so all give the same bits.
 // Expand.  A workgroup owns 512 output columns of one tile (256 in the MFMA kernel at
 // ranks above 32).
 //   - tiles of < 8 rows: each wavefront loads its quarter of the rank-rows of B once
@@ -868,7 +872,7 @@ __device__ inline void stage_load(const uint16_t *const (&src)[RPW], int k, int 
     for (int i = 0; i < RPW; ++i) st[i] = (src[i] && k < d_in) ? load16(src[i] + k) : z4;
 }
 
-template <int MTX, int NS, int RB, bool OFFS>
+template <int MTX, int NS, bool OFFS>
 __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_kernel(Args args)
 {
     const Args &a = kernel_args<true>(args);
@@ -879,10 +883,9 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_ke
     uint16_t *stg = reinterpret_cast<uint16_t *>(smem);  // [ROWS][kStageStride]
     float *red = reinterpret_cast<float *>(smem);        // reused after the k loop
     const int wi = work_item(blockIdx.x, a.grid);
-    // work item: (tile, row block b of RB, group of NS rank slices)
+    // work item: (tile, group of NS rank slices)
     const int groups = (a.per_tile + NS - 1) / NS;
-    const int tile = wi / (groups * RB), rem = wi - tile * (groups * RB);
-    const int b = RB == 1 ? 0 : rem / groups, g0 = (rem - b * groups) * NS;
+    const int tile = wi / groups, g0 = (wi - tile * groups) * NS;
     if (tile >= a.n_tiles) return;
     prepare_tile<false, OFFS, kMfmaShrinkThreads>(a.ts, a.n_rows, tile);
     const TileHead th = tile_head<false, OFFS>(a.ts, a.p[0].w, tile);
@@ -890,10 +893,9 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_ke
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
     const MfmaSlices<NS> m = mfma_slices<NS>(a, th.slot, g0);
-    // The tile's rows XR at a time: block b of every RB (one block per workgroup for the
-    // tile heights the launch was planned for; the row height is only a hint).  RB > 1
-    // spreads one tile's rows over RB workgroups, each reading the slices' A^T itself.
-    for (int m0 = b * XR; m0 < th.nrows; m0 += RB * XR) {
+    // The tile's rows XR at a time (one block for the tile heights the launch was planned
+    // for; the row height is only a hint).
+    for (int m0 = 0; m0 < th.nrows; m0 += XR) {
     const TileHead tb{th.slot, th.pos0 + m0, th.nrows - m0, th.valid};
     const int MT = min((tb.nrows + 15) >> 4, MTX);
     // staged row r: x row r of the block (r < XR), else A^T rank-row of slice (r - XR) / 16
@@ -944,6 +946,230 @@ __global__ __launch_bounds__(kMfmaShrinkThreads) void lora_shrink_mfma_staged_ke
         __syncthreads();
     }
     mfma_shrink_store<MTX, NS>(a, tb, m, MT, acc, red);
+    }
+}
+
+// MFMA shrink with four wavefronts and no barrier inside the k loop, for RB workgroups
+// of 16 * MTX rows per tile and NS rank slices per workgroup (the planner launches it for
+// a single slice on 64-row tiles: MTX 2, RB 2, NS 1).  Wavefront w takes the 128-column
+// chunks w, w + 4, w + 8, ... of d_in.  Each chunk's x rows and the slices' A^T
+// rank-rows are loaded as 256-byte row spans (four rows per load instruction), written
+// to the wavefront's own LDS region (16-byte groups XOR-swizzled by row, so both the
+// row-span writes and the operand reads spread over the banks) and read back in the
+// MFMA operand layout while the next chunk's loads are in flight.  A chunk holds the
+// 32-wide k-steps 4c .. 4c+3 of d_in; k-step kk is accumulated into class kk mod 16
+// (classes 4w .. 4w+3 in wavefront w), in ascending kk, and the 16 classes are added in
+// LDS in class order.  That is the summation order of the other MFMA shrinks (16
+// wavefronts, wavefront w owning k-steps w, w + 16, ...), so every MFMA shrink gives the
+// same bits.  Against the staged kernel it drops the two workgroup barriers per chunk,
+// each of which waits for the slowest of the chunk's row loads.
+constexpr int kWaveChunk = 128;                      // columns per chunk: 4 k-steps
+constexpr int kWaveBlock = 16 * kWaveChunk / 8;      // 16-byte groups of one staged 16-row block
+
+__host__ __device__ constexpr size_t wave_lds_bytes(int mtx, int ns)
+{
+    // the wavefronts' staged blocks, or the 16 classes' sums (16 * mtx KB) after the k loop
+    return (size_t)kWaves * (mtx + ns) * kWaveBlock * 16;
+}
+
+// v where c holds, else zero.  A value select: `c ? v : z` of two lvalues is an lvalue
+// that clang forms by selecting between their addresses, which puts both in scratch.
+__device__ inline uint4 keep_if(bool c, uint4 v) { return c ? v : make_uint4(0, 0, 0, 0); }
+
+// Rows of block positions r[i] (relative to pos0) as row_of gives them, -1 for positions
+// at or past nrows: every row-map read is issued unconditionally (at a clamped index)
+// before any is used, so a lane's lookups take one round trip, not one each.
+template <int N>
+__device__ inline void rows_of_block(const TileSrc &ts, int n_rows, int pos0, int nrows, int (&r)[N])
+{
+    if (ts.row_map && ts.n_pos > 0) {
+        const int last = ts.n_pos - 1;
+        int v[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = ts.row_map[min(max(pos0 + r[i], 0), last)];
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int pos = pos0 + r[i];
+            r[i] = (r[i] < nrows && pos >= 0 && pos < ts.n_pos) ? v[i] : -1;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) r[i] = (!ts.row_map && r[i] < nrows) ? pos0 + r[i] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) r[i] = (r[i] >= 0 && r[i] < n_rows) ? r[i] : -1;
+}
+
+template <int MTX, int NS, int RB, bool OFFS>
+__global__ __launch_bounds__(kThreads) void lora_shrink_mfma_wave_kernel(Args args)
+{
+    const Args &a = kernel_args<true>(args);
+    constexpr int NB = MTX + NS;  // staged blocks per wavefront: x row blocks, then A^T per slice
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int wi = work_item(blockIdx.x, a.grid);
+    const int groups = (a.per_tile + NS - 1) / NS;
+    const int tile = wi / (groups * RB), rem = wi - tile * (groups * RB);
+    const int rbk = RB == 1 ? 0 : rem / groups, g0 = (rem - rbk * groups) * NS;
+    if (tile >= a.n_tiles) return;
+    prepare_tile<false, OFFS, kThreads>(a.ts, a.n_rows, tile);
+    const TileHead th = tile_head<false, OFFS>(a.ts, a.p[0].w, tile);
+    if (th.slot < 0 || th.nrows <= 0) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, li = lane & 15, lg = lane >> 4;
+    uint4 *const my = reinterpret_cast<uint4 *>(smem) + wave * NB * kWaveBlock;
+    float *const red = reinterpret_cast<float *>(smem);  // [16 classes][MTX][256], after the k loop
+    const MfmaSlices<NS> m = mfma_slices<NS>(a, th.slot, g0);
+    const int d_in = a.p[0].w.d_in;
+    const int nct = (d_in + kWaveChunk - 1) / kWaveChunk;
+    const int nc = (nct - wave + kWaves - 1) / kWaves;  // chunks wave, wave + 4, ...
+    // this lane loads 16-byte group li of rows 4i + lg (i = 0..3) of every staged block;
+    // past d_in it reloads the last group in range and the chunk masks it to zero
+    const int lim = d_in - 8 - 8 * li;
+    const bool tail = nct * kWaveChunk > d_in;
+    // A^T rank-rows past r_max or of a slice without work: x row 0 stands in, masked to zero
+    const uint16_t *ap[NS][4];
+    bool aok[NS][4];
+    bool amask = false;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+        const WeightsDev &w = a.p[m.sp[q]].w;
+        amask |= !(m.sok[q] && m.sj0[q] + 16 <= w.r_max);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int j = m.sj0[q] + 4 * i + lg;
+            aok[q][i] = m.sok[q] && j < w.r_max;
+            ap[q][i] = (aok[q][i] ? dense_row<false>(w, th.slot, j) : a.x) + 8 * li;
+        }
+    }
+    // The tile's rows 16 * MTX at a time: block rbk of every RB (one block per workgroup
+    // for the planned tile height; the row height is only a hint).
+    for (int m0 = rbk * 16 * MTX; m0 < th.nrows; m0 += RB * 16 * MTX) {
+        const int pos0 = th.pos0 + m0, nrows = th.nrows - m0;
+        const int MT = min((nrows + 15) >> 4, MTX);
+        // Rows of this lane's x loads (rows 16b + 4i + lg of the block) and of its v stores
+        // (rows 16b + tid / 16), all row-map reads in flight together.  Rows past the tile or
+        // without a source load x row 0; their results are not stored.
+        int rows[5 * MTX];
+#pragma unroll
+        for (int b = 0; b < MTX; ++b) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rows[4 * b + i] = 16 * b + 4 * i + lg;
+            rows[4 * MTX + b] = 16 * b + (tid >> 4);
+        }
+        rows_of_block<5 * MTX>(a.ts, a.n_rows, pos0, nrows, rows);
+        const uint16_t *xp[MTX][4];
+#pragma unroll
+        for (int b = 0; b < MTX; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xp[b][i] = a.x + (int64_t)max(rows[4 * b + i], 0) * a.ldx + 8 * li;
+        auto load = [&](int jc, uint4 (&X)[MTX][4], uint4 (&A)[NS][4]) __attribute__((always_inline)) {
+            const int k = min((kWaves * jc + wave) * kWaveChunk, lim);
+#pragma unroll
+            for (int b = 0; b < MTX; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) X[b][i] = load16(xp[b][i] + k);
+#pragma unroll
+            for (int q = 0; q < NS; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) A[q][i] = load16(ap[q][i] + k);
+        };
+        f4_t acc[MTX][NS][4];
+#pragma unroll
+        for (int b = 0; b < MTX; ++b)
+#pragma unroll
+            for (int q = 0; q < NS; ++q)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc[b][q][s] = f4_t{0.f, 0.f, 0.f, 0.f};
+        // valid: false for the pipeline's reload past this wavefront's last chunk
+        auto process = [&](int jc, bool valid, uint4 (&X)[MTX][4], uint4 (&A)[NS][4]) __attribute__((always_inline)) {
+            const int k = (kWaves * jc + wave) * kWaveChunk + 8 * li;
+            if (tail && k - 8 * li + kWaveChunk > d_in) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int b = 0; b < MTX; ++b) X[b][i] = keep_if(k < d_in, X[b][i]);
+#pragma unroll
+                    for (int q = 0; q < NS; ++q) A[q][i] = keep_if(k < d_in, A[q][i]);
+                }
+            }
+            if (amask) {
+#pragma unroll
+                for (int q = 0; q < NS; ++q)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) A[q][i] = keep_if(aok[q][i], A[q][i]);
+            }
+            if (!valid) {  // zero products, and no Inf or NaN of x times 0
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int b = 0; b < MTX; ++b) X[b][i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+                    for (int q = 0; q < NS; ++q) A[q][i] = make_uint4(0, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * i + lg, o = 16 * r + (li ^ r);
+#pragma unroll
+                for (int b = 0; b < MTX; ++b) my[b * kWaveBlock + o] = X[b][i];
+#pragma unroll
+                for (int q = 0; q < NS; ++q) my[(MTX + q) * kWaveBlock + o] = A[q][i];
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int o = 16 * li + ((4 * s + lg) ^ li);
+                h8_t bop[NS];
+#pragma unroll
+                for (int q = 0; q < NS; ++q) bop[q] = __builtin_bit_cast(h8_t, my[(MTX + q) * kWaveBlock + o]);
+#pragma unroll
+                for (int b = 0; b < MTX; ++b) {
+                    const h8_t xop = __builtin_bit_cast(h8_t, my[b * kWaveBlock + o]);
+#pragma unroll
+                    for (int q = 0; q < NS; ++q)
+                        acc[b][q][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xop, bop[q], acc[b][q][s], 0, 0, 0);
+                }
+            }
+        };
+        // two chunks in flight: the next one's loads are issued before this one is
+        // processed (the scheduling barriers keep the compiler from sinking them)
+        if (nc > 0) {
+            uint4 X0[MTX][4], A0[NS][4], X1[MTX][4], A1[NS][4];
+            load(0, X0, A0);
+            for (int jc = 0; jc < nc; jc += 2) {
+                load(min(jc + 1, nc - 1), X1, A1);
+                __builtin_amdgcn_sched_barrier(0);
+                process(jc, true, X0, A0);
+                load(min(jc + 2, nc - 1), X0, A0);
+                __builtin_amdgcn_sched_barrier(0);
+                process(min(jc + 1, nc - 1), jc + 1 < nc, X1, A1);
+            }
+        }
+        __syncthreads();  // every wavefront is done with its staged blocks
+        // the classes' sums, one rank slice at a time; columns at or past the rank are 0
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+#pragma unroll
+            for (int b = 0; b < MTX; ++b)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        red[((kWaves * wave + s) * MTX + b) * 256 + (4 * lg + e) * 16 + li] = acc[b][q][s][e];
+            __syncthreads();
+            if (m.sok[q] && m.srank[q] > 0) {
+                const ProjDev &pd = a.p[m.sp[q]];
+                const int col = m.sj0[q] + (tid & 15);
+#pragma unroll
+                for (int b = 0; b < MTX; ++b) {
+                    const int o = tid + 256 * b, row = rows[4 * MTX + b];
+                    if (b >= MT || row < 0 || col >= pd.w.r_max) continue;
+                    float sum = 0.f;
+#pragma unroll
+                    for (int cl = 0; cl < 16; ++cl) sum += red[cl * MTX * 256 + o];
+                    pd.v[(int64_t)row * pd.ldv + col] = col < m.srank[q] ? sum : 0.f;
+                }
+            }
+            __syncthreads();
+        }
     }
 }
 
@@ -1860,13 +2086,13 @@ int shrink_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSr
         const int ns = paged ? 1 : (a.per_tile + (a.per_tile + ns_max - 1) / ns_max - 1) /
                                        ((a.per_tile + ns_max - 1) / ns_max);
         // A single rank slice per tile (one projection of rank <= 16) with 64-row tiles:
-        // the tile's rows go to four workgroups of 16 rows each, as many as the CUs hold at
-        // once (the tiles alone leave CUs idle); each reads the slice's A^T again (from L2).
-        const int rb = !paged && mtx > 2 && ns == 1 && a.per_tile == 1 ? 4 : 1;
-        a.grid = pad8((int64_t)n_tiles * rb * ((a.per_tile + ns - 1) / ns));
+        // the wave-staged kernel, each tile's rows in two workgroups of 32 (the tiles alone
+        // leave CUs idle); each reads the slice's A^T itself (from L2).
+        const bool wave = !paged && mtx > 2 && ns == 1;
+        a.grid = pad8((int64_t)n_tiles * (wave ? 2 : 1) * ((a.per_tile + ns - 1) / ns));
         const dim3 g((unsigned)a.grid);
 #define LORA_SHRINK_STAGED(MTX, NS) \
-    launch(lora_shrink_mfma_staged_kernel<MTX, NS, 1, OFFS>, g, kMfmaShrinkThreads, stage_lds_bytes(MTX, NS), s, a)
+    launch(lora_shrink_mfma_staged_kernel<MTX, NS, OFFS>, g, kMfmaShrinkThreads, stage_lds_bytes(MTX, NS), s, a)
         if (paged) {
             if (mtx <= 1) launch(lora_shrink_mfma_kernel<true, 1, 1, OFFS>, g, kMfmaShrinkThreads, 0, s, a);
             else if (mtx == 2) launch(lora_shrink_mfma_kernel<true, 2, 1, OFFS>, g, kMfmaShrinkThreads, 0, s, a);
@@ -1881,11 +2107,10 @@ int shrink_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileSr
             else if (ns == 2) LORA_SHRINK_STAGED(2, 2);
             else if (ns == 3) LORA_SHRINK_STAGED(2, 3);
             else LORA_SHRINK_STAGED(2, 4);
-        } else if (rb == 4) {
-            launch(lora_shrink_mfma_staged_kernel<1, 1, 4, OFFS>, g, kMfmaShrinkThreads, stage_lds_bytes(1, 1), s, a);
+        } else if (wave) {
+            launch(lora_shrink_mfma_wave_kernel<2, 1, 2, OFFS>, g, kThreads, wave_lds_bytes(2, 1), s, a);
         } else {
-            if (ns == 1) LORA_SHRINK_STAGED(4, 1);
-            else if (ns == 2) LORA_SHRINK_STAGED(4, 2);
+            if (ns == 2) LORA_SHRINK_STAGED(4, 2);
             else LORA_SHRINK_STAGED(4, 3);
         }
 #undef LORA_SHRINK_STAGED

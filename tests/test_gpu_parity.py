@@ -244,26 +244,37 @@ def test_dense_and_paged_are_bitwise_identical():
     assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
 
 
-def test_mfma_shrink_row_blocks_match_paged_bitwise():
-    """64-row tiles of one projection of rank <= 16: the dense MFMA shrink spreads each
-    tile over four 16-row workgroups, the paged one keeps a tile in one; every element is
-    summed in the same order, so y and v must agree bit for bit (and with the oracle)."""
+@pytest.mark.parametrize("d_in,r_max,page,shuffled", [(2048, 16, 512, False), (1288, 16, 8, True),
+                                                      (1288, 12, 8, True)])
+def test_mfma_shrink_row_blocks_match_paged_bitwise(d_in, r_max, page, shuffled):
+    """64-row tiles of one projection of rank <= 16: the dense shrink takes the wave-staged
+    kernel (two 32-row workgroups per tile, four wavefronts staging their own 128-column
+    chunks), the paged one keeps a tile in one 16-wavefront workgroup; every element is
+    summed in the same order, so y and v must agree bit for bit (and with the oracle).
+    Cases: d_in a multiple of the chunk, and 1288 (a last chunk of one 16-byte group);
+    r_max 12 (A^T rank-rows past r_max masked); rows in batch order or shuffled (a row
+    map from the library's builder); tiles of 64 down to 1 rows."""
     lens = [64, 130, 17, 200, 3, 64]
-    seg_ptr = wl.segments_from_lengths(lens)
     seg_slot = np.array([0, 1, 2, 3, 4, 1], dtype=np.int32)
     idx = np.repeat(seg_slot, lens).astype(np.int32)
-    rank = np.array([16, 8, 16, 1, 12], dtype=np.int32)
+    rank = np.minimum(np.array([16, 8, 16, 1, 12], dtype=np.int32), r_max)
     scale = wl.scale_for_rank(rank)
-    dense = wl.dense_store(19, 0, 5, 2048, 1536, rank, scale, r_max=16)
-    paged = wl.paged_store(19, 0, 5, 2048, 1536, rank, scale, 512, spare_pages=5)
-    x, y0 = wl.activations(19, 0, len(idx), 2048, 1536)
+    dense = wl.dense_store(19, r_max, 5, d_in, 1536, rank, scale, r_max=r_max)
+    paged = wl.paged_store(19, r_max, 5, d_in, 1536, rank, scale, page, spare_pages=5)
+    if shuffled:
+        idx = np.random.default_rng([19, d_in]).permutation(idx).astype(np.int32)
+    x, y0 = wl.activations(19, r_max, len(idx), d_in, 1536)
     y_ref, v_ref = _oracle(dense, x, y0, idx)
+    G.say(f"case wave-shrink d_in={d_in} r_max={r_max} shuffled={shuffled}")
     outs = []
     for store in (dense, paged):
-        dc = G.DeviceCase(x, y0, 16)
-        outs.append(G.run_sgmv(B.weights_from_store(store), dc, seg_ptr=seg_ptr, seg_slot=seg_slot,
-                               max_tile_rows=64))
-        G.check(dc, *outs[-1], y_ref, v_ref, G.active_rows(idx, rank), "row-blocks")
+        dc = G.DeviceCase(x, y0, r_max)
+        if shuffled:
+            outs.append(G.run_sgmv(B.weights_from_store(store), dc, idx=idx, max_tile_rows=64))
+        else:
+            outs.append(G.run_sgmv(B.weights_from_store(store), dc, seg_ptr=wl.segments_from_lengths(lens),
+                                   seg_slot=seg_slot, max_tile_rows=64))
+        G.check(dc, *outs[-1], y_ref, v_ref, G.active_rows(idx, rank), f"row-blocks-{d_in}-{r_max}")
     assert np.array_equal(outs[0][0].view(np.uint16), outs[1][0].view(np.uint16))
     assert np.array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
 
