@@ -1428,11 +1428,25 @@ __device__ inline HalfVec<CW> load_halves(const uint16_t *p)
     return h;
 }
 
-template <int CW>
+// NT: a non-temporal (streaming) store.  The expand of tiles taller than 16 rows (prefill)
+// writes y of hundreds of MB, far beyond the L2 and memory-side caches; streaming it out
+// measured 0.5 % faster per 7B prefill layer (the expands 1-4 % faster, the shrink after
+// them slower by less).  Short tiles keep normal stores: there y is small and read again
+// soon by the caller's next operation.
+template <int CW, bool NT = false>
 __device__ inline void store_halves(uint16_t *p, const HalfVec<CW> &h)
 {
-    if constexpr (CW == 8) *reinterpret_cast<uint4 *>(p) = make_uint4(h.w[0], h.w[1], h.w[2], h.w[3]);
-    else *reinterpret_cast<uint2 *>(p) = make_uint2(h.w[0], h.w[1]);
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    if constexpr (CW == 8) {
+        const u32x4_t v{h.w[0], h.w[1], h.w[2], h.w[3]};
+        if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
+        else *reinterpret_cast<u32x4_t *>(p) = v;
+    } else {
+        const u32x2_t v{h.w[0], h.w[1]};
+        if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t *>(p));
+        else *reinterpret_cast<u32x2_t *>(p) = v;
+    }
 }
 
 // keep a loaded value in flight where it was issued (see the callers)
@@ -1598,7 +1612,7 @@ void lora_expand_mfma_kernel(Args args)
                     const float hi = h2f((uint16_t)yv[e].half(2 * e2 + 1)) + __builtin_ldexpf(acc[2 * e2 + 1][e], exr);
                     out.w[e2] = (uint32_t)f2h(lo) | ((uint32_t)f2h(hi) << 16);
                 }
-                store_halves<CW>(pd.y + (int64_t)yr[e] * pd.ldy + c, out);
+                store_halves<CW, TM>(pd.y + (int64_t)yr[e] * pd.ldy + c, out);
             }
         }
         if (!more) break;
