@@ -281,6 +281,18 @@ __device__ inline const uint16_t *a_paged(const WeightsDev &w, const int *cache,
 }
 
 __device__ inline uint4 load16(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// A non-temporal (streaming) 16-byte load, for data read once per launch that dwarfs the
+// caches: prefill's x rows in the MFMA shrinks and y in the expand of tall tiles.  Kept
+// at normal priority, those streams evict the weights the next tiles reuse and fill the
+// memory-side cache with lines that the next launch must first write back or displace;
+// streamed, the 7B prefill layer measured 609 -> 554 us (its shrinks 1.2-1.8x faster).
+__device__ inline uint4 load16_nt(const uint16_t *p)
+{
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ inline h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
 
 // fp32 += dot of 8 fp16 pairs (v_dot2_f32_f16; fp16 products are exact in fp32).
@@ -863,13 +875,15 @@ __host__ __device__ constexpr size_t stage_lds_bytes(int mtx, int ns)
 }
 
 // Octet k .. k+7 of every staged row this wavefront loads; zero past d_in or for rows
-// without a source.
+// without a source.  Streaming loads for every staged row: the x rows make up most of
+// each chunk, and the few A^T rank-rows take the same load so the loop has no per-row
+// branch.
 template <int RPW>
 __device__ inline void stage_load(const uint16_t *const (&src)[RPW], int k, int d_in, uint4 (&st)[RPW])
 {
     const uint4 z4 = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) st[i] = (src[i] && k < d_in) ? load16(src[i] + k) : z4;
+    for (int i = 0; i < RPW; ++i) st[i] = (src[i] && k < d_in) ? load16_nt(src[i] + k) : z4;
 }
 
 template <int MTX, int NS, bool OFFS>
@@ -1066,7 +1080,7 @@ __global__ __launch_bounds__(kThreads) void lora_shrink_mfma_wave_kernel(Args ar
 #pragma unroll
             for (int b = 0; b < MTX; ++b)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) X[b][i] = load16(xp[b][i] + k);
+                for (int i = 0; i < 4; ++i) X[b][i] = load16_nt(xp[b][i] + k);
 #pragma unroll
             for (int q = 0; q < NS; ++q)
 #pragma unroll
@@ -1414,25 +1428,28 @@ struct HalfVec {
     __device__ uint32_t half(int m) const { return (m & 1) ? (w[m >> 1] >> 16) : (w[m >> 1] & 0xffff); }
 };
 
-template <int CW>
+// NT: a streaming load (y of tall tiles, see load16_nt).
+template <int CW, bool NT = false>
 __device__ inline HalfVec<CW> load_halves(const uint16_t *p)
 {
     HalfVec<CW> h;
     if constexpr (CW == 8) {
-        const uint4 q = *reinterpret_cast<const uint4 *>(p);
+        const uint4 q = NT ? load16_nt(p) : *reinterpret_cast<const uint4 *>(p);
         h.w[0] = q.x, h.w[1] = q.y, h.w[2] = q.z, h.w[3] = q.w;
     } else {
-        const uint2 q = *reinterpret_cast<const uint2 *>(p);
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t q = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p))
+                             : *reinterpret_cast<const u32x2_t *>(p);
         h.w[0] = q.x, h.w[1] = q.y;
     }
     return h;
 }
 
 // NT: a non-temporal (streaming) store.  The expand of tiles taller than 16 rows (prefill)
-// writes y of hundreds of MB, far beyond the L2 and memory-side caches; streaming it out
-// measured 0.5 % faster per 7B prefill layer (the expands 1-4 % faster, the shrink after
-// them slower by less).  Short tiles keep normal stores: there y is small and read again
-// soon by the caller's next operation.
+// reads and writes y of hundreds of MB, far beyond the L2 and memory-side caches, and
+// streams both (see load16_nt; the stores alone measured 0.5 % faster per 7B prefill
+// layer).  Short tiles keep normal accesses: there y is small and read again soon by the
+// caller's next operation.
 template <int CW, bool NT = false>
 __device__ inline void store_halves(uint16_t *p, const HalfVec<CW> &h)
 {
@@ -1516,7 +1533,7 @@ void lora_expand_mfma_kernel(Args args)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         yr[e] = __shfl(vr, 4 * lg + e);
-        yv[e] = load_halves<CW>(pd.y + (int64_t)max(yr[e], 0) * pd.ldy + cc);
+        yv[e] = load_halves<CW, TM>(pd.y + (int64_t)max(yr[e], 0) * pd.ldy + cc);
     }
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
@@ -1558,7 +1575,7 @@ void lora_expand_mfma_kernel(Args args)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 yr_n[e] = __shfl(vr_n, 4 * lg + e);
-                yv_n[e] = load_halves<CW>(pd.y + (int64_t)max(yr_n[e], 0) * pd.ldy + cc);
+                yv_n[e] = load_halves<CW, TM>(pd.y + (int64_t)max(yr_n[e], 0) * pd.ldy + cc);
             }
         }
         // row li's scale 2^ex: above max_j |s v[row][j]| (its four 16-lane groups)
@@ -1635,7 +1652,7 @@ void lora_expand_mfma_kernel(Args args)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 yr[e] = __shfl(vr, 4 * lg + e);
-                yv[e] = load_halves<CW>(pd.y + (int64_t)max(yr[e], 0) * pd.ldy + cc);
+                yv[e] = load_halves<CW, TM>(pd.y + (int64_t)max(yr[e], 0) * pd.ldy + cc);
             }
         }
     }
