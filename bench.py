@@ -964,6 +964,9 @@ def main():
                     help="per-row and segment forms: one launch per unit with v handed from the shrink's "
                          "workgroups to the expand's (auto: the per-row form with dense weights, where it measures "
                          "faster than two launches)")
+    ap.add_argument("--stream-weights", choices=["auto", "on", "off"], default="auto",
+                    help="lora_set_stream_weights: auto = on for the per-row form with dense weights when "
+                         "the batch's active rows use distinct adapters")
     ap.add_argument("--no-floors", action="store_true", help="skip the empty-launch and copy reference steps")
     ap.add_argument("--plan", default="0,0", metavar="JW,NR",
                     help="fix rank-rows per VALU shrink workgroup and rows per pass of the segment-form VALU "
@@ -1054,6 +1057,14 @@ def main():
         for ops in groups:
             for op in ops:
                 op.work = work
+    # the caller's hint that each row of the per-row form uses its own adapter (dense
+    # weights then stream through the caches): on where the batch's active rows carry
+    # distinct adapters, as the host that built the batch knows
+    act = spec["batch"].idx[spec["batch"].idx >= 0]
+    distinct = len(np.unique(act)) == len(act)
+    stream_w = args.stream_weights == "on" or (args.stream_weights == "auto" and spec["form"] == "bgmv"
+                                               and spec["layout"] == "dense" and distinct)
+    B.lora_set_stream_weights(stream_w)
     plan = launches(groups, grouped, handoff)
     n_launch = len(plan)
 
@@ -1146,6 +1157,7 @@ def main():
                    "grouped": grouped, "launches_per_step": n_launch, "tile_rows": args.tile_rows,
                    "expand_tile_rows": spec.get("expand_tile_rows"),
                    "handoff": handoff,
+                   "stream_weights": bool(stream_w),
                    "plan": args.plan,
                    "graph": not args.no_graph,
                    "parallelism": "none"},

@@ -466,6 +466,21 @@ int lora_set_launch_events(void *start_event, void *stop_event);
 int lora_set_plan(int32_t shrink_rank_rows, int32_t rows_per_pass);
 
 /*
+ * Caller hint for the per-row calls (lora_bgmv_shrink/expand and their _multi and
+ * _handoff forms) with dense weights: on = 1 when every active row of the calling
+ * thread's later calls uses an adapter that no other row of the same call uses (a decode
+ * batch whose requests all carry different adapters; Punica summary, the "Distinct" case
+ * of the SGMV kernel schedule).  The kernels then read the A^T and B rows with streaming
+ * (non-temporal) loads: each is read once, and keeping it in the caches only displaces
+ * the rest (7B decode, 32 distinct adapters, one launch per unit: 35.8 -> 34.7 us per
+ * layer).  With adapters shared between rows it is slower (13B Zipf 1.5 mix in the
+ * per-row form: 81.5 -> 103.4), hence off (0) by default.  The segment form and paged
+ * weights ignore it.  Results are bit-identical either way.  Returns LORA_E_SHAPE for
+ * values other than 0 and 1.  Per-thread state, like lora_set_plan.
+ */
+int lora_set_stream_weights(int32_t on);
+
+/*
  * Test hook: the number of polls an expand workgroup of lora_bgmv_multi_handoff makes
  * for its v before computing v itself, for the calling thread's later calls (0: every
  * expand workgroup computes its v; a negative value restores the default, about 30 ms

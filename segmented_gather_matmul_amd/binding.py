@@ -33,7 +33,7 @@ EXPORTS = ["lora_build_segments", "lora_tiles_bound", "lora_build_tiles", "lora_
            "lora_abi_version", "lora_set_launch_events", "lora_sgmv_shrink_multi", "lora_sgmv_expand_multi",
            "lora_bgmv_shrink_multi", "lora_bgmv_expand_multi", "lora_pick_tile_rows", "lora_pick_expand_tile_rows",
            "lora_bgmv_multi",
-           "lora_set_plan", "lora_pool_state_bytes", "lora_pool_init", "lora_pool_alloc", "lora_pool_release",
+           "lora_set_plan", "lora_set_stream_weights", "lora_pool_state_bytes", "lora_pool_init", "lora_pool_alloc", "lora_pool_release",
            "lora_pool_free_count", "lora_pool_pages_for", "lora_pool_load_header_bytes", "lora_pool_load",
            "lora_handoff_bytes", "lora_bgmv_multi_handoff", "lora_sgmv_multi_handoff", "lora_set_handoff_polls",
            "lora_sgmv_workspace_bytes", "lora_bgmv_multi_handoff_noalloc"]
@@ -108,6 +108,7 @@ def lib() -> ctypes.CDLL:
             "lora_pick_expand_tile_rows": [P, I32],
             "lora_bgmv_multi": [P, P, I64, P, I32, I32, P],
             "lora_set_plan": [I32, I32],
+            "lora_set_stream_weights": [I32],
             "lora_bgmv_multi_handoff": [P, P, I64, P, I32, I32, P, P, ctypes.c_size_t],
             "lora_set_handoff_polls": [I32],
             "lora_sgmv_multi_handoff": [P, P, I64, I32, P, I32, P, P, ctypes.c_size_t],
@@ -551,6 +552,12 @@ def lora_set_plan(shrink_rank_rows=0, rows_per_pass=0):
     pass of the segment-form VALU kernels for this thread's later launches; results are
     bit-identical either way."""
     _check(lib().lora_set_plan(int(shrink_rank_rows), int(rows_per_pass)))
+
+
+def lora_set_stream_weights(on: bool):
+    """Per-thread hint: the later per-row calls' rows use distinct adapters, so dense
+    weights are read with streaming loads (same bits; slower when adapters repeat)."""
+    _check(lib().lora_set_stream_weights(1 if on else 0))
 
 
 def lora_set_handoff_polls(polls=-1):

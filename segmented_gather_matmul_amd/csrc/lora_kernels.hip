@@ -293,6 +293,10 @@ __device__ inline uint4 load16_nt(const uint16_t *p)
     const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+
+// SW, a template flag of the per-row VALU and hand-off kernels: the adapters' dense A^T and
+// B rows are read with streaming loads (lora_set_stream_weights: a batch whose rows all
+// use distinct adapters reads every weight row once).
 __device__ inline h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
 
 // fp32 += dot of 8 fp16 pairs (v_dot2_f32_f16; fp16 products are exact in fp32).
@@ -524,7 +528,8 @@ struct ShrinkHalf {
 // every data load unconditionally (page 0, which always exists, stands in for a rank-row
 // that needs none) and mask the results: loads under per-lane branches were issued one
 // page-id round trip apart.
-template <bool PAGED, bool CACHED, int NR, int RJ>
+// NT: streaming loads of dense A^T rank-rows (the SW flag of the kernels).
+template <bool PAGED, bool CACHED, int NR, int RJ, bool NT = false>
 __device__ inline ShrinkHalf<NR, RJ> load_half(const ShrinkSrc &s, const int (&rows)[NR], int o)
 {
     ShrinkHalf<NR, RJ> h;
@@ -536,7 +541,9 @@ __device__ inline ShrinkHalf<NR, RJ> load_half(const ShrinkSrc &s, const int (&r
 #pragma unroll
         for (int jj = 0; jj < RJ; ++jj) {
             const int j = s.jb + jj;
-            h.a[jj] = (in && j < s.jload) ? load16(dense_row<false>(s.w, s.slot, j) + 8 * o) : z4;
+            h.a[jj] = (in && j < s.jload) ? (NT ? load16_nt(dense_row<false>(s.w, s.slot, j) + 8 * o)
+                                                 : load16(dense_row<false>(s.w, s.slot, j) + 8 * o))
+                                          : z4;
         }
     } else {
         const int P = s.w.page_elems, k = 8 * o, q = k / P, within = k - q * P, npg = s.w.d_in / P;
@@ -566,7 +573,7 @@ __device__ inline uint32_t *handoff_row(const HandoffDev &ho, int row, int p);
 
 // The VALU shrink's sums over halves [0, h_end) of octet pairs for NR rows and RJ
 // rank-rows: D halves (whole pairs) are requested together, then summed in order.
-template <bool PAGED, bool CACHED, int NR, int RJ, int D>
+template <bool PAGED, bool CACHED, int NR, int RJ, int D, bool NT = false>
 __device__ inline void shrink_halves(const ShrinkSrc &src, const int (&rows)[NR], int n_half, int h_end,
                                      float (&acc)[NR][RJ])
 {
@@ -575,7 +582,7 @@ __device__ inline void shrink_halves(const ShrinkSrc &src, const int (&rows)[NR]
         ShrinkHalf<NR, RJ> hf[D];
 #pragma unroll
         for (int d = 0; d < D; ++d)
-            if (d == 0 || h0 + d < n_half) hf[d] = load_half<PAGED, CACHED, NR, RJ>(src, rows, tid + kThreads * (h0 + d));
+            if (d == 0 || h0 + d < n_half) hf[d] = load_half<PAGED, CACHED, NR, RJ, NT>(src, rows, tid + kThreads * (h0 + d));
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             // a pair runs when its first octet exists; its second term may be zero
@@ -606,7 +613,7 @@ enum class VSink { Global, Lds, Handoff };
 // DH: halves of octet pairs in flight together (0: about 16 loads per lane); it changes
 // the batching of the loads, not the order of any sum.  only_rg >= 0: only the pass over
 // the tile's rows [only_rg, only_rg + NR).
-template <bool PAGED, bool PERROW, int RJ, int NR, VSink SINK, int DH = 0, bool OFFS = false>
+template <bool PAGED, bool PERROW, int RJ, int NR, VSink SINK, int DH = 0, bool OFFS = false, bool SW = false>
 __device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *red, int *pcache, float *vlds,
                                         int only_rg = -1, bool use_known = false, lora_tile known = lora_tile{})
 {
@@ -644,7 +651,7 @@ __device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *re
             // weights: rank-rows at or past the slot's rank (known here) need neither x nor
             // A; their sums stay zero, as the loop would leave them.
             const int h_end = (!PAGED || jb < jload) ? n_half : 0;
-            if (!PAGED || cached) shrink_halves<PAGED, true, NR, RJ, D>(src, rows, n_half, h_end, acc);
+            if (!PAGED || cached) shrink_halves<PAGED, true, NR, RJ, D, SW>(src, rows, n_half, h_end, acc);
             else shrink_halves<PAGED, false, NR, RJ, D>(src, rows, n_half, h_end, acc);
 #pragma unroll
             for (int q = 0; q < NR; ++q)
@@ -681,7 +688,7 @@ __device__ inline bool shrink_valu_item(const Args &a, const Item &it, float *re
     return rank > 0;
 }
 
-template <bool PAGED, bool PERROW, int RJ, int NR, bool OFFS>
+template <bool PAGED, bool PERROW, int RJ, int NR, bool OFFS, bool SW = false>
 __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args args)
 {
     const Args &a = kernel_args<!PAGED>(args);
@@ -690,7 +697,7 @@ __global__ __launch_bounds__(kThreads) void lora_shrink_valu_kernel(Args args)
     const Item it = work(a);
     if (!it.ok) return;
     prepare_tile<PERROW, OFFS, kThreads>(a.ts, a.n_rows, it.tile);
-    shrink_valu_item<PAGED, PERROW, RJ, NR, VSink::Global, 0, OFFS>(a, it, red, pcache, nullptr);
+    shrink_valu_item<PAGED, PERROW, RJ, NR, VSink::Global, 0, OFFS, SW>(a, it, red, pcache, nullptr);
 }
 
 // Rank slices of an MFMA shrink workgroup: slices g0 .. g0 + NS - 1 of the launch's
@@ -1228,7 +1235,7 @@ __device__ inline void load_b_paged(const WeightsDev &w, int slot, int jlim, int
 // data loads as the rank needs (a quarter, half or all of RU, picked once per
 // wavefront), unconditionally and masked, because a load under a per-lane branch is
 // sunk by the compiler next to its conditional use and waited on alone.
-template <bool PAGED, int RU>
+template <bool PAGED, int RU, bool NT = false>
 __device__ inline void load_b_octets(const WeightsDev &w, int slot, int jlim, int wave, int u0, int c, bool cin,
                                      uint4 *bv)
 {
@@ -1237,7 +1244,7 @@ __device__ inline void load_b_octets(const WeightsDev &w, int slot, int jlim, in
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
             const int j = wave + kWaves * (u0 + u);
-            bv[u] = (cin && j < jlim) ? load16(dense_row<true>(w, slot, j) + c) : z4;
+            bv[u] = (cin && j < jlim) ? (NT ? load16_nt(dense_row<true>(w, slot, j) + c) : load16(dense_row<true>(w, slot, j) + c)) : z4;
         }
     } else if constexpr (RU >= 8) {
         // entries this wavefront needs: rank-rows wave + 4 u below jlim, from u0 on
@@ -1343,7 +1350,7 @@ __device__ inline void expand_pass(const ProjDev &pd, const ExpandPass<PERROW, N
 template <bool PAGED, int NR, int RU>
 constexpr int expand_valu_waves() { return PAGED && NR == 4 && RU == 16 ? 1 : 4; }
 
-template <bool PAGED, bool PERROW, int NR, int RU, bool OFFS>
+template <bool PAGED, bool PERROW, int NR, int RU, bool OFFS, bool SW = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(expand_valu_waves<PAGED, NR, RU>())))
 void lora_expand_valu_kernel(Args args)
 {
@@ -1373,7 +1380,7 @@ void lora_expand_valu_kernel(Args args)
             p1.load(a, pd, th, r);
             const uint4 y1 = p1.load_y(pd, cr, cin);
             uint4 b1[RU];
-            load_b_octets<PAGED, RU>(pd.w, th.slot, jr, wr, 0, cr, cin, b1);
+            load_b_octets<PAGED, RU, SW>(pd.w, th.slot, jr, wr, 0, cr, cin, b1);
             expand_pass<PERROW, 1, RU>(pd, p1, sc, rank, b1, y1, cr, cin, red);
         }
         return;
@@ -1383,7 +1390,7 @@ void lora_expand_valu_kernel(Args args)
     ps.load(a, pd, th, 0);
     const uint4 yv = ps.load_y(pd, c, cin);
     uint4 bv[RU];
-    load_b_octets<PAGED, RU>(pd.w, th.slot, jlim, wave, 0, c, cin, bv);
+    load_b_octets<PAGED, RU, SW>(pd.w, th.slot, jlim, wave, 0, c, cin, bv);
     expand_pass<PERROW, NR, RU>(pd, ps, sc, rank, bv, yv, c, cin, red);
 }
 
@@ -1752,7 +1759,7 @@ constexpr int kHandoffArgsOffset = 24;  // byte offset of the argument block aft
                                         // leading arguments (8 + 3 * 4 bytes, 8-byte aligned)
 static_assert(alignof(Args) == 8, "argument block alignment");
 
-template <bool PAGED, bool PERROW, int RJ, int NR, int RU, bool OFFS>
+template <bool PAGED, bool PERROW, int RJ, int NR, int RU, bool OFFS, bool SW = false>
 __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(const void *__restrict__ pre_src, int32_t pre_n_shrink,
                                                                 int32_t pre_per_tile, int32_t pre_e_per_tile, Args args)
 {
@@ -1785,7 +1792,7 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(const void *__re
     if (!it.ok) return;
     prepare_tile<PERROW, OFFS, kThreads>(a.ts, a.n_rows, it.tile);
     if (shrink) {
-        const bool stored = shrink_valu_item<PAGED, PERROW, RJ, NR, VSink::Handoff, kDH, OFFS>(
+        const bool stored = shrink_valu_item<PAGED, PERROW, RJ, NR, VSink::Handoff, kDH, OFFS, SW>(
             a, it, red, pcache, nullptr, -1, have_early, early);
         // wavefront 0 made every v store of this workgroup
         if (stored && wave == 0) {
@@ -1815,7 +1822,7 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(const void *__re
         for (int r = 0; r < th.nrows; ++r) {
             for (int sl = 0; sl < a.p[it.p].slices; ++sl) {
                 const Item si{it.tile, it.p, sl, true};
-                shrink_valu_item<PAGED, PERROW, 1, 1, VSink::Lds, 2, OFFS>(a, si, red, pcache, &vrow[0][0], r, have_early,
+                shrink_valu_item<PAGED, PERROW, 1, 1, VSink::Lds, 2, OFFS, SW>(a, si, red, pcache, &vrow[0][0], r, have_early,
                                                                      early);
             }
             ExpandPass<PERROW, 1> ps;
@@ -1823,7 +1830,7 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(const void *__re
             ps.my_row = wave == 0 ? ps.rows[0] : -1;
             const uint4 yv = ps.load_y(pd, c, cin);
             uint4 bw[RU];
-            load_b_octets<PAGED, RU>(pd.w, th.slot, jlim, wave, 0, c, cin, bw);
+            load_b_octets<PAGED, RU, SW>(pd.w, th.slot, jlim, wave, 0, c, cin, bw);
             ps.sv[0] = lane < pd.w.r_max ? vrow[0][lane] : 0.f;
             expand_pass<PERROW, 1, RU>(pd, ps, sc, rank, bw, yv, c, cin, red);
             if (wave == 0 && rank > 0)
@@ -1840,7 +1847,7 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(const void *__re
     if (wave >= NR) ps.my_row = -1;
     const uint4 yv = ps.load_y(pd, c, cin);
     uint4 bv[RU];
-    load_b_octets<PAGED, RU>(pd.w, th.slot, jlim, wave, 0, c, cin, bv);
+    load_b_octets<PAGED, RU, SW>(pd.w, th.slot, jlim, wave, 0, c, cin, bv);
     // A rank-0 row's shrink items store nothing: such a workgroup neither waits nor
     // counts, and its expand writes nothing.  Tested as a predicate rather than by an
     // early return so that the loads above are not held back behind the rank.
@@ -1871,7 +1878,7 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(const void *__re
                 const Item si{it.tile, it.p, sl, true};
                 // one rank-row and one pair of halves at a time: few registers on a path
                 // that only runs when the poll limit runs out
-                shrink_valu_item<PAGED, PERROW, 1, NR, VSink::Lds, 2, OFFS>(a, si, red, pcache, &vrow[0][0], 0, have_early,
+                shrink_valu_item<PAGED, PERROW, 1, NR, VSink::Lds, 2, OFFS, SW>(a, si, red, pcache, &vrow[0][0], 0, have_early,
                                                                       early);
             }
         }
@@ -1886,6 +1893,10 @@ __global__ __launch_bounds__(kThreads) void lora_handoff_kernel(const void *__re
 // ------------------------------------------------------------------------ launchers
 // Event pair attached to this thread's next kernel launch (lora_set_launch_events).
 thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+// Set by lora_set_stream_weights for the calling thread: the per-row calls' rows use
+// distinct adapters, so their dense weights are read with streaming loads.
+thread_local int32_t t_stream_w = 0;
 
 // A launch whose kernel takes leading scalar arguments before the argument block.
 template <typename Kernel>
@@ -2058,9 +2069,13 @@ int rows_per_pass(int32_t max_rows)
 template <bool PERROW, int NR, bool OFFS>
 void shrink_valu_launch(bool paged, int32_t jw, dim3 grid, hipStream_t s, const Args &a)
 {
-#define LORA_SHRINK_VALU(RJ)                                                                         \
-    (paged ? launch(lora_shrink_valu_kernel<true, PERROW, RJ, NR, OFFS>, grid, kThreads, 0, s, a)   \
-           : launch(lora_shrink_valu_kernel<false, PERROW, RJ, NR, OFFS>, grid, kThreads, 0, s, a))
+// Per-row launches with dense weights stream the weights when the caller said the rows'
+// adapters are distinct (lora_set_stream_weights); SW = PERROW keeps the segment form on
+// its one instance.
+#define LORA_SHRINK_VALU(RJ)                                                                                   \
+    (paged           ? launch(lora_shrink_valu_kernel<true, PERROW, RJ, NR, OFFS>, grid, kThreads, 0, s, a)     \
+     : t_stream_w    ? launch(lora_shrink_valu_kernel<false, PERROW, RJ, NR, OFFS, PERROW>, grid, kThreads, 0, s, a) \
+                     : launch(lora_shrink_valu_kernel<false, PERROW, RJ, NR, OFFS>, grid, kThreads, 0, s, a))
     if (jw == 1) LORA_SHRINK_VALU(1);
     else if (jw == 2) LORA_SHRINK_VALU(2);
     else LORA_SHRINK_VALU(4);
@@ -2070,9 +2085,10 @@ void shrink_valu_launch(bool paged, int32_t jw, dim3 grid, hipStream_t s, const 
 template <bool PERROW, int NR, bool OFFS>
 void expand_valu_launch(bool paged, int32_t r_max, dim3 grid, hipStream_t s, const Args &a)
 {
-#define LORA_EXPAND_VALU(RU)                                                                        \
-    (paged ? launch(lora_expand_valu_kernel<true, PERROW, NR, RU, OFFS>, grid, kThreads, 0, s, a)  \
-           : launch(lora_expand_valu_kernel<false, PERROW, NR, RU, OFFS>, grid, kThreads, 0, s, a))
+#define LORA_EXPAND_VALU(RU)                                                                                   \
+    (paged           ? launch(lora_expand_valu_kernel<true, PERROW, NR, RU, OFFS>, grid, kThreads, 0, s, a)     \
+     : t_stream_w    ? launch(lora_expand_valu_kernel<false, PERROW, NR, RU, OFFS, PERROW>, grid, kThreads, 0, s, a) \
+                     : launch(lora_expand_valu_kernel<false, PERROW, NR, RU, OFFS>, grid, kThreads, 0, s, a))
     if (r_max <= 16) LORA_EXPAND_VALU(4);
     else if (r_max <= 32) LORA_EXPAND_VALU(8);
     else LORA_EXPAND_VALU(16);
@@ -2273,29 +2289,30 @@ int handoff_impl(void *stream, const void *x, int64_t ldx, int32_t n_rows, TileS
     hipStream_t s = static_cast<hipStream_t>(stream);
     // the preloaded leading arguments: tile source and grid layout
     const void *pre_src = PERROW ? static_cast<const void *>(ts.idx) : static_cast<const void *>(ts.tiles);
-#define LORA_HANDOFF_RU(PG, RJ, NR)                                                                              \
+#define LORA_HANDOFF_RU(PG, RJ, NR, SW)                                                                          \
     if (r_max <= 16)                                                                                             \
-        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 4, OFFS>, grid, kThreads, 0, s, pre_src, a.ho.n_shrink,    \
-                   a.per_tile, a.ho.e_per_tile, a);                                                              \
+        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 4, OFFS, SW>, grid, kThreads, 0, s, pre_src,          \
+                   a.ho.n_shrink, a.per_tile, a.ho.e_per_tile, a);                                               \
     else if (r_max <= 32)                                                                                        \
-        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 8, OFFS>, grid, kThreads, 0, s, pre_src, a.ho.n_shrink,    \
-                   a.per_tile, a.ho.e_per_tile, a);                                                              \
+        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 8, OFFS, SW>, grid, kThreads, 0, s, pre_src,          \
+                   a.ho.n_shrink, a.per_tile, a.ho.e_per_tile, a);                                               \
     else                                                                                                         \
-        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 16, OFFS>, grid, kThreads, 0, s, pre_src, a.ho.n_shrink,   \
-                   a.per_tile, a.ho.e_per_tile, a)
-#define LORA_HANDOFF_JW(PG, NR)                      \
-    if (a.jw == 1) { LORA_HANDOFF_RU(PG, 1, NR); }    \
-    else if (a.jw == 2) { LORA_HANDOFF_RU(PG, 2, NR); } \
-    else { LORA_HANDOFF_RU(PG, 4, NR); }
+        launch_pre(lora_handoff_kernel<PG, PERROW, RJ, NR, 16, OFFS, SW>, grid, kThreads, 0, s, pre_src,         \
+                   a.ho.n_shrink, a.per_tile, a.ho.e_per_tile, a)
+#define LORA_HANDOFF_JW(PG, NR, SW)                          \
+    if (a.jw == 1) { LORA_HANDOFF_RU(PG, 1, NR, SW); }        \
+    else if (a.jw == 2) { LORA_HANDOFF_RU(PG, 2, NR, SW); }   \
+    else { LORA_HANDOFF_RU(PG, 4, NR, SW); }
     if constexpr (PERROW) {
         (void)max_rows;
-        if (paged) { LORA_HANDOFF_JW(true, 1) }
-        else { LORA_HANDOFF_JW(false, 1) }
+        if (paged) { LORA_HANDOFF_JW(true, 1, false) }
+        else if (t_stream_w) { LORA_HANDOFF_JW(false, 1, true) }
+        else { LORA_HANDOFF_JW(false, 1, false) }
     } else {
         const int nr = rows_per_pass(max_rows);
-        if (nr == 1) { LORA_HANDOFF_JW(false, 1) }
-        else if (nr == 2) { LORA_HANDOFF_JW(false, 2) }
-        else { LORA_HANDOFF_JW(false, 4) }
+        if (nr == 1) { LORA_HANDOFF_JW(false, 1, false) }
+        else if (nr == 2) { LORA_HANDOFF_JW(false, 2, false) }
+        else { LORA_HANDOFF_JW(false, 4, false) }
     }
 #undef LORA_HANDOFF_JW
 #undef LORA_HANDOFF_RU
@@ -2384,6 +2401,14 @@ int lora_set_launch_events(void *start_event, void *stop_event)
     clear_error();
     t_ev_start = static_cast<hipEvent_t>(start_event);
     t_ev_stop = static_cast<hipEvent_t>(stop_event);
+    return LORA_OK;
+}
+
+int lora_set_stream_weights(int32_t on)
+{
+    clear_error();
+    if (on != 0 && on != 1) return fail(LORA_E_SHAPE, "on = %d is not 0 or 1", on);
+    t_stream_w = on;
     return LORA_OK;
 }
 

@@ -34,7 +34,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 36 and set(names) == set(B.EXPORTS)
+    assert len(names) == 37 and set(names) == set(B.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", build_mod.LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT (lora_\w+)", out))
@@ -359,6 +359,14 @@ def test_set_plan_ranges():
     assert L.lora_set_plan(0, -1) == B.LORA_E_SHAPE
     assert L.lora_set_plan(64, 4) == B.LORA_OK
     assert L.lora_set_plan(0, 0) == B.LORA_OK
+
+
+def test_set_stream_weights_values():
+    L = B.lib()
+    assert L.lora_set_stream_weights(2) == B.LORA_E_SHAPE
+    assert L.lora_set_stream_weights(-1) == B.LORA_E_SHAPE
+    assert L.lora_set_stream_weights(1) == B.LORA_OK
+    assert L.lora_set_stream_weights(0) == B.LORA_OK
 
 
 def test_pick_tile_rows():

@@ -50,25 +50,30 @@ def _assert_clear(work, label):
 
 
 def _compare(label, x_d, idx_d, ws, dcs, work):
-    """Two launches, then the hand-off form at the default and at a zero poll limit;
-    returns the two-launch results."""
+    """Two launches, then the hand-off form at the default and at a zero poll limit, and
+    both forms again with the streaming-weights hint (lora_set_stream_weights; same bits
+    whether or not the rows' adapters are distinct); returns the two-launch results."""
     results = {}
-    for mode in ("two", "handoff", "local"):
+    for mode in ("two", "handoff", "local", "two-sw", "handoff-sw"):
         for dc in dcs:
             dc.reset()
         items = [(w, dc.v, dc.y) for w, dc in zip(ws, dcs)]
-        if mode == "two":
-            B.lora_bgmv_multi(x_d, idx_d, items)
-        else:
-            B.lora_set_handoff_polls(0 if mode == "local" else -1)
-            try:
-                B.lora_bgmv_multi_handoff(x_d, idx_d, items, work)
-            finally:
-                B.lora_set_handoff_polls(-1)
+        B.lora_set_stream_weights(mode.endswith("-sw"))
+        try:
+            if mode.startswith("two"):
+                B.lora_bgmv_multi(x_d, idx_d, items)
+            else:
+                B.lora_set_handoff_polls(0 if mode == "local" else -1)
+                try:
+                    B.lora_bgmv_multi_handoff(x_d, idx_d, items, work)
+                finally:
+                    B.lora_set_handoff_polls(-1)
+        finally:
+            B.lora_set_stream_weights(False)
         results[mode] = [dc.results() for dc in dcs]
         _assert_clear(work, f"{label} {mode}")
     base = results["two"]
-    for mode in ("handoff", "local"):
+    for mode in ("handoff", "local", "two-sw", "handoff-sw"):
         for p, ((yb, vb), (yg, vg)) in enumerate(zip(base, results[mode])):
             assert np.array_equal(yb.view(np.uint16), yg.view(np.uint16)), f"{label}: {mode} proj {p}: y"
             assert np.array_equal(vb.view(np.uint32), vg.view(np.uint32)), f"{label}: {mode} proj {p}: v"
